@@ -1,0 +1,133 @@
+"""Independent reference arithmetic used to pin the oracle (tests only).
+
+Nothing here is shared with the oracle or the HIP library:
+  * exact router logits by integer arithmetic on the dyadic fp32 inputs;
+  * a numpy decoder of the canonical expert blob;
+  * a dense, masked float64 brute force of the whole layer (every expert is
+    evaluated for every token and masked by the exact top-k).
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+_SHIFT = 149  # every finite fp32 value is an integer multiple of 2^-149
+
+
+def f32_to_int(v: np.ndarray) -> list:
+    """fp32 values -> exact Python ints v * 2^149."""
+    out = []
+    for a in np.asarray(v, dtype=np.float32).reshape(-1).tolist():
+        fr = Fraction(a) * (1 << _SHIFT)
+        assert fr.denominator == 1
+        out.append(int(fr))
+    return out
+
+
+def exact_logits(x: np.ndarray, Wr: np.ndarray, bias=None) -> list:
+    """z[t][e] * 2^298 as exact integers (x: [T,d] fp32, Wr: [E,d] fp32)."""
+    T, d = x.shape
+    E = Wr.shape[0]
+    xi = [f32_to_int(x[t]) for t in range(T)]
+    wi = [f32_to_int(Wr[e]) for e in range(E)]
+    bi = None if bias is None else [b << _SHIFT for b in f32_to_int(bias)]
+    z = []
+    for t in range(T):
+        row = []
+        for e in range(E):
+            acc = sum(a * b for a, b in zip(xi[t], wi[e]))
+            if bi is not None:
+                acc += bi[e]
+            row.append(acc)
+        z.append(row)
+    return z
+
+
+def exact_topk(zrow: list, k: int) -> list:
+    """Top-k ids by (logit descending, index ascending) -- Python's sort."""
+    return sorted(range(len(zrow)), key=lambda e: (-zrow[e], e))[:k]
+
+
+def logits_to_float(zrow: list) -> np.ndarray:
+    return np.array([float(Fraction(v, 1 << (2 * _SHIFT))) for v in zrow], dtype=np.float64)
+
+
+def decode_blob(blob: np.ndarray, wfmt: int, d: int, f: int):
+    """numpy decoder of the canonical blob -> (Wg [f,d], Wu [f,d], Wd [d,f]) float64."""
+    n = d * f
+    qb = n // 2 if wfmt == 4 else n
+    sb = (n // 32) * 2
+    blob = np.asarray(blob, dtype=np.uint8)
+
+    def quants(off, R, K):
+        raw = blob[off:off + qb]
+        if wfmt == 8:
+            q = raw.view(np.int8).astype(np.int64)
+        else:
+            q = np.empty(n, dtype=np.int64)
+            q[0::2] = (raw & 0xF).astype(np.int64) - 8
+            q[1::2] = (raw >> 4).astype(np.int64) - 8
+        return q.reshape(R, K)
+
+    def scales(off, R, K):
+        return blob[off:off + sb].view(np.float16).astype(np.float64).reshape(R, K // 32)
+
+    def mat(qoff, soff, R, K):
+        return quants(qoff, R, K) * np.repeat(scales(soff, R, K), 32, axis=1)
+
+    return (mat(0, 3 * qb, f, d), mat(qb, 3 * qb + sb, f, d), mat(2 * qb, 3 * qb + 2 * sb, d, f))
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def dense_ffn(X: np.ndarray, W) -> np.ndarray:
+    wg, wu, wd = W
+    X = X.astype(np.float64)
+    return (silu(X @ wg.T) * (X @ wu.T)) @ wd.T
+
+
+def brute_force_layer(x, Wr, bias, experts, shared, wfmt, d, f, k, residual=None):
+    """Dense masked evaluation: all experts on all tokens, masked by the exact top-k."""
+    x = np.asarray(x, dtype=np.float32)
+    T = x.shape[0]
+    E = Wr.shape[0]
+    z = exact_logits(x, Wr, bias)
+    mask = np.zeros((T, E))
+    ids = []
+    for t in range(T):
+        top = exact_topk(z[t], k)
+        ids.append(top)
+        zf = logits_to_float([z[t][e] for e in top])
+        p = np.exp(zf - zf[0])
+        g = (p / p.sum()).astype(np.float32).astype(np.float64)
+        mask[t, top] = g
+    out = np.zeros((T, d)) if residual is None else residual.astype(np.float64).copy()
+    for e in range(E):
+        if not mask[:, e].any():
+            continue
+        out += mask[:, e:e + 1] * dense_ffn(x, decode_blob(experts[e], wfmt, d, f))
+    if shared is not None:
+        out += dense_ffn(x, decode_blob(shared, wfmt, d, f))
+    return np.array(ids, dtype=np.int32), out
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))
+
+
+def within_tolerance(got, ref, rel=2e-3, maxabs_frac=1e-2):
+    """Float parity bar: rel-L2 <= 2e-3 and max-abs <= 1e-2 * RMS(ref); exact if ref == 0."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    if rms == 0.0:
+        return bool(np.all(got == 0.0)), 0.0, float(np.max(np.abs(got))) if got.size else 0.0
+    r = rel_l2(got, ref)
+    m = float(np.max(np.abs(got - ref)))
+    return (r <= rel and m <= maxabs_frac * rms), r, m / rms
