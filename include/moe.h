@@ -1,0 +1,252 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse mixture-of-experts FFN library.
+ *
+ * The operation (Strata pages: "single RTX 5090 runs a 125B model", section on
+ * on-demand expert scheduling; "How Strata works", section on the three storage
+ * tiers): hidden states x [T, d] pass a router that picks the top-k of E
+ * experts per token; each picked expert is a SwiGLU FFN; the layer output is
+ * the gate-weighted sum of the picked experts' outputs plus an ungated,
+ * always-resident shared expert.  The model these pages describe has 24,576
+ * experts (512 per layer over 48 layers) with 10 picked per token.
+ *
+ *   out[t] = residual[t] + shared(x_t) + sum_{j<k} g[t,j] * FFN_{ids[t,j]}(x_t)
+ *   FFN(x) = Wd (silu(Wg x) * (Wu x)),   silu(z) = z / (1 + exp(-z))
+ *
+ * Call sequence for one layer (all enqueued on the caller's stream):
+ *   moe_route -> moe_permute -> [moe_quantize_act] -> moe_expert_ffn -> moe_combine
+ *
+ * Conventions
+ *  - Every tensor argument is a DEVICE pointer owned by the caller unless the
+ *    argument says "host".  The library never frees caller memory and never
+ *    allocates in the per-layer calls; scratch comes from a caller-provided
+ *    workspace sized by moe_workspace_size.
+ *  - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *    and return without synchronising; no call reads device data back to the
+ *    host.  Asynchronous kernel faults surface at the caller's next sync.
+ *  - Arguments are validated before any HIP call.  Return value: MOE_OK or an
+ *    MOE_ERR_* status; on MOE_ERR_HIP, moe_last_hip_error() gives the
+ *    hipError_t of the failing runtime call.  No C++ exception crosses the ABI.
+ *  - Row-major layouts; int32 indices; T == 0 is a valid no-op.
+ *  - Shape limits: d % 128 == 0, f % 128 == 0, 1 <= k <= 64, k <= E <= 1024.
+ *  - Not thread-safe for concurrent calls that share a workspace or a cache
+ *    handle; otherwise reentrant.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_VERSION 10000
+
+typedef void* moe_stream_t; /* hipStream_t */
+typedef void* moe_event_t;  /* hipEvent_t  */
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1    /* null pointer, bad shape, k > E, unsupported dtype value */
+#define MOE_ERR_UNSUPPORTED 2    /* valid request this build does not implement */
+#define MOE_ERR_HIP 3            /* a HIP runtime call failed; see moe_last_hip_error */
+#define MOE_ERR_NO_MEMORY 4      /* workspace too small, or host bookkeeping allocation failed */
+#define MOE_ERR_CACHE_CAPACITY 5 /* slot pool or staging buffer too small for the request */
+
+/* element types of activations */
+#define MOE_DT_F32 0
+#define MOE_DT_BF16 1
+#define MOE_DT_F16 2
+
+/* expert weight formats: block-32 quantisation along each row (the reduction
+ * axis), one IEEE fp16 scale per 32 weights; int4 values are offset-binary
+ * nibbles u = q + 8 (element 2i in the low nibble), int8 values are
+ * two's complement. */
+#define MOE_WFMT_I4B32 4
+#define MOE_WFMT_I8B32 8
+
+/* activation modes of the expert FFN */
+#define MOE_ACT_FLOAT 0 /* fp32 accumulation of dequantised weights x activations */
+#define MOE_ACT_Q8 1    /* int8 activations per 32-feature block, int8 matrix cores */
+
+int moe_version(void);
+/* hipError_t of the most recent failing HIP call made by this thread (0 = none). */
+int moe_last_hip_error(void);
+/* Static string naming a status code. */
+const char* moe_status_string(int status);
+
+/*
+ * Size in bytes of one expert blob (canonical or packed; both have the same
+ * size): three matrices Wg [f,d], Wu [f,d], Wd [d,f] of block-32 quants
+ * followed by their fp16 scales.  Canonical blob layout, all row-major:
+ *   [qg][qu][qd][sg : f x d/32][su : f x d/32][sd : d x f/32]
+ * Returns 0 for an invalid format or shape.
+ */
+size_t moe_expert_bytes(int wfmt, int d, int f);
+
+/*
+ * Repack n canonical expert blobs (device, contiguous [n, expert_bytes]) into
+ * the kernel-native tiled layout consumed by moe_expert_ffn (device `dst`,
+ * same size, must not alias `src`).  One-time, untimed preparation step.
+ * The packed layout is private to this library version.
+ */
+int moe_pack_experts(const void* src, void* dst, int n, int wfmt, int d, int f, moe_stream_t stream);
+/* Inverse of moe_pack_experts (for verification): packed -> canonical. */
+int moe_unpack_experts(const void* src, void* dst, int n, int wfmt, int d, int f, moe_stream_t stream);
+
+/*
+ * Workspace bytes needed by route, permute and expert_ffn for a layer with
+ * these shapes (the same workspace may be passed to all three calls of one
+ * layer; calls on one stream are ordered).  Writes *bytes.
+ */
+int moe_workspace_size(int T, int d, int f, int E, int k, int act_mode, size_t* bytes);
+
+/*
+ * Router: logits z[t,e] = sum_i x[t,i] * Wr[e,i] (+ bias[e]) and top-k
+ * selection, as described on "single RTX 5090 runs a 125B model" (on-demand
+ * expert scheduling: a light gating network picks the top-K experts).
+ *   x     [T, d]   x_dtype MOE_DT_F32 or MOE_DT_BF16
+ *   Wr    [E, d]   fp32
+ *   bias  [E]      fp32 or NULL (added to the logits before selection)
+ *   ids   [T, k]   int32 out: experts in descending-logit order; equal logits
+ *                  are ordered by ascending expert index.  The ranking is that
+ *                  of the exact real-valued logits (products of the fp32/bf16
+ *                  inputs are exact in double; sums are double).
+ *   gates [T, k]   fp32 out: softmax over the k selected logits (equal to the
+ *                  full softmax renormalised over the top k).
+ */
+int moe_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
+              int32_t* ids, float* gates, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Stable grouping of the T*k routing slots by expert (flat slot f = t*k + j).
+ *   counts     [E]      number of slots routed to each expert
+ *   offsets    [E+1]    exclusive prefix sum of counts (offsets[E] = T*k)
+ *   sorted_idx [T*k]    slots in (expert, slot) order: expert-major, ascending
+ *                       slot (hence ascending token) within an expert
+ *   dest       [T*k]    position of slot f in sorted_idx (inverse permutation)
+ *   active     [E+1]    work list: active[0] = number of experts with
+ *                       count > 0, active[1..] = those experts, ascending
+ * Integer outputs; bit-exact and deterministic.  Ids outside [0, E) are
+ * ignored (not counted, not placed).
+ */
+int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
+                int32_t* dest, int32_t* active, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * int8 activation quantisation (MOE_ACT_Q8 input): per token, per 32
+ * consecutive features, s = amax / 127 (fp32, IEEE division),
+ * q = clamp(rint(x / s), -127, 127) with ties to even; an all-zero block gives
+ * s = 0 and q = 0.  x [T, d] (F32 or BF16) -> xq [T, d] int8, sx [T, d/32] fp32.
+ */
+int moe_quantize_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float* sx, moe_stream_t stream);
+
+/* Arguments of moe_expert_ffn. */
+typedef struct moe_ffn_args {
+    int T, d, f, E, k;
+    int wfmt;     /* MOE_WFMT_* of every expert blob */
+    int act_mode; /* MOE_ACT_FLOAT or MOE_ACT_Q8 */
+    /* MOE_ACT_FLOAT input */
+    const void* x; /* [T, d] */
+    int x_dtype;   /* MOE_DT_F32 or MOE_DT_BF16 */
+    /* MOE_ACT_Q8 input, from moe_quantize_act */
+    const int8_t* xq; /* [T, d] */
+    const float* sx;  /* [T, d/32] */
+    /* experts: DEVICE array [E] of device pointers to PACKED blobs (pool
+       slots and staging buffers are interchangeable) */
+    const void* const* expert_ptrs;
+    /* from moe_permute */
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* sorted_idx;
+    const int32_t* active;
+    /* routed expert outputs, row p = position p of sorted_idx, ungated */
+    void* y_perm; /* [T*k, d] */
+    int y_dtype;  /* MOE_DT_F32 or MOE_DT_F16 */
+    /* shared expert (NULL = none): packed blob, output [T, d] fp32 */
+    const void* shared_blob;
+    float* y_shared;
+    void* ws;
+    size_t ws_bytes;
+} moe_ffn_args;
+
+/*
+ * Grouped SwiGLU expert FFN over the rows grouped by moe_permute, plus the
+ * shared expert over all T tokens.  Block-32 weights are dequantised in
+ * registers.  MOE_ACT_FLOAT: fp32 accumulation (fp16 matrix-core products of
+ * exact weight integers and fp16-rounded activations, per-block scales applied
+ * in fp32).  MOE_ACT_Q8: int8 x int8 matrix cores with exact per-block
+ * integer sums; the SwiGLU intermediate is requantised to int8 per 32 features
+ * before the down projection.
+ */
+int moe_expert_ffn(const moe_ffn_args* args, moe_stream_t stream);
+
+/*
+ * Combine: out[t] = residual[t] + y_shared[t] + sum_{j<k} gates[t,j] * y_perm[dest[t*k+j]],
+ * summed in j order (deterministic).
+ *   y_perm [T*k, d] (y_dtype F32 or F16), dest [T*k], gates [T, k],
+ *   y_shared [T, d] fp32 or NULL, residual [T, d] fp32 or NULL, out [T, d] fp32.
+ * out may alias residual.
+ */
+int moe_combine(const void* y_perm, int y_dtype, const int32_t* dest, const float* gates, const float* y_shared,
+                const float* residual, int T, int k, int d, float* out, moe_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Expert slot cache ("How Strata works", section on the adaptive expert cache:
+ * the most-used ~4,500 experts by a usage ranking are loaded into GPU memory;
+ * "Strata benchmarks", prefill optimisation table: next-layer experts stream
+ * over PCIe while the current layer computes).
+ *
+ * A handle holds host bookkeeping only: which global expert id (layer*E + e)
+ * occupies which slot of a caller-owned device pool, and pinned host staging
+ * of per-layer pointer tables.  Misses of a layer are copied from caller-owned
+ * pinned host blobs into a caller-owned device staging buffer on a side
+ * stream, after which the layer's device pointer table [E] is rewritten so
+ * that moe_expert_ffn reads hits from the pool and misses from staging.
+ * ------------------------------------------------------------------------- */
+typedef struct moe_cache moe_cache;
+
+/*
+ *   dev_pool     device memory of n_slots * expert_bytes (caller-owned)
+ *   dev_staging  device memory of n_staging_bufs * staging_slots * expert_bytes
+ *   n_staging_bufs  number of staging buffers used in rotation (>= 1)
+ */
+int moe_cache_create(moe_cache** cache, int n_layers, int E, int n_slots, size_t expert_bytes, void* dev_pool,
+                     void* dev_staging, int n_staging_bufs, int staging_slots);
+int moe_cache_destroy(moe_cache* cache);
+
+/*
+ * Make the given global ids resident: slot i receives global_ids[i] (host
+ * array, n <= n_slots, ids distinct and in [0, n_layers*E)), copied from the
+ * host blob host_src[i] (host array of host pointers; pinned memory gives
+ * asynchronous copies).  Enqueued on `stream`.
+ */
+int moe_cache_set_resident(moe_cache* cache, const int32_t* global_ids, int n, const void* const* host_src,
+                           moe_stream_t stream);
+
+/*
+ * Host-side lookup for one layer: the experts of `layer` that are not
+ * resident, ascending (miss_ids host array with room for E), their count in
+ * *n_miss, and the resident ones (hit_ids, may be NULL) with *n_hit.
+ */
+int moe_cache_lookup(const moe_cache* cache, int layer, int32_t* hit_ids, int* n_hit, int32_t* miss_ids,
+                     int* n_miss);
+
+/*
+ * Stage one layer: copy each missing expert of `layer` (ascending id) from its
+ * host blob host_src[e] (host array [E] of pinned host pointers; only the
+ * misses are read) into consecutive slots of staging buffer `buf`, then write
+ * the layer's device pointer table dev_table [E] (hits -> pool slots, misses ->
+ * staging slots), all on `stream`, and record `done` (may be NULL) on it.
+ * Returns MOE_ERR_CACHE_CAPACITY if the misses exceed staging_slots.  The
+ * caller must not reuse staging buffer `buf` before the compute that reads it
+ * has finished (order with events).
+ */
+int moe_cache_stage(moe_cache* cache, int layer, int buf, const void* const* host_src, void** dev_table,
+                    moe_stream_t stream, moe_event_t done);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

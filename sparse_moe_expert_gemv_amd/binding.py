@@ -1,0 +1,239 @@
+"""Thin ctypes binding of libmoe.so (the C ABI declared in include/moe.h).
+
+Argument marshalling only: every step of the MoE layer runs in the library's
+HIP kernels.  Tensors are torch device tensors (PyTorch supplies device memory
+and streams); functions take an optional ``stream`` (a torch.cuda.Stream,
+default: the current stream).  If the library is not built, or a call returns
+an error status, a RuntimeError is raised -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_HIP = 3
+MOE_ERR_NO_MEMORY = 4
+MOE_ERR_CACHE_CAPACITY = 5
+MOE_DT_F32, MOE_DT_BF16, MOE_DT_F16 = 0, 1, 2
+MOE_WFMT_I4B32, MOE_WFMT_I8B32 = 4, 8
+MOE_ACT_FLOAT, MOE_ACT_Q8 = 0, 1
+
+EXPORTED = [
+    "moe_version", "moe_last_hip_error", "moe_status_string", "moe_expert_bytes", "moe_pack_experts",
+    "moe_unpack_experts", "moe_workspace_size", "moe_route", "moe_permute", "moe_quantize_act", "moe_expert_ffn",
+    "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
+    "moe_cache_stage",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, hip_err):
+        self.status = status
+        self.hip_error = hip_err
+        super().__init__("%s failed: status %d (%s), hipError %d" % (fn, status, _status_name(status), hip_err))
+
+
+class FfnArgs(C.Structure):
+    _fields_ = [
+        ("T", C.c_int), ("d", C.c_int), ("f", C.c_int), ("E", C.c_int), ("k", C.c_int),
+        ("wfmt", C.c_int), ("act_mode", C.c_int),
+        ("x", C.c_void_p), ("x_dtype", C.c_int),
+        ("xq", C.c_void_p), ("sx", C.c_void_p),
+        ("expert_ptrs", C.c_void_p),
+        ("counts", C.c_void_p), ("offsets", C.c_void_p), ("sorted_idx", C.c_void_p), ("active", C.c_void_p),
+        ("y_perm", C.c_void_p), ("y_dtype", C.c_int),
+        ("shared_blob", C.c_void_p), ("y_shared", C.c_void_p),
+        ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmoe.so not built: run `python -m sparse_moe_expert_gemv_amd.build` "
+                               "(or __graft_entry__.build()) first")
+        L = C.CDLL(LIB_PATH)
+        P, I, S = C.c_void_p, C.c_int, C.c_size_t
+        sig = {
+            "moe_version": ([], I), "moe_last_hip_error": ([], I), "moe_status_string": ([I], C.c_char_p),
+            "moe_expert_bytes": ([I, I, I], S),
+            "moe_pack_experts": ([P, P, I, I, I, I, P], I), "moe_unpack_experts": ([P, P, I, I, I, I, P], I),
+            "moe_workspace_size": ([I, I, I, I, I, I, C.POINTER(S)], I),
+            "moe_route": ([P, I, I, I, P, P, I, I, P, P, P, S, P], I),
+            "moe_permute": ([P, I, I, I, P, P, P, P, P, P, S, P], I),
+            "moe_quantize_act": ([P, I, I, I, P, P, P], I),
+            "moe_expert_ffn": ([C.POINTER(FfnArgs), P], I),
+            "moe_combine": ([P, I, P, P, P, P, I, I, I, P, P], I),
+            "moe_cache_create": ([C.POINTER(P), I, I, I, S, P, P, I, I], I),
+            "moe_cache_destroy": ([P], I),
+            "moe_cache_set_resident": ([P, P, I, P, P], I),
+            "moe_cache_lookup": ([P, I, P, C.POINTER(I), P, C.POINTER(I)], I),
+            "moe_cache_stage": ([P, I, I, P, P, P, P], I),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _status_name(st):
+    try:
+        return lib().moe_status_string(st).decode()
+    except Exception:  # noqa: BLE001 - only used for messages
+        return "?"
+
+
+def _check(name, st):
+    if st != MOE_OK:
+        raise MoeError(name, st, lib().moe_last_hip_error())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _xdtype(t):
+    import torch
+    if t.dtype == torch.float32:
+        return MOE_DT_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_DT_BF16
+    raise ValueError("hidden states must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ydtype(t):
+    import torch
+    return {torch.float32: MOE_DT_F32, torch.float16: MOE_DT_F16}[t.dtype]
+
+
+# ---------------------------------------------------------------- calls ----
+
+def moe_version() -> int:
+    return lib().moe_version()
+
+
+def moe_expert_bytes(wfmt: int, d: int, f: int) -> int:
+    return int(lib().moe_expert_bytes(wfmt, d, f))
+
+
+def moe_workspace_size(T, d, f, E, k, act_mode) -> int:
+    out = C.c_size_t(0)
+    _check("moe_workspace_size", lib().moe_workspace_size(T, d, f, E, k, act_mode, C.byref(out)))
+    return out.value
+
+
+def moe_pack_experts(src, dst, n, wfmt, d, f, stream=None):
+    _check("moe_pack_experts", lib().moe_pack_experts(_ptr(src), _ptr(dst), n, wfmt, d, f, _stream(stream)))
+
+
+def moe_unpack_experts(src, dst, n, wfmt, d, f, stream=None):
+    _check("moe_unpack_experts", lib().moe_unpack_experts(_ptr(src), _ptr(dst), n, wfmt, d, f, _stream(stream)))
+
+
+def moe_route(x, Wr, bias, k, ids, gates, ws, stream=None):
+    T, d = x.shape
+    E = Wr.shape[0]
+    _check("moe_route", lib().moe_route(_ptr(x), _xdtype(x), T, d, _ptr(Wr), _ptr(bias), E, k, _ptr(ids),
+                                        _ptr(gates), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_permute(ids, E, counts, offsets, sorted_idx, dest, active, ws, stream=None):
+    T, k = ids.shape
+    _check("moe_permute", lib().moe_permute(_ptr(ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(sorted_idx),
+                                            _ptr(dest), _ptr(active), _ptr(ws), ws.numel() * ws.element_size(),
+                                            _stream(stream)))
+
+
+def moe_quantize_act(x, xq, sx, stream=None):
+    T, d = x.shape
+    _check("moe_quantize_act", lib().moe_quantize_act(_ptr(x), _xdtype(x), T, d, _ptr(xq), _ptr(sx),
+                                                      _stream(stream)))
+
+
+def moe_expert_ffn(*, T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offsets, sorted_idx, active, y_perm,
+                   ws, x=None, xq=None, sx=None, shared_blob=None, y_shared=None, stream=None):
+    a = FfnArgs()
+    a.T, a.d, a.f, a.E, a.k = T, d, f, E, k
+    a.wfmt, a.act_mode = wfmt, act_mode
+    a.x = None if x is None else x.data_ptr()
+    a.x_dtype = MOE_DT_F32 if x is None else _xdtype(x)
+    a.xq = None if xq is None else xq.data_ptr()
+    a.sx = None if sx is None else sx.data_ptr()
+    a.expert_ptrs = expert_ptrs.data_ptr()
+    a.counts, a.offsets = counts.data_ptr(), offsets.data_ptr()
+    a.sorted_idx, a.active = sorted_idx.data_ptr(), active.data_ptr()
+    a.y_perm, a.y_dtype = y_perm.data_ptr(), _ydtype(y_perm)
+    a.shared_blob = None if shared_blob is None else shared_blob.data_ptr()
+    a.y_shared = None if y_shared is None else y_shared.data_ptr()
+    a.ws, a.ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
+    _check("moe_expert_ffn", lib().moe_expert_ffn(C.byref(a), _stream(stream)))
+
+
+def moe_combine(y_perm, dest, gates, y_shared, residual, out, stream=None):
+    T, k = gates.shape
+    d = out.shape[1]
+    _check("moe_combine", lib().moe_combine(_ptr(y_perm), _ydtype(y_perm), _ptr(dest), _ptr(gates),
+                                            _ptr(y_shared), _ptr(residual), T, k, d, _ptr(out), _stream(stream)))
+
+
+# ---------------------------------------------------------- slot cache ----
+
+class SlotCache:
+    """Handle around moe_cache_* (host bookkeeping; device memory is the caller's)."""
+
+    def __init__(self, n_layers, E, n_slots, expert_bytes, dev_pool, dev_staging, n_staging_bufs, staging_slots):
+        h = C.c_void_p()
+        _check("moe_cache_create", lib().moe_cache_create(C.byref(h), n_layers, E, n_slots, expert_bytes,
+                                                          _ptr(dev_pool), _ptr(dev_staging), n_staging_bufs,
+                                                          staging_slots))
+        self.h = h
+        self.E = E
+
+    def set_resident(self, global_ids, host_ptrs, stream=None):
+        n = len(global_ids)
+        ids = (C.c_int32 * n)(*[int(g) for g in global_ids])
+        src = (C.c_void_p * n)(*[int(p) for p in host_ptrs])
+        _check("moe_cache_set_resident", lib().moe_cache_set_resident(self.h, ids, n, src, _stream(stream)))
+
+    def lookup(self, layer):
+        hit = (C.c_int32 * self.E)()
+        miss = (C.c_int32 * self.E)()
+        nh, nm = C.c_int(), C.c_int()
+        _check("moe_cache_lookup", lib().moe_cache_lookup(self.h, layer, hit, C.byref(nh), miss, C.byref(nm)))
+        return list(hit[:nh.value]), list(miss[:nm.value])
+
+    def stage(self, layer, buf, host_ptrs, dev_table, stream=None, done_event=None):
+        src = (C.c_void_p * self.E)(*[int(p) for p in host_ptrs])
+        ev = None if done_event is None else C.c_void_p(done_event.cuda_event)
+        _check("moe_cache_stage", lib().moe_cache_stage(self.h, layer, buf, src, _ptr(dev_table), _stream(stream),
+                                                        ev))
+
+    def close(self):
+        if self.h:
+            lib().moe_cache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001
+            pass

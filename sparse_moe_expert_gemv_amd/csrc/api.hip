@@ -1,0 +1,166 @@
+// C ABI entry points: argument validation (before any HIP call), workspace
+// carve-up and dispatch to the kernel launchers.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace moe {
+
+static thread_local int g_last_hip_error = 0;
+
+void set_last_hip_error(hipError_t e) { g_last_hip_error = (int)e; }
+
+int check_launch() {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_last_hip_error(e);
+        return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+static size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* base, Workspace* w) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + off : nullptr;
+        off = align_up(off + bytes);
+        return p;
+    };
+    const size_t rows = (size_t)T * k + (size_t)T;
+    const size_t nch = ((size_t)T * k + kPermChunk - 1) / kPermChunk;
+    w->logits = reinterpret_cast<double*>(take(sizeof(double) * (size_t)T * E));
+    w->route_bytes = off;
+    w->hist = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * std::max<size_t>(nch, 1) * E));
+    w->permute_bytes = off;
+    if (act_mode == MOE_ACT_Q8) {
+        w->tiles = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (2 * q8_tile_capacity(T, k, E) + 4)));
+        w->x16 = nullptr;
+        w->h = take(rows * (size_t)f);
+        w->hs = reinterpret_cast<float*>(take(sizeof(float) * rows * (size_t)(f / 32)));
+    } else {
+        w->tiles = nullptr;
+        w->x16 = reinterpret_cast<_Float16*>(take(sizeof(_Float16) * (size_t)T * d));
+        w->h = take(sizeof(_Float16) * rows * (size_t)f);
+        w->hs = nullptr;
+    }
+    w->bytes = off;
+}
+
+static bool shape_ok(int d, int E, int k) { return d > 0 && d % 128 == 0 && k >= 1 && k <= 64 && E >= k && E <= 1024; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_version(void) { return MOE_VERSION; }
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        case MOE_ERR_NO_MEMORY: return "MOE_ERR_NO_MEMORY";
+        case MOE_ERR_CACHE_CAPACITY: return "MOE_ERR_CACHE_CAPACITY";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+size_t moe_expert_bytes(int wfmt, int d, int f) {
+    if ((wfmt != MOE_WFMT_I4B32 && wfmt != MOE_WFMT_I8B32) || d <= 0 || f <= 0 || d % 32 || f % 32) return 0;
+    return canon_layout(wfmt, d, f).total;
+}
+
+static int pack_common(const void* src, void* dst, int n, int wfmt, int d, int f, bool unpack, moe_stream_t s) {
+    if (n < 0 || (wfmt != MOE_WFMT_I4B32 && wfmt != MOE_WFMT_I8B32) || d <= 0 || f <= 0 || d % 128 || f % 128)
+        return MOE_ERR_INVALID_ARG;
+    if (n == 0) return MOE_OK;
+    if (!src || !dst || src == dst || n > 65535) return MOE_ERR_INVALID_ARG;
+    return launch_pack(src, dst, n, wfmt, d, f, unpack, as_stream(s));
+}
+
+int moe_pack_experts(const void* src, void* dst, int n, int wfmt, int d, int f, moe_stream_t s) {
+    return pack_common(src, dst, n, wfmt, d, f, false, s);
+}
+
+int moe_unpack_experts(const void* src, void* dst, int n, int wfmt, int d, int f, moe_stream_t s) {
+    return pack_common(src, dst, n, wfmt, d, f, true, s);
+}
+
+int moe_workspace_size(int T, int d, int f, int E, int k, int act_mode, size_t* bytes) {
+    if (!bytes || T < 0 || !shape_ok(d, E, k) || f <= 0 || f % 128 ||
+        (act_mode != MOE_ACT_FLOAT && act_mode != MOE_ACT_Q8))
+        return MOE_ERR_INVALID_ARG;
+    Workspace w;
+    workspace_layout(T, d, f, E, k, act_mode, nullptr, &w);
+    *bytes = w.bytes;
+    return MOE_OK;
+}
+
+int moe_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
+              int32_t* ids, float* gates, void* ws, size_t ws_bytes, moe_stream_t s) {
+    if (T < 0 || !shape_ok(d, E, k) || (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16)) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !Wr || !ids || !gates || !ws) return MOE_ERR_INVALID_ARG;
+    Workspace w;
+    workspace_layout(T, d, 128, E, k, MOE_ACT_FLOAT, (char*)ws, &w);
+    if (ws_bytes < w.route_bytes) return MOE_ERR_NO_MEMORY;
+    return launch_route(x, x_dtype, T, d, Wr, bias, E, k, ids, gates, w.logits, as_stream(s));
+}
+
+int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
+                int32_t* dest, int32_t* active, void* ws, size_t ws_bytes, moe_stream_t s) {
+    if (T < 0 || k < 1 || k > 64 || E < k || E > 1024 || (long)T * k > (1l << 30)) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!ids || !counts || !offsets || !sorted_idx || !dest || !active || !ws) return MOE_ERR_INVALID_ARG;
+    Workspace w;
+    workspace_layout(T, 128, 128, E, k, MOE_ACT_FLOAT, (char*)ws, &w);
+    if (ws_bytes < w.permute_bytes) return MOE_ERR_NO_MEMORY;
+    return launch_permute(ids, T, k, E, counts, offsets, sorted_idx, dest, active, w.hist, as_stream(s));
+}
+
+int moe_quantize_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float* sx, moe_stream_t s) {
+    if (T < 0 || d <= 0 || d % 32 || (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16)) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !xq || !sx) return MOE_ERR_INVALID_ARG;
+    return launch_quant_act(x, x_dtype, T, d, xq, sx, as_stream(s));
+}
+
+int moe_expert_ffn(const moe_ffn_args* a, moe_stream_t s) {
+    if (!a) return MOE_ERR_INVALID_ARG;
+    if (a->T < 0 || !shape_ok(a->d, a->E, a->k) || a->f <= 0 || a->f % 128 ||
+        (a->wfmt != MOE_WFMT_I4B32 && a->wfmt != MOE_WFMT_I8B32) ||
+        (a->act_mode != MOE_ACT_FLOAT && a->act_mode != MOE_ACT_Q8) ||
+        (a->y_dtype != MOE_DT_F32 && a->y_dtype != MOE_DT_F16))
+        return MOE_ERR_INVALID_ARG;
+    if (a->T == 0) return MOE_OK;
+    if (!a->expert_ptrs || !a->counts || !a->offsets || !a->sorted_idx || !a->active || !a->y_perm || !a->ws)
+        return MOE_ERR_INVALID_ARG;
+    if (a->shared_blob && !a->y_shared) return MOE_ERR_INVALID_ARG;
+    if (a->act_mode == MOE_ACT_FLOAT) {
+        if (!a->x || (a->x_dtype != MOE_DT_F32 && a->x_dtype != MOE_DT_BF16)) return MOE_ERR_INVALID_ARG;
+    } else {
+        if (!a->xq || !a->sx) return MOE_ERR_INVALID_ARG;
+    }
+    Workspace w;
+    workspace_layout(a->T, a->d, a->f, a->E, a->k, a->act_mode, (char*)a->ws, &w);
+    if (a->ws_bytes < w.bytes) return MOE_ERR_NO_MEMORY;
+    return a->act_mode == MOE_ACT_FLOAT ? launch_ffn_float(a, w, as_stream(s)) : launch_ffn_q8(a, w, as_stream(s));
+}
+
+int moe_combine(const void* y_perm, int y_dtype, const int32_t* dest, const float* gates, const float* y_shared,
+                const float* residual, int T, int k, int d, float* out, moe_stream_t s) {
+    if (T < 0 || k < 1 || d <= 0 || d % 4 || (y_dtype != MOE_DT_F32 && y_dtype != MOE_DT_F16))
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!y_perm || !dest || !gates || !out) return MOE_ERR_INVALID_ARG;
+    return launch_combine(y_perm, y_dtype, dest, gates, y_shared, residual, T, k, d, out, as_stream(s));
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Internal definitions shared by the library's HIP sources (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---- packed expert layout --------------------------------------------------
+// Every matrix W [R, K] (R output rows, K reduction, block-32 along K) is stored
+// as tiles of 16 rows x 1 KiB of quants, tile (rs, kt) at ((rs * nkt) + kt) KiB:
+//   int4: a tile covers 128 k (4 blocks).  Lane l of a wave (row rs*16 + l%16,
+//         k sub-range 8*(l/16) .. +7 inside each block) owns 16 bytes: dword i
+//         holds block 4*kt+i as 8 offset-binary nibbles in the order
+//         [k0 k2 k4 k6 k1 k3 k5 k7] (nibble j at bits 4j), so that
+//         (w >> 4s) & 0x000F000F yields the pair (k_2s, k_2s+1) in two 16-bit
+//         halves.
+//   int8: a tile covers 64 k (2 blocks).  Lane l owns 16 bytes: bytes 0..7 are
+//         k = 8*(l/16)+0..7 of block 2*kt, bytes 8..15 the same of block
+//         2*kt+1, stored offset-binary (q + 128).
+// Scales follow all quants, per matrix, as fp16 tiles [16 rows][blocks/tile]
+// in the same (rs, kt) order (128 B per int4 tile, 64 B per int8 tile).
+// Blob: [Wg tiles][Wu tiles][Wd tiles][Wg scales][Wu scales][Wd scales].
+struct MatLayout {
+    size_t qoff, soff;  // byte offsets in the blob
+    int R, K;           // rows, reduction length
+    int nkt;            // k tiles per 16-row strip
+};
+
+struct ExpertLayout {
+    MatLayout g, u, dn;
+    size_t total;
+};
+
+__host__ __device__ inline int k_per_tile(int wfmt) { return wfmt == MOE_WFMT_I4B32 ? 128 : 64; }
+__host__ __device__ inline int scale_tile_bytes(int wfmt) { return wfmt == MOE_WFMT_I4B32 ? 128 : 64; }
+
+__host__ __device__ inline ExpertLayout expert_layout(int wfmt, int d, int f) {
+    ExpertLayout L;
+    const size_t n = (size_t)d * f;
+    const size_t qb = wfmt == MOE_WFMT_I4B32 ? n / 2 : n;
+    const size_t sb = (n / 32) * 2;
+    const int kpt = k_per_tile(wfmt);
+    L.g = {0, 3 * qb, f, d, d / kpt};
+    L.u = {qb, 3 * qb + sb, f, d, d / kpt};
+    L.dn = {2 * qb, 3 * qb + 2 * sb, d, f, f / kpt};
+    L.total = 3 * qb + 3 * sb;
+    return L;
+}
+
+// canonical layout offsets (row-major quants, row-major scales)
+struct CanonLayout {
+    size_t qg, qu, qd, sg, su, sd, total;
+};
+__host__ __device__ inline CanonLayout canon_layout(int wfmt, int d, int f) {
+    CanonLayout C;
+    const size_t n = (size_t)d * f;
+    const size_t qb = wfmt == MOE_WFMT_I4B32 ? n / 2 : n;
+    const size_t sb = (n / 32) * 2;
+    C.qg = 0; C.qu = qb; C.qd = 2 * qb;
+    C.sg = 3 * qb; C.su = C.sg + sb; C.sd = C.su + sb;
+    C.total = C.sd + sb;
+    return C;
+}
+
+// ---- vector types -----------------------------------------------------------
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int16v __attribute__((ext_vector_type(16)));
+typedef unsigned uint4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ---- error plumbing -----------------------------------------------------------
+void set_last_hip_error(hipError_t e);
+int check_launch();  // MOE_OK or MOE_ERR_HIP after a kernel launch
+
+inline hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---- workspace carve-up -------------------------------------------------------
+// Regions are laid out in this order so that route and permute only need a
+// prefix of the workspace.
+struct Workspace {
+    double* logits;   // [T, E]                         route
+    int32_t* hist;    // [ceil(T*k / kPermChunk), E]    permute
+    int32_t* tiles;   // q8 tile list (int2) + count    ffn
+    _Float16* x16;    // float mode: activations as fp16 [T, d]
+    void* h;          // SwiGLU intermediate, rows T*k + T: fp16 (float mode) or int8 (q8)
+    float* hs;        // q8: [T*k + T, f/32] block scales of h
+    size_t route_bytes, permute_bytes, bytes;
+};
+constexpr int kPermChunk = 1024;
+// Fills w (pointers relative to base, which may be null to size only).
+void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* base, Workspace* w);
+
+// ---- launchers (defined in the .hip files) -----------------------------------
+int launch_pack(const void* src, void* dst, int n, int wfmt, int d, int f, bool unpack, hipStream_t s);
+int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
+                 int32_t* ids, float* gates, double* logits, hipStream_t s);
+int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
+                   int32_t* dest, int32_t* active, int32_t* hist, hipStream_t s);
+int launch_quant_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float* sx, hipStream_t s);
+int launch_ffn_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s);
+int launch_ffn_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s);
+size_t q8_tile_capacity(int T, int k, int E);  // int2 entries of the q8 tile list
+int launch_combine(const void* y_perm, int y_dtype, const int32_t* dest, const float* gates, const float* y_shared,
+                   const float* residual, int T, int k, int d, float* out, hipStream_t s);
+
+}  // namespace moe

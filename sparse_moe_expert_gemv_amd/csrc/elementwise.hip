@@ -1,0 +1,100 @@
+// Activation quantisation (int8 per 32 features) and the weighted combine.
+#include "common.hpp"
+
+namespace moe {
+
+// One thread per (token, 32-feature block).  s = amax / 127 (IEEE fp32
+// division), q = clamp(rint(x / s), -127, 127) with ties to even; s = 0 and
+// q = 0 for an all-zero block.  Bit-exact by construction: max, division and
+// round-to-nearest-even are exact operations on identical inputs.
+template <typename XT>
+__global__ __launch_bounds__(256) void quant_act(const XT* __restrict__ x, int T, int d, int8_t* __restrict__ xq,
+                                                 float* __restrict__ sx) {
+    const int nb = d / 32;
+    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (long)T * nb) return;
+    const size_t base = (size_t)gid * 32;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        if constexpr (sizeof(XT) == 4) v[i] = x[base + i];
+        else v[i] = bf16_bits_to_float(x[base + i]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float s = amax / 127.0f;
+    sx[gid] = s;
+    uint32_t packed[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int q = 0;
+            if (s != 0.0f) q = (int)fminf(fmaxf(rintf(v[4 * w + j] / s), -127.0f), 127.0f);
+            word |= ((uint32_t)q & 0xffu) << (8 * j);
+        }
+        packed[w] = word;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(xq + base);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+}
+
+int launch_quant_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float* sx, hipStream_t s) {
+    const long n = (long)T * (d / 32);
+    if (n == 0) return MOE_OK;
+    const int grid = (int)((n + 255) / 256);
+    if (x_dtype == MOE_DT_F32) quant_act<float><<<grid, 256, 0, s>>>((const float*)x, T, d, xq, sx);
+    else quant_act<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)x, T, d, xq, sx);
+    return check_launch();
+}
+
+// out[t, o] = residual + y_shared + sum_j gates[t, j] * y_perm[dest[t*k + j], o]; j ascending.
+// One thread per (token, 4 consecutive features).
+template <typename YT>
+__global__ __launch_bounds__(256) void combine(const YT* __restrict__ y, const int32_t* __restrict__ dest,
+                                               const float* __restrict__ gates, const float* __restrict__ ysh,
+                                               const float* residual, int T, int k, int d, float* out) {
+    const int q = d / 4;
+    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (long)T * q) return;
+    const int t = (int)(gid / q), o = (int)(gid % q) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (residual) acc = *reinterpret_cast<const float4*>(residual + (size_t)t * d + o);
+    if (ysh) {
+        const float4 v = *reinterpret_cast<const float4*>(ysh + (size_t)t * d + o);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    for (int j = 0; j < k; ++j) {
+        const float g = gates[(size_t)t * k + j];
+        const size_t row = (size_t)dest[(size_t)t * k + j] * d + o;
+        float4 v;
+        if constexpr (sizeof(YT) == 4) {
+            v = *reinterpret_cast<const float4*>(y + row);
+        } else {
+            const half2v* hp = reinterpret_cast<const half2v*>(y + row);
+            const half2v a = hp[0], b = hp[1];
+            v = make_float4((float)a.x, (float)a.y, (float)b.x, (float)b.y);
+        }
+        acc.x = fmaf(g, v.x, acc.x); acc.y = fmaf(g, v.y, acc.y);
+        acc.z = fmaf(g, v.z, acc.z); acc.w = fmaf(g, v.w, acc.w);
+    }
+    *reinterpret_cast<float4*>(out + (size_t)t * d + o) = acc;
+}
+
+int launch_combine(const void* y_perm, int y_dtype, const int32_t* dest, const float* gates, const float* y_shared,
+                   const float* residual, int T, int k, int d, float* out, hipStream_t s) {
+    const long n = (long)T * (d / 4);
+    if (n == 0) return MOE_OK;
+    const int grid = (int)((n + 255) / 256);
+    if (y_dtype == MOE_DT_F32)
+        combine<float><<<grid, 256, 0, s>>>((const float*)y_perm, dest, gates, y_shared, residual, T, k, d, out);
+    else
+        combine<_Float16><<<grid, 256, 0, s>>>((const _Float16*)y_perm, dest, gates, y_shared, residual, T, k, d,
+                                                out);
+    return check_launch();
+}
+
+}  // namespace moe

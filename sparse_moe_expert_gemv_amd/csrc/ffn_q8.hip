@@ -1,0 +1,360 @@
+// Grouped SwiGLU expert FFN, int8-activation mode (prefill chunks).
+//
+// Per expert, the tokens routed to it form a dense M x K tile (about 160 rows
+// for an 8,192-token chunk over 512 experts with top-10), so both projections
+// run on int8 matrix cores: v_mfma_i32_32x32x32_i8, one instruction per
+// 32-wide quantisation block (A = 32 tokens x 32 k, B = 32 k x 32 weight
+// rows).  The Strata pages report moving expert matmuls to an int8
+// tensor-core kernel that needs no dequantisation ("Strata benchmarks",
+// prefill optimisation table); here the int4 weights become int8 while they
+// are staged in LDS, once per workgroup and k-chunk.
+//
+// Block sums are exact integers |P| < 2^22.  The MFMA accumulator is seeded
+// with the bit pattern of 1.5 * 2^23, so the int32 result read as fp32 is
+// exactly 1.5 * 2^23 + P.  With the weight row's block scale sw constant per
+// lane, t = fma(D, sw, -1.5 * 2^23 * sw) = sw * P (one rounding; the constant
+// is exact), then acc += sx * t with the token's block scale: two VALU
+// operations per output and block.
+//
+// gate/up: a workgroup owns 64 features of f (gate rows + up rows = 128
+// weight rows) for up to 128 tokens of one expert (one 32-token m-tile per
+// wavefront), and writes h = silu(g) * u requantised to int8 per 32 features
+// (per-token scale amax/127, ties-to-even), the down projection's A operand.
+// down: a workgroup owns 128 output rows for the same token tile.
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kMG = 128;        // tokens per tile (4 m-tiles of 32, one per wavefront)
+constexpr int kKC = 256;        // k per LDS chunk (8 blocks)
+constexpr int kRows = 128;      // weight rows per workgroup
+constexpr int kLdsRow = kKC + 16;  // padded int8 row stride
+constexpr uint32_t kMagicBits = 0x4B400000u;  // 1.5 * 2^23
+constexpr float kMagic = 12582912.0f;
+
+size_t q8_tile_capacity(int T, int k, int E) {
+    return (size_t)E + (size_t)T * k / kMG + (size_t)T / kMG + 4;
+}
+
+struct Q8Smem {
+    int8_t w[kRows][kLdsRow];          // staged weights, signed int8
+    float sw[kKC / 32][kRows];         // weight block scales
+    float sa[kKC / 32][kMG];           // activation block scales of the tile's tokens
+};
+
+// Plan: tile list of (slot, m0) over the active experts (slot = expert id) and
+// the shared expert (slot = E), kMG tokens per tile.  One workgroup.
+__global__ __launch_bounds__(1024) void q8_plan(const int32_t* __restrict__ counts,
+                                                const int32_t* __restrict__ active, int E, int T, int has_shared,
+                                                int2* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+    __shared__ int32_t sc[1024];
+    const int a = threadIdx.x;
+    const int n_active = active[0];
+    int e = -1, c = 0, nt = 0;
+    if (a < n_active) {
+        e = active[1 + a];
+        c = counts[e];
+        nt = (c + kMG - 1) / kMG;
+    }
+    sc[a] = nt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int v = a >= off ? sc[a - off] : 0;
+        __syncthreads();
+        sc[a] += v;
+        __syncthreads();
+    }
+    const int start = sc[a] - nt;
+    for (int i = 0; i < nt; ++i) tiles[start + i] = make_int2(e, i * kMG);
+    if (a == 1023) {
+        int total = sc[1023];
+        if (has_shared) {
+            const int ns = (T + kMG - 1) / kMG;
+            for (int i = 0; i < ns; ++i) tiles[total + i] = make_int2(E, i * kMG);
+            total += ns;
+        }
+        n_tiles[0] = total;
+    }
+}
+
+// Stage rows [row0 + 16*s .. +16) for strips s of `mats` (strip list) and k-chunk kc into LDS.
+// `ntile` packed tiles (<= kKC / k-per-tile) starting at packed tile kt0.
+template <int WFMT>
+__device__ __forceinline__ void stage_chunk(Q8Smem& S, const uint8_t* const* qbase, const uint8_t* const* sbase,
+                                            const int* strip_ids, int nkt_total, int kt0, int ntile) {
+    constexpr int KPT = WFMT == MOE_WFMT_I4B32 ? 128 : 64;  // k per packed tile
+    constexpr int NB = KPT / 32;
+    constexpr int STB = NB * 32;
+    // quants: 8 strips x ntile tiles x 64 lanes, 16 bytes each
+    for (int task = threadIdx.x; task < 8 * ntile * 64; task += 256) {
+        const int s = task / (ntile * 64), rem = task % (ntile * 64), tl = rem / 64, ll = rem % 64;
+        const uint4v w = *reinterpret_cast<const uint4v*>(qbase[s] + ((size_t)strip_ids[s] * nkt_total + kt0 + tl) * 1024 +
+                                                          (size_t)ll * 16);
+        const int row = s * 16 + (ll & 15);
+        const int kq = 8 * (ll >> 4);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            uint32_t w0, w1;
+            if constexpr (WFMT == MOE_WFMT_I4B32) {
+                const uint32_t v = w[b];
+                const uint32_t lo = v & 0x0F0F0F0Fu;         // bytes: k0 k4 k1 k5
+                const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;  // bytes: k2 k6 k3 k7
+                w0 = (lo & 0xFFu) | ((lo >> 8) & 0xFF00u) | ((hi & 0xFFu) << 16) | ((hi << 8) & 0xFF000000u);
+                w1 = ((lo >> 8) & 0xFFu) | ((lo >> 16) & 0xFF00u) | ((hi << 8) & 0xFF0000u) | (hi & 0xFF000000u);
+                // offset-binary nibble u -> signed byte u - 8 (no carries: u + 0x78 <= 0x87)
+                w0 = (w0 + 0x78787878u) ^ 0x80808080u;
+                w1 = (w1 + 0x78787878u) ^ 0x80808080u;
+            } else {
+                w0 = w[2 * b] ^ 0x80808080u;
+                w1 = w[2 * b + 1] ^ 0x80808080u;
+            }
+            *reinterpret_cast<uint2*>(&S.w[row][(tl * NB + b) * 32 + kq]) = make_uint2(w0, w1);
+        }
+    }
+    // scales: 8 strips x TPC tiles x 16 rows, NB fp16 each
+    for (int task = threadIdx.x; task < 8 * ntile * 16; task += 256) {
+        const int s = task / (ntile * 16), rem = task % (ntile * 16), tl = rem / 16, rr = rem % 16;
+        const _Float16* sp = reinterpret_cast<const _Float16*>(sbase[s] + ((size_t)strip_ids[s] * nkt_total + kt0 + tl) * STB) + rr * NB;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) S.sw[tl * NB + b][s * 16 + rr] = (float)sp[b];
+    }
+}
+
+// One k-chunk of MFMA work for one wavefront: 32 tokens x 4 n-tiles of 32 rows.
+// arow: this lane's A-operand row (int8 activations, chunk-relative k = 0),
+// valid: whether the row exists; sa rows are token rows of the wavefront's m-tile.
+__device__ __forceinline__ void mma_chunk(const Q8Smem& S, const int8_t* arow, bool valid, int mtile, int nblk,
+                                          float16v (&acc)[4]) {
+    const int lane = threadIdx.x & 63;
+    const int16v cmagic = {(int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
+                           (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
+                           (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
+                           (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits};
+    for (int b = 0; b < nblk; ++b) {
+        const int kk = b * 32 + 16 * (lane >> 5);
+        const int4v A = valid ? *reinterpret_cast<const int4v*>(arow + kk) : int4v{0, 0, 0, 0};
+        // activation scales of this lane's 16 token rows: 8*(r/4) + 4*(lane/32) + r%4
+        float sa[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(&S.sa[b][mtile * 32 + 8 * q + 4 * (lane >> 5)]);
+            sa[4 * q + 0] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int row = nt * 32 + (lane & 31);
+            const int4v B = *reinterpret_cast<const int4v*>(&S.w[row][kk]);
+            const int16v D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, cmagic, 0, 0, 0);
+            const float sw = S.sw[b][row];
+            const float nc = -kMagic * sw;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float t = fmaf(__int_as_float(D[r]), sw, nc);
+                acc[nt][r] = fmaf(t, sa[r], acc[nt][r]);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float silu_q(float z) { return z / (1.0f + expf(-z)); }
+
+template <int WFMT>
+__global__ __launch_bounds__(256) void ffn_q8_gateup(const int8_t* __restrict__ xq, const float* __restrict__ sx,
+                                                     int T, int d, int f, int k, int E,
+                                                     const void* const* __restrict__ expert_ptrs,
+                                                     const uint8_t* __restrict__ shared_blob,
+                                                     const int32_t* __restrict__ counts,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ sorted_idx,
+                                                     const int2* __restrict__ tiles,
+                                                     const int32_t* __restrict__ n_tiles_p, int8_t* __restrict__ hq,
+                                                     float* __restrict__ hs) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Q8Smem& S = *reinterpret_cast<Q8Smem*>(smem_raw);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_fg = f / 64;
+    const int n_items = n_tiles_p[0] * n_fg;
+    const ExpertLayout L = expert_layout(WFMT, d, f);
+    const int nkt = L.g.nkt;
+    const int nb_d = d / 32;
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int2 tl = tiles[item / n_fg];
+        const int fg = item % n_fg;
+        const bool routed = tl.x < E;
+        const uint8_t* blob = routed ? (const uint8_t*)expert_ptrs[tl.x] : shared_blob;
+        const int c = routed ? counts[tl.x] : T;
+        const int p0 = routed ? offsets[tl.x] : T * k;  // first h row of the slot
+        const int m0 = tl.y;
+        // this lane's A row (token) for the wavefront's m-tile
+        const int m = m0 + wave * 32 + (lane & 31);
+        const bool valid = m < c;
+        const int tok = valid ? (routed ? sorted_idx[p0 + m] / k : m) : 0;
+        const int8_t* xrow = xq + (size_t)tok * d;
+        // scales of the tile's tokens, per chunk: staged below
+        const uint8_t* qb[8];
+        const uint8_t* sb[8];
+        int sid[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const MatLayout& M = s < 4 ? L.g : L.u;
+            qb[s] = blob + M.qoff;
+            sb[s] = blob + M.soff;
+            sid[s] = fg * 4 + (s & 3);
+        }
+        float16v acc[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+        constexpr int KPT = WFMT == MOE_WFMT_I4B32 ? 128 : 64;
+        const int nkc = (d + kKC - 1) / kKC;
+        for (int kc = 0; kc < nkc; ++kc) {
+            const int nblk = min(kKC, d - kc * kKC) / 32;
+            __syncthreads();
+            stage_chunk<WFMT>(S, qb, sb, sid, nkt, kc * (kKC / KPT), nblk * 32 / KPT);
+            for (int task = threadIdx.x; task < (kKC / 32) * kMG; task += 256) {
+                const int b = task / kMG, mm = task % kMG;
+                const int mt = m0 + mm;
+                float v = 0.0f;
+                if (mt < c && b < nblk) {
+                    const int t = routed ? sorted_idx[p0 + mt] / k : mt;
+                    v = sx[(size_t)t * nb_d + kc * (kKC / 32) + b];
+                }
+                S.sa[b][mm] = v;
+            }
+            __syncthreads();
+            if (m0 + wave * 32 < c) mma_chunk(S, xrow + kc * kKC, valid, wave, nblk, acc);
+        }
+        // SwiGLU + int8 requantisation of h per (token, 32 features)
+        if (m0 + wave * 32 < c) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {  // f-blocks fg*2 + half: gate n-tile half, up n-tile 2+half
+                const int feat = fg * 64 + half * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float hv = silu_q(acc[half][r]) * acc[2 + half][r];
+                    float amax = fabsf(hv);
+#pragma unroll
+                    for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+                    const float s = amax / 127.0f;
+                    int q = 0;
+                    if (s != 0.0f) q = (int)fminf(fmaxf(rintf(hv / s), -127.0f), 127.0f);
+                    const int mrow = m0 + wave * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (mrow < c) {
+                        const size_t hrow = (size_t)(p0 + mrow);
+                        hq[hrow * f + feat] = (int8_t)q;
+                        if ((lane & 31) == 0) hs[hrow * (f / 32) + fg * 2 + half] = s;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int WFMT, typename YT>
+__global__ __launch_bounds__(256) void ffn_q8_down(const int8_t* __restrict__ hq, const float* __restrict__ hs,
+                                                   int T, int d, int f, int k, int E,
+                                                   const void* const* __restrict__ expert_ptrs,
+                                                   const uint8_t* __restrict__ shared_blob,
+                                                   const int32_t* __restrict__ counts,
+                                                   const int32_t* __restrict__ offsets,
+                                                   const int2* __restrict__ tiles,
+                                                   const int32_t* __restrict__ n_tiles_p, YT* __restrict__ y_perm,
+                                                   float* __restrict__ y_shared) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Q8Smem& S = *reinterpret_cast<Q8Smem*>(smem_raw);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_og = d / kRows;
+    const int n_items = n_tiles_p[0] * n_og;
+    const ExpertLayout L = expert_layout(WFMT, d, f);
+    const int nkt = L.dn.nkt;
+    const int nb_f = f / 32;
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int2 tl = tiles[item / n_og];
+        const int og = item % n_og;
+        const bool routed = tl.x < E;
+        const uint8_t* blob = routed ? (const uint8_t*)expert_ptrs[tl.x] : shared_blob;
+        const int c = routed ? counts[tl.x] : T;
+        const int p0 = routed ? offsets[tl.x] : T * k;
+        const int m0 = tl.y;
+        const int m = m0 + wave * 32 + (lane & 31);
+        const bool valid = m < c;
+        const int8_t* arow = hq + (size_t)(p0 + (valid ? m : 0)) * f;
+        const uint8_t* qb[8];
+        const uint8_t* sb[8];
+        int sid[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            qb[s] = blob + L.dn.qoff;
+            sb[s] = blob + L.dn.soff;
+            sid[s] = og * 8 + s;
+        }
+        float16v acc[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+        const int nkc = (f + kKC - 1) / kKC;
+        for (int kc = 0; kc < nkc; ++kc) {
+            const int kbase = kc * kKC;
+            const int nblk = min(kKC, f - kbase) / 32;
+            constexpr int KPT = WFMT == MOE_WFMT_I4B32 ? 128 : 64;
+            __syncthreads();
+            stage_chunk<WFMT>(S, qb, sb, sid, nkt, kc * (kKC / KPT), nblk * 32 / KPT);
+            for (int task = threadIdx.x; task < (kKC / 32) * kMG; task += 256) {
+                const int b = task / kMG, mm = task % kMG;
+                const int mt = m0 + mm;
+                S.sa[b][mm] = (mt < c && b < nblk) ? hs[(size_t)(p0 + mt) * nb_f + kc * (kKC / 32) + b] : 0.0f;
+            }
+            __syncthreads();
+            if (m0 + wave * 32 < c) mma_chunk(S, arow + kbase, valid, wave, nblk, acc);
+        }
+        if (m0 + wave * 32 < c) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int o = og * kRows + nt * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int mrow = m0 + wave * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (mrow >= c) continue;
+                    if (routed) y_perm[(size_t)(p0 + mrow) * d + o] = (YT)acc[nt][r];
+                    else y_shared[(size_t)mrow * d + o] = acc[nt][r];
+                }
+            }
+        }
+    }
+}
+
+template <int WFMT>
+static int run_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
+    int2* tiles = reinterpret_cast<int2*>(w.tiles);
+    int32_t* n_tiles = w.tiles + 2 * q8_tile_capacity(a->T, a->k, a->E);
+    q8_plan<<<1, 1024, 0, s>>>(a->counts, a->active, a->E, a->T, a->shared_blob ? 1 : 0, tiles, n_tiles);
+    int rc = check_launch();
+    if (rc) return rc;
+    const long max_tiles = (long)std::min(a->E, a->T * a->k) + (long)a->T * a->k / kMG + (a->shared_blob ? a->T / kMG + 1 : 0);
+    const size_t smem = sizeof(Q8Smem);
+    int8_t* hq = reinterpret_cast<int8_t*>(w.h);
+    const int g1 = (int)std::min<long>(max_tiles * (a->f / 64), 4096);
+    ffn_q8_gateup<WFMT><<<g1, 256, smem, s>>>(a->xq, a->sx, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs,
+                                              (const uint8_t*)a->shared_blob, a->counts, a->offsets, a->sorted_idx,
+                                              tiles, n_tiles, hq, w.hs);
+    rc = check_launch();
+    if (rc) return rc;
+    const int g2 = (int)std::min<long>(max_tiles * (a->d / kRows), 4096);
+    if (a->y_dtype == MOE_DT_F32)
+        ffn_q8_down<WFMT, float><<<g2, 256, smem, s>>>(hq, w.hs, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs,
+                                                       (const uint8_t*)a->shared_blob, a->counts, a->offsets, tiles,
+                                                       n_tiles, (float*)a->y_perm, a->y_shared);
+    else
+        ffn_q8_down<WFMT, _Float16><<<g2, 256, smem, s>>>(hq, w.hs, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs,
+                                                          (const uint8_t*)a->shared_blob, a->counts, a->offsets,
+                                                          tiles, n_tiles, (_Float16*)a->y_perm, a->y_shared);
+    return check_launch();
+}
+
+int launch_ffn_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
+    return a->wfmt == MOE_WFMT_I4B32 ? run_q8<MOE_WFMT_I4B32>(a, w, s) : run_q8<MOE_WFMT_I8B32>(a, w, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Integer outputs (ids, counts, offsets, permutation,
+active list, int8 activations) must match bit for bit; float outputs must meet
+rel-L2 <= 2e-3 and max-abs <= 1e-2 * RMS(oracle) (exactly zero where the oracle
+is exactly zero).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import refmath as R
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_util import DEV, act_mode, gpu_layer, host, routing_state, x_tensor  # noqa: E402
+from sparse_moe_expert_gemv_amd import binding as B  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    oracle.build(force=False)
+
+
+def _oracle_mode(L):
+    return oracle.ACT_Q8 if L.cfg.act_mode == "q8" else oracle.ACT_FLOAT
+
+
+def check_routing(st, o, E):
+    assert np.array_equal(st["ids"], o["ids"]), "expert ids differ"
+    assert np.max(np.abs(st["gates"] - o["gates"])) <= 1e-6
+    assert np.array_equal(st["counts"], o["counts"])
+    assert np.array_equal(st["offsets"], o["offsets"])
+    assert np.array_equal(st["sorted_idx"], o["sorted_idx"])
+    assert np.array_equal(st["dest"], o["dest"])
+    act = np.nonzero(o["counts"])[0]
+    assert st["active"][0] == len(act)
+    assert np.array_equal(st["active"][1:1 + len(act)], act)
+
+
+def check_float(got, ref, what):
+    ok, rel, mx = R.within_tolerance(got, ref)
+    assert ok, "%s: rel-L2 %.3e, max-abs/RMS %.3e" % (what, rel, mx)
+
+
+def run_layer(L, mode=None, x=None, residual=None, tokens=None, y_dtype=None):
+    G = gpu_layer(L, mode=mode, y_dtype=y_dtype)
+    xt = x_tensor(L, x)
+    res_t = None if residual is None else torch.from_numpy(residual).to(DEV)
+    out = host(G.forward(xt, residual=res_t))
+    torch.cuda.synchronize()
+    st = routing_state(G, xt.shape[0])
+    xf = L.x_f32() if x is None else (synth.bf16_bits_to_f32(x) if L.cfg.x_dtype == "bf16" else x)
+    om = _oracle_mode(L) if mode is None else (oracle.ACT_Q8 if mode == B.MOE_ACT_Q8 else oracle.ACT_FLOAT)
+    o = oracle.moe_layer(xf, L.Wr, L.bias, L.experts, L.shared, L.cfg.wfmt, L.cfg.f, L.cfg.k, act_mode=om,
+                         residual=residual, tokens=tokens)
+    return G, out, st, o
+
+
+# ------------------------------------------------------------- building blocks
+
+@pytest.mark.parametrize("name", ["tiny", "decode_t1", "skew"])
+def test_pack_unpack_roundtrip_bitexact(name):
+    L = synth.make_layer(name, overrides={"E": 8} if name != "tiny" else None)
+    c = L.cfg
+    src = torch.from_numpy(L.experts).to(DEV)
+    packed = torch.empty_like(src)
+    back = torch.empty_like(src)
+    B.moe_pack_experts(src, packed, src.shape[0], c.wfmt, c.d, c.f)
+    B.moe_unpack_experts(packed, back, src.shape[0], c.wfmt, c.d, c.f)
+    torch.cuda.synchronize()
+    assert torch.equal(back, src)
+    assert not torch.equal(packed, src)
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 32), ("decode_t4", 4), ("prefill", 8192), ("tiny", 37)])
+def test_quantize_act_bitexact(name, T):
+    L = synth.make_layer(name, overrides={"E": 16})
+    x = synth.gen_x(0, L.cfg, T=T, draw=3)
+    xt = x_tensor(L, x)
+    xq = torch.empty((T, L.cfg.d), dtype=torch.int8, device=DEV)
+    sx = torch.empty((T, L.cfg.d // 32), dtype=torch.float32, device=DEV)
+    B.moe_quantize_act(xt, xq, sx)
+    q_ref, s_ref = oracle.quant8(synth.bf16_bits_to_f32(x) if L.cfg.x_dtype == "bf16" else x)
+    assert np.array_equal(host(xq), q_ref)
+    assert np.array_equal(host(sx).view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_t1", "decode_t4", "skew"])
+def test_route_and_permute_bitexact(name):
+    L = _layer(name)
+    G = gpu_layer(L)
+    xt = x_tensor(L)
+    T, k, E = L.cfg.T, L.cfg.k, L.cfg.E
+    ws = G._ws_for(T)
+    B.moe_route(xt, G.Wr, G.bias, k, G.ids[:T], G.gates[:T], ws)
+    B.moe_permute(G.ids[:T], E, G.counts, G.offsets, G.sorted_idx[:T * k], G.dest[:T * k], G.active, ws)
+    torch.cuda.synchronize()
+    ids, gates = oracle.route(L.x_f32(), L.Wr, L.bias, k)
+    counts, offsets, sorted_idx, dest = oracle.permute(ids, E)
+    check_routing(routing_state(G, T), dict(ids=ids, gates=gates, counts=counts, offsets=offsets,
+                                            sorted_idx=sorted_idx, dest=dest), E)
+
+
+_LAYERS = {}
+
+
+def _layer(name):
+    if name not in _LAYERS:
+        _LAYERS[name] = synth.make_layer(name)
+    return _LAYERS[name]
+
+
+# ---------------------------------------------------------------- full layers
+
+@pytest.mark.parametrize("mode", [B.MOE_ACT_FLOAT, B.MOE_ACT_Q8])
+def test_layer_tiny(mode):
+    """Tiny layer (T=32, d=256, E=64, top-4, f=128, int8 weights), both modes."""
+    L = _layer("tiny")
+    G, out, st, o = run_layer(L, mode=mode)
+    check_routing(st, o, L.cfg.E)
+    check_float(out, o["out"], "tiny layer")
+
+
+@pytest.mark.parametrize("name", ["decode_t1", "decode_t4"])
+def test_layer_decode(name):
+    """Decode layer: T=1 and the T=4 MTP-verify batch, int4 experts + shared."""
+    L = _layer(name)
+    G, out, st, o = run_layer(L)
+    check_routing(st, o, L.cfg.E)
+    check_float(out, o["out"], name)
+
+
+def test_layer_skew():
+    """T=64 with a Zipf(1.1) router bias: a few experts take most tokens."""
+    L = _layer("skew")
+    G, out, st, o = run_layer(L)
+    check_routing(st, o, L.cfg.E)
+    assert o["counts"].max() >= 48 and (o["counts"] == 0).sum() > 400  # the skew is real
+    check_float(out, o["out"], "skew")
+
+
+def test_layer_prefill_sampled():
+    """8,192-token prefill chunk in int8-activation mode: routing compared in
+    full, outputs on a seeded sample of 48 tokens (plus the first and last)."""
+    L = _layer("prefill")
+    rng = np.random.Generator(np.random.PCG64(11))
+    tokens = np.r_[0, np.sort(rng.choice(np.arange(1, L.cfg.T - 1), 48, replace=False)), L.cfg.T - 1]
+    G, out, st, o = run_layer(L, tokens=tokens)
+    check_routing(st, o, L.cfg.E)
+    assert o["counts"].min() > 0  # every expert sees tokens (~160 each)
+    check_float(out[tokens], o["out"], "prefill sample")
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_ragged_token_counts_and_float_mode_large_batch():
+    """T=77 (not a multiple of any tile) on the decode-shaped layer with fewer
+    experts, float mode: experts receive >64 tokens, exercising multi-pass
+    m-tiles and ragged tails in both projections."""
+    L = synth.make_layer("decode_t4", T=77, overrides={"E": 16, "k": 14})
+    G, out, st, o = run_layer(L)
+    check_routing(st, o, L.cfg.E)
+    assert o["counts"].max() > 64
+    check_float(out, o["out"], "T=77 float")
+
+
+def test_one_expert_takes_every_token_q8():
+    """Router bias forces one expert into every token's top-k (count = T = 300
+    > one 128-token tile) in int8 mode; ties elsewhere still resolve to the
+    lower index."""
+    L = synth.make_layer("tiny", T=300, overrides={"act_mode": "q8"})
+    L.bias = np.zeros(L.cfg.E, np.float32)
+    L.bias[37] = 50.0
+    G, out, st, o = run_layer(L, mode=B.MOE_ACT_Q8)
+    check_routing(st, o, L.cfg.E)
+    assert o["counts"][37] == 300
+    check_float(out, o["out"], "one expert q8")
+
+
+def test_zero_input_gives_exact_zero_both_modes():
+    L = _layer("tiny")
+    z = np.zeros_like(L.x)
+    for mode in (B.MOE_ACT_FLOAT, B.MOE_ACT_Q8):
+        G, out, st, o = run_layer(L, mode=mode, x=z)
+        check_routing(st, o, L.cfg.E)
+        assert np.all(out == 0.0)
+
+
+def test_residual_and_shared_expert_tiny():
+    L = synth.make_layer("tiny", overrides={"has_shared": True})
+    res = np.random.Generator(np.random.PCG64(12)).standard_normal((L.cfg.T, L.cfg.d)).astype(np.float32)
+    G, out, st, o = run_layer(L, residual=res)
+    check_float(out, o["out"], "tiny + shared + residual")
+
+
+def test_identical_experts_equal_dense_ffn_on_gpu():
+    """All routed experts identical: GPU layer output equals the oracle's
+    single dense FFN plus shared expert (the layer-level invariant)."""
+    L = synth.make_layer("decode_t4", overrides={"E": 32})
+    L.experts = np.tile(L.experts[3], (L.cfg.E, 1))
+    G = gpu_layer(L)
+    out = host(G.forward(x_tensor(L)))
+    ref = (oracle.expert_ffn(L.x_f32(), L.experts[3], L.cfg.wfmt, L.cfg.f)
+           + oracle.expert_ffn(L.x_f32(), L.shared, L.cfg.wfmt, L.cfg.f))
+    check_float(out, ref, "identical experts")
+
+
+def test_deterministic_two_runs_bit_identical():
+    L = _layer("skew")
+    G = gpu_layer(L)
+    xt = x_tensor(L)
+    a = host(G.forward(xt)).copy()
+    b = host(G.forward(xt)).copy()
+    assert np.array_equal(a, b)
+
+
+def test_zero_tokens_is_noop():
+    L = _layer("tiny")
+    G = gpu_layer(L)
+    xt = x_tensor(L)[:0]
+    out = G.forward(xt)
+    torch.cuda.synchronize()
+    assert out.shape == (0, L.cfg.d)

@@ -1,0 +1,104 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every entry point declared in include/moe.h, sizes agree with the format
+definition, and invalid arguments are rejected before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle
+import synth
+from sparse_moe_expert_gemv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_entry_points():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = declared_entry_points()
+    assert len(names) >= 17
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTED) == names
+
+
+def test_version_and_status_strings():
+    assert B.moe_version() == 10000
+    assert B.lib().moe_status_string(B.MOE_ERR_CACHE_CAPACITY) == b"MOE_ERR_CACHE_CAPACITY"
+
+
+@pytest.mark.parametrize("wfmt", [4, 8])
+@pytest.mark.parametrize("d,f", [(2048, 768), (256, 128), (64, 32)])
+def test_expert_bytes_agree_with_format(wfmt, d, f):
+    n = B.moe_expert_bytes(wfmt, d, f)
+    assert n == synth.expert_bytes(wfmt, d, f) == oracle.expert_bytes(wfmt, d, f)
+    assert B.moe_expert_bytes(3, d, f) == 0
+
+
+def test_workspace_size_grows_with_tokens_and_rejects_bad_shapes():
+    a = B.moe_workspace_size(1, 2048, 768, 512, 10, B.MOE_ACT_FLOAT)
+    b = B.moe_workspace_size(8192, 2048, 768, 512, 10, B.MOE_ACT_Q8)
+    assert 0 < a < b
+    with pytest.raises(B.MoeError):
+        B.moe_workspace_size(4, 2000, 768, 512, 10, B.MOE_ACT_FLOAT)  # d % 128 != 0
+    with pytest.raises(B.MoeError):
+        B.moe_workspace_size(4, 2048, 768, 8, 10, B.MOE_ACT_FLOAT)  # k > E
+    with pytest.raises(B.MoeError):
+        B.moe_workspace_size(4, 2048, 768, 2048, 10, B.MOE_ACT_FLOAT)  # E > 1024
+
+
+def test_invalid_arguments_rejected_before_any_hip_call():
+    L = B.lib()
+    null = None
+    assert L.moe_route(null, B.MOE_DT_F32, 4, 2048, null, null, 512, 10, null, null, null, 0, null) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_route(null, 7, 4, 2048, null, null, 512, 10, null, null, null, 0, null) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_route(null, B.MOE_DT_F32, -1, 2048, null, null, 512, 10, null, null, null, 0, null) == \
+        B.MOE_ERR_INVALID_ARG
+    # T == 0 is a no-op even with null pointers
+    assert L.moe_route(null, B.MOE_DT_F32, 0, 2048, null, null, 512, 10, null, null, null, 0, null) == B.MOE_OK
+    assert L.moe_permute(null, 4, 11, 10, null, null, null, null, null, null, 0, null) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_act(null, B.MOE_DT_BF16, 4, 100, null, null, null) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(null, B.MOE_DT_F32, null, null, null, null, 2, 10, 2048, null, null) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(null, 5, null, null, null, null, 2, 10, 2048, null, null) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_experts(null, null, 3, 5, 2048, 768, null) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_experts(null, null, 3, 4, 2048, 760, null) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn(None, None) == B.MOE_ERR_INVALID_ARG
+    a = B.FfnArgs()
+    a.T, a.d, a.f, a.E, a.k, a.wfmt, a.act_mode, a.y_dtype = 4, 2048, 768, 512, 10, 4, 0, 0
+    assert L.moe_expert_ffn(C.byref(a), None) == B.MOE_ERR_INVALID_ARG  # null pointers
+    a.act_mode = 9
+    assert L.moe_expert_ffn(C.byref(a), None) == B.MOE_ERR_INVALID_ARG
+    a.act_mode, a.T = 0, 0
+    assert L.moe_expert_ffn(C.byref(a), None) == B.MOE_OK
+
+
+def test_workspace_too_small_is_reported():
+    """A too-small workspace is rejected with MOE_ERR_NO_MEMORY (pointers are
+    never dereferenced on the host, so fake non-null values are safe)."""
+    L = B.lib()
+    fake = C.c_void_p(0x1000)
+    st = L.moe_route(fake, B.MOE_DT_F32, 4, 2048, fake, None, 512, 10, fake, fake, fake, 16, None)
+    assert st == B.MOE_ERR_NO_MEMORY
+    st = L.moe_permute(fake, 4, 10, 512, fake, fake, fake, fake, fake, fake, 16, None)
+    assert st == B.MOE_ERR_NO_MEMORY
+
+
+def test_cache_argument_validation():
+    L = B.lib()
+    h = C.c_void_p()
+    assert L.moe_cache_create(None, 48, 512, 10, 100, None, None, 2, 10) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_cache_create(C.byref(h), 0, 512, 10, 100, C.c_void_p(1), C.c_void_p(1), 2, 10) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_cache_create(C.byref(h), 48, 512, 10, 0, C.c_void_p(1), C.c_void_p(1), 2, 10) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_cache_destroy(None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_cache_lookup(None, 0, None, None, None, None) == B.MOE_ERR_INVALID_ARG
