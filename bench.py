@@ -1,0 +1,271 @@
+"""Benchmark of the sparse-MoE FFN layer hot path on one MI355X.
+
+One step = one pass of the whole layer (moe_route -> moe_permute ->
+[moe_quantize_act] -> moe_expert_ffn -> moe_combine) over one batch of seeded
+synthetic input already resident in HBM.  Default workload: the decode layer
+(d=2048, 512 int4 experts + shared, top-10, f=768) at T=4 tokens, the MTP
+verify batch; ``--workload`` selects another layer (decode_t1, prefill, skew,
+tiny).
+
+Layer weights are replicated into ``--rotate`` device copies and consecutive
+steps use consecutive copies with their own inputs, so each step streams its
+expert weights from HBM rather than from the 256 MB Infinity Cache.  Each
+copy's step is one captured HIP graph.  Two timed regions, both bracketed by a
+device synchronisation: (A) ``--steps`` whole-layer steps, which give
+``value`` and ``ms_per_step``; (B) ``--steps`` back-to-back launches of the
+dominant kernel alone (the expert gate/up projection, ``moe_expert_ffn``
+phase 1, rotating over the weight copies) between two HIP events on its launch
+stream, whose mean launch time gives the roofline figure.
+
+Prints one JSON line (rank 0).  ``--gpus`` above 1 is not supported: this
+build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA, TOPS
+WORKLOADS = ("decode_t4", "decode_t1", "prefill", "skew", "tiny")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
+    p.add_argument("--workload", default="decode_t4", choices=WORKLOADS)
+    p.add_argument("--rotate", type=int, default=None, help="device copies of the layer weights")
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline leg")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+def gateup_algorithmic(cfg, n_active: int, T: int):
+    """Algorithmic bytes and ops of one gate/up launch (the dominant kernel).
+
+    Bytes: the gate and up matrices (quants + fp16 block scales) of every
+    expert that has tokens, plus the shared expert, plus the activations read
+    and the SwiGLU intermediate written.  Ops: 2 per multiply-add over the
+    gate and up projections of every routed and shared row.
+    """
+    import synth
+    eb = synth.expert_bytes(cfg.wfmt, cfg.d, cfg.f)
+    n_exp = n_active + (1 if cfg.has_shared else 0)
+    weight_bytes = n_exp * eb * 2 // 3
+    rows = T * cfg.k + (T if cfg.has_shared else 0)
+    if cfg.act_mode == "q8":
+        xbytes = T * cfg.d + T * (cfg.d // 32) * 4
+        hbytes = rows * cfg.f + rows * (cfg.f // 32) * 4
+    else:
+        xbytes = T * cfg.d * (2 if cfg.x_dtype == "bf16" else 4)
+        hbytes = rows * cfg.f * 2
+    ops = 2.0 * 2 * cfg.d * cfg.f * rows
+    return weight_bytes + xbytes + hbytes, ops
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus %d" % a.gpus)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from sparse_moe_expert_gemv_amd import binding as B
+    from sparse_moe_expert_gemv_amd.layer import MoELayer, pack_blobs, pointer_table
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = a.workload
+    big = name == "prefill"
+    steps = a.steps if a.steps is not None else (20 if big else 200)
+    warmup = a.warmup if a.warmup is not None else (3 if big else 20)
+    rotate = a.rotate if a.rotate is not None else (2 if big else 8)
+    t_gen = time.time()
+    L = synth.make_layer(name, seed=a.seed)
+    cfg = L.cfg
+    T = cfg.T
+    mode = B.MOE_ACT_Q8 if cfg.act_mode == "q8" else B.MOE_ACT_FLOAT
+    print("[bench] workload %s T=%d d=%d E=%d k=%d f=%d wfmt=%d mode=%s rotate=%d (generated in %.1fs)"
+          % (name, T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.wfmt, cfg.act_mode, rotate, time.time() - t_gen),
+          file=sys.stderr, flush=True)
+
+    # one packed copy, replicated
+    canon = torch.from_numpy(L.experts).to(dev)
+    packed0 = pack_blobs(canon, cfg.wfmt, cfg.d, cfg.f)
+    del canon
+    layers, xs = [], []
+    for r in range(rotate):
+        packed = packed0 if r == 0 else packed0.clone()
+        G = MoELayer(L.Wr, L.bias, packed, None, d=cfg.d, f=cfg.f, k=cfg.k, wfmt=cfg.wfmt, act_mode=mode,
+                     max_T=T, device=dev, expert_ptrs=pointer_table(packed))
+        if L.shared is not None:
+            sh = torch.from_numpy(L.shared).to(dev).reshape(1, -1)
+            G.shared = pack_blobs(sh, cfg.wfmt, cfg.d, cfg.f)[0]
+        layers.append(G)
+        xb = synth.gen_x(a.seed, cfg, layer=0, draw=r)
+        if cfg.x_dtype == "bf16":
+            xs.append(torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16))
+        else:
+            xs.append(torch.from_numpy(xb).to(dev))
+    torch.cuda.synchronize()
+
+    def run_route(G, x):
+        ws = G._ws_for(T)
+        n = T * cfg.k
+        B.moe_route_permute(x, G.Wr, G.bias, cfg.k, G.ids[:T], G.gates[:T], G.counts, G.offsets,
+                            G.sorted_idx[:n], G.dest[:n], G.active, ws)
+        if mode == B.MOE_ACT_Q8:
+            B.moe_quantize_act(x, G.xq[:T], G.sx[:T])
+
+    def run_ffn(G, x, phase=0):
+        n = T * cfg.k
+        common = dict(T=T, d=cfg.d, f=cfg.f, E=cfg.E, k=cfg.k, wfmt=cfg.wfmt, act_mode=mode,
+                      expert_ptrs=G.expert_ptrs, counts=G.counts, offsets=G.offsets, sorted_idx=G.sorted_idx[:n],
+                      active=G.active, y_perm=G.y_perm[:n], ws=G._ws_for(T), shared_blob=G.shared,
+                      y_shared=G.y_shared[:T] if G.shared is not None else None, phase=phase)
+        if mode == B.MOE_ACT_Q8:
+            B.moe_expert_ffn(xq=G.xq[:T], sx=G.sx[:T], **common)
+        else:
+            B.moe_expert_ffn(x=x, **common)
+
+    def run_combine(G, x):
+        n = T * cfg.k
+        B.moe_combine(G.y_perm[:n], G.dest[:n], G.gates[:T], G.y_shared[:T] if G.shared is not None else None,
+                      None, G.out[:T])
+
+    def run_step(G, x):
+        run_route(G, x)
+        run_ffn(G, x)
+        run_combine(G, x)
+
+    # warm up eagerly on every copy
+    for i in range(max(warmup, rotate)):
+        r = i % rotate
+        run_step(layers[r], xs[r])
+    torch.cuda.synchronize()
+
+    use_graph = not a.no_graph
+    stream = torch.cuda.Stream()
+    step_graphs = []
+    if use_graph:
+        with torch.cuda.stream(stream):
+            for r in range(rotate):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    run_step(layers[r], xs[r])
+                step_graphs.append(g)
+        torch.cuda.synchronize()
+
+    def timed(fn, n):
+        with torch.cuda.stream(stream):
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record(stream)
+            for i in range(n):
+                fn(i)
+            end.record(stream)
+            torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    # region A: whole steps
+    def step_i(i):
+        r = i % rotate
+        if use_graph:
+            step_graphs[r].replay()
+        else:
+            run_step(layers[r], xs[r])
+
+    timed(step_i, rotate)  # one more pass over the copies
+    total_ms = timed(step_i, steps)
+    ms_step = total_ms / steps
+
+    # region B: the dominant kernel (gate/up) alone: --steps back-to-back launches on
+    # the stream, rotating over the weight copies, between two HIP events
+    def gu_i(i):
+        r = i % rotate
+        run_ffn(layers[r], xs[r], phase=1)
+
+    timed(gu_i, rotate)
+    gu_ms = timed(gu_i, steps) / steps
+
+    # algorithmic work per gate/up launch, from each copy's routing (fixed input per copy)
+    n_act = [int(G.active[0].item()) for G in layers]
+    per = [gateup_algorithmic(cfg, n, T) for n in n_act]
+    alg_bytes = float(np.mean([p[0] for p in per]))
+    alg_ops = float(np.mean([p[1] for p in per]))
+    if mode == B.MOE_ACT_Q8:
+        achieved = alg_ops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None}
+    else:
+        achieved = alg_bytes / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = "ffn_%s_gateup (moe_expert_ffn phase 1)" % ("q8" if mode == B.MOE_ACT_Q8 else "float")
+    roof["kernel_ms"] = round(gu_ms, 5)
+    roof["algorithmic_bytes_per_launch"] = int(alg_bytes)
+    roof["algorithmic_ops_per_launch"] = int(alg_ops)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(L, a.cpu_seconds)
+
+    value = T / (ms_step * 1e-3)
+    line = {
+        "metric": "MoE-layer tokens/s (8192-tok prefill; 1-4 tok decode); % HBM BW / MFMA peak",
+        "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8" if mode == B.MOE_ACT_Q8 else "fp16",
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,0.02) router and block-32-quantised experts)",
+        "config": {"workload": name, "T": T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "f": cfg.f,
+                   "weights": "int4-b32" if cfg.wfmt == 4 else "int8-b32", "shared_expert": cfg.has_shared,
+                   "act_mode": cfg.act_mode, "x_dtype": cfg.x_dtype, "weight_copies_rotated": rotate,
+                   "graph": use_graph, "active_experts_per_step": float(np.mean(n_act))},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(L, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    cfg = L.cfg
+    om = oracle.ACT_Q8 if cfg.act_mode == "q8" else oracle.ACT_FLOAT
+    x = L.x_f32()
+    if cfg.T <= 64:
+        toks, sample = None, "full layer (all %d tokens), repeated" % cfg.T
+        per_call = cfg.T
+    else:
+        toks = np.arange(0, cfg.T, cfg.T // 16, dtype=np.int32)[:16]
+        sample = ("routing of all %d tokens + expert FFN and combine of 16 evenly spaced tokens; "
+                  "tokens/s counts the 16 tokens" % cfg.T)
+        per_call = len(toks)
+    t0 = time.time()
+    n = 0
+    while True:
+        oracle.moe_layer(x, L.Wr, L.bias, L.experts, L.shared, cfg.wfmt, cfg.f, cfg.k, act_mode=om, tokens=toks)
+        n += 1
+        el = time.time() - t0
+        if el >= budget_s or (n >= 1 and el * (n + 1) / n > 3 * budget_s):
+            break
+    return {"value": round(per_call * n / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": sample + "; %d call(s) in %.1fs" % (n, el)}
+
+
+if __name__ == "__main__":
+    main()

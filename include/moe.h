@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_VERSION 10000
+#define MOE_VERSION 10100
 
 typedef void* moe_stream_t; /* hipStream_t */
 typedef void* moe_event_t;  /* hipEvent_t  */
@@ -98,7 +98,8 @@ int moe_unpack_experts(const void* src, void* dst, int n, int wfmt, int d, int f
 /*
  * Workspace bytes needed by route, permute and expert_ffn for a layer with
  * these shapes (the same workspace may be passed to all three calls of one
- * layer; calls on one stream are ordered).  Writes *bytes.
+ * layer; calls on one stream are ordered).  Writes *bytes.  The workspace is
+ * scratch: its contents need no initialisation and are not preserved.
  */
 int moe_workspace_size(int T, int d, int f, int E, int k, int act_mode, size_t* bytes);
 
@@ -118,6 +119,17 @@ int moe_workspace_size(int T, int d, int f, int E, int k, int act_mode, size_t* 
  */
 int moe_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
               int32_t* ids, float* gates, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * moe_route followed by moe_permute.  For small batches (T <= 64 and
+ * T*k <= 512: decode, MTP verify) this is two launches: the router logits,
+ * then one workgroup that selects the top-k of every token and groups the
+ * slots; larger batches run the two calls' kernels in sequence.  Outputs and
+ * numerics are those of the two calls.
+ */
+int moe_route_permute(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
+                      int32_t* ids, float* gates, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
+                      int32_t* dest, int32_t* active, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
  * Stable grouping of the T*k routing slots by expert (flat slot f = t*k + j).
@@ -169,6 +181,9 @@ typedef struct moe_ffn_args {
     float* y_shared;
     void* ws;
     size_t ws_bytes;
+    /* 0 = whole FFN; 1 = gate/up + SwiGLU only (h left in the workspace);
+       2 = down projection only (reads h from the same workspace) */
+    int phase;
 } moe_ffn_args;
 
 /*

@@ -26,7 +26,8 @@ MOE_ACT_FLOAT, MOE_ACT_Q8 = 0, 1
 
 EXPORTED = [
     "moe_version", "moe_last_hip_error", "moe_status_string", "moe_expert_bytes", "moe_pack_experts",
-    "moe_unpack_experts", "moe_workspace_size", "moe_route", "moe_permute", "moe_quantize_act", "moe_expert_ffn",
+    "moe_unpack_experts", "moe_workspace_size", "moe_route", "moe_route_permute", "moe_permute", "moe_quantize_act",
+    "moe_expert_ffn",
     "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
     "moe_cache_stage",
 ]
@@ -50,6 +51,7 @@ class FfnArgs(C.Structure):
         ("y_perm", C.c_void_p), ("y_dtype", C.c_int),
         ("shared_blob", C.c_void_p), ("y_shared", C.c_void_p),
         ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
+        ("phase", C.c_int),
     ]
 
 
@@ -72,6 +74,7 @@ def lib():
             "moe_workspace_size": ([I, I, I, I, I, I, C.POINTER(S)], I),
             "moe_route": ([P, I, I, I, P, P, I, I, P, P, P, S, P], I),
             "moe_permute": ([P, I, I, I, P, P, P, P, P, P, S, P], I),
+            "moe_route_permute": ([P, I, I, I, P, P, I, I, P, P, P, P, P, P, P, P, S, P], I),
             "moe_quantize_act": ([P, I, I, I, P, P, P], I),
             "moe_expert_ffn": ([C.POINTER(FfnArgs), P], I),
             "moe_combine": ([P, I, P, P, P, P, I, I, I, P, P], I),
@@ -156,6 +159,14 @@ def moe_route(x, Wr, bias, k, ids, gates, ws, stream=None):
                                         _ptr(gates), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def moe_route_permute(x, Wr, bias, k, ids, gates, counts, offsets, sorted_idx, dest, active, ws, stream=None):
+    T, d = x.shape
+    E = Wr.shape[0]
+    _check("moe_route_permute", lib().moe_route_permute(
+        _ptr(x), _xdtype(x), T, d, _ptr(Wr), _ptr(bias), E, k, _ptr(ids), _ptr(gates), _ptr(counts), _ptr(offsets),
+        _ptr(sorted_idx), _ptr(dest), _ptr(active), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def moe_permute(ids, E, counts, offsets, sorted_idx, dest, active, ws, stream=None):
     T, k = ids.shape
     _check("moe_permute", lib().moe_permute(_ptr(ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(sorted_idx),
@@ -170,7 +181,7 @@ def moe_quantize_act(x, xq, sx, stream=None):
 
 
 def moe_expert_ffn(*, T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offsets, sorted_idx, active, y_perm,
-                   ws, x=None, xq=None, sx=None, shared_blob=None, y_shared=None, stream=None):
+                   ws, x=None, xq=None, sx=None, shared_blob=None, y_shared=None, stream=None, phase=0):
     a = FfnArgs()
     a.T, a.d, a.f, a.E, a.k = T, d, f, E, k
     a.wfmt, a.act_mode = wfmt, act_mode
@@ -185,6 +196,7 @@ def moe_expert_ffn(*, T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offset
     a.shared_blob = None if shared_blob is None else shared_blob.data_ptr()
     a.y_shared = None if y_shared is None else y_shared.data_ptr()
     a.ws, a.ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
+    a.phase = phase
     _check("moe_expert_ffn", lib().moe_expert_ffn(C.byref(a), _stream(stream)))
 
 

@@ -36,13 +36,11 @@ void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* bas
     w->permute_bytes = off;
     if (act_mode == MOE_ACT_Q8) {
         w->tiles = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (2 * q8_tile_capacity(T, k, E) + 4)));
-        w->x16 = nullptr;
         w->h = take(rows * (size_t)f);
         w->hs = reinterpret_cast<float*>(take(sizeof(float) * rows * (size_t)(f / 32)));
     } else {
         w->tiles = nullptr;
-        w->x16 = reinterpret_cast<_Float16*>(take(sizeof(_Float16) * (size_t)T * d));
-        w->h = take(sizeof(_Float16) * rows * (size_t)f);
+        w->h = take(float_h_bytes(T, f, k));
         w->hs = nullptr;
     }
     w->bytes = off;
@@ -114,6 +112,24 @@ int moe_route(const void* x, int x_dtype, int T, int d, const float* Wr, const f
     return launch_route(x, x_dtype, T, d, Wr, bias, E, k, ids, gates, w.logits, as_stream(s));
 }
 
+int moe_route_permute(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
+                      int32_t* ids, float* gates, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
+                      int32_t* dest, int32_t* active, void* ws, size_t ws_bytes, moe_stream_t s) {
+    if (T < 0 || !shape_ok(d, E, k) || (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16)) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !Wr || !ids || !gates || !counts || !offsets || !sorted_idx || !dest || !active || !ws)
+        return MOE_ERR_INVALID_ARG;
+    Workspace w;
+    workspace_layout(T, d, 128, E, k, MOE_ACT_FLOAT, (char*)ws, &w);
+    if (ws_bytes < w.permute_bytes) return MOE_ERR_NO_MEMORY;
+    if (route_small_ok(T, d, k))
+        return launch_route_small(x, x_dtype, T, d, Wr, bias, E, k, ids, gates, w.logits, true, counts, offsets,
+                                  sorted_idx, dest, active, as_stream(s));
+    int rc = launch_route(x, x_dtype, T, d, Wr, bias, E, k, ids, gates, w.logits, as_stream(s));
+    if (rc) return rc;
+    return launch_permute(ids, T, k, E, counts, offsets, sorted_idx, dest, active, w.hist, as_stream(s));
+}
+
 int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
                 int32_t* dest, int32_t* active, void* ws, size_t ws_bytes, moe_stream_t s) {
     if (T < 0 || k < 1 || k > 64 || E < k || E > 1024 || (long)T * k > (1l << 30)) return MOE_ERR_INVALID_ARG;
@@ -137,7 +153,7 @@ int moe_expert_ffn(const moe_ffn_args* a, moe_stream_t s) {
     if (a->T < 0 || !shape_ok(a->d, a->E, a->k) || a->f <= 0 || a->f % 128 ||
         (a->wfmt != MOE_WFMT_I4B32 && a->wfmt != MOE_WFMT_I8B32) ||
         (a->act_mode != MOE_ACT_FLOAT && a->act_mode != MOE_ACT_Q8) ||
-        (a->y_dtype != MOE_DT_F32 && a->y_dtype != MOE_DT_F16))
+        (a->y_dtype != MOE_DT_F32 && a->y_dtype != MOE_DT_F16) || a->phase < 0 || a->phase > 2)
         return MOE_ERR_INVALID_ARG;
     if (a->T == 0) return MOE_OK;
     if (!a->expert_ptrs || !a->counts || !a->offsets || !a->sorted_idx || !a->active || !a->y_perm || !a->ws)

@@ -86,12 +86,11 @@ inline hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream
 // Regions are laid out in this order so that route and permute only need a
 // prefix of the workspace.
 struct Workspace {
-    double* logits;   // [T, E]                         route
-    int32_t* hist;    // [ceil(T*k / kPermChunk), E]    permute
-    int32_t* tiles;   // q8 tile list (int2) + count    ffn
-    _Float16* x16;    // float mode: activations as fp16 [T, d]
-    void* h;          // SwiGLU intermediate, rows T*k + T: fp16 (float mode) or int8 (q8)
-    float* hs;        // q8: [T*k + T, f/32] block scales of h
+    double* logits;     // [T, E]                         route
+    int32_t* hist;      // [ceil(T*k / kPermChunk), E]    permute
+    int32_t* tiles;     // q8 tile list (int2) + count    ffn
+    void* h;            // SwiGLU intermediate [T*k + T, f]: fp16 (float mode) or int8 (q8)
+    float* hs;          // q8: [T*k + T, f/32] block scales of h
     size_t route_bytes, permute_bytes, bytes;
 };
 constexpr int kPermChunk = 1024;
@@ -102,6 +101,11 @@ void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* bas
 int launch_pack(const void* src, void* dst, int n, int wfmt, int d, int f, bool unpack, hipStream_t s);
 int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
                  int32_t* ids, float* gates, double* logits, hipStream_t s);
+bool route_small_ok(int T, int d, int k);
+int launch_route_small(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
+                       int32_t* ids, float* gates, double* logits, bool do_permute, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_idx, int32_t* dest, int32_t* active, hipStream_t s);
+size_t float_h_bytes(int T, int f, int k);
 int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
                    int32_t* dest, int32_t* active, int32_t* hist, hipStream_t s);
 int launch_quant_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float* sx, hipStream_t s);

@@ -52,7 +52,19 @@ int launch_quant_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float
 }
 
 // out[t, o] = residual + y_shared + sum_j gates[t, j] * y_perm[dest[t*k + j], o]; j ascending.
-// One thread per (token, 4 consecutive features).
+// One thread per (token, 4 consecutive features); the k gathers of a chunk of
+// 16 slots are all issued before they are summed, in order.
+template <typename YT>
+__device__ __forceinline__ float4 load_y4(const YT* y, size_t off) {
+    if constexpr (sizeof(YT) == 4) {
+        return *reinterpret_cast<const float4*>(y + off);
+    } else {
+        const uint2 raw = *reinterpret_cast<const uint2*>(y + off);
+        const half2v a = __builtin_bit_cast(half2v, raw.x), b = __builtin_bit_cast(half2v, raw.y);
+        return make_float4((float)a.x, (float)a.y, (float)b.x, (float)b.y);
+    }
+}
+
 template <typename YT>
 __global__ __launch_bounds__(256) void combine(const YT* __restrict__ y, const int32_t* __restrict__ dest,
                                                const float* __restrict__ gates, const float* __restrict__ ysh,
@@ -67,19 +79,24 @@ __global__ __launch_bounds__(256) void combine(const YT* __restrict__ y, const i
         const float4 v = *reinterpret_cast<const float4*>(ysh + (size_t)t * d + o);
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
-    for (int j = 0; j < k; ++j) {
-        const float g = gates[(size_t)t * k + j];
-        const size_t row = (size_t)dest[(size_t)t * k + j] * d + o;
-        float4 v;
-        if constexpr (sizeof(YT) == 4) {
-            v = *reinterpret_cast<const float4*>(y + row);
-        } else {
-            const half2v* hp = reinterpret_cast<const half2v*>(y + row);
-            const half2v a = hp[0], b = hp[1];
-            v = make_float4((float)a.x, (float)a.y, (float)b.x, (float)b.y);
+    constexpr int U = 16;
+    for (int j0 = 0; j0 < k; j0 += U) {
+        float g[U];
+        float4 v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            if (j0 + j < k) {
+                g[j] = gates[(size_t)t * k + j0 + j];
+                v[j] = load_y4(y, (size_t)dest[(size_t)t * k + j0 + j] * d + o);
+            }
         }
-        acc.x = fmaf(g, v.x, acc.x); acc.y = fmaf(g, v.y, acc.y);
-        acc.z = fmaf(g, v.z, acc.z); acc.w = fmaf(g, v.w, acc.w);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            if (j0 + j < k) {
+                acc.x = fmaf(g[j], v[j].x, acc.x); acc.y = fmaf(g[j], v[j].y, acc.y);
+                acc.z = fmaf(g[j], v[j].z, acc.z); acc.w = fmaf(g[j], v[j].w, acc.w);
+            }
+        }
     }
     *reinterpret_cast<float4*>(out + (size_t)t * d + o) = acc;
 }

@@ -2,21 +2,24 @@
 //
 // Matrix-core formulation of the bandwidth-bound expert GEMV: a wavefront owns
 // a strip of 16 weight rows and multiplies it with up to 16 tokens per
-// v_mfma_f32_16x16x32_f16 (A = tokens x 32 k, B = 32 k x 16 weight rows, one
-// instruction per 32-wide quantisation block).  Weights are dequantised in
+// v_mfma_f32_16x16x32_f16 (A = 16 tokens x 32 k, B = 32 k x 16 weight rows,
+// one instruction per 32-wide quantisation block).  Weights are dequantised in
 // registers to exact fp16 integers (int4: 0x6400|u is 1024+u, minus 1032;
-// int8: 0x6400|(q+128) minus 1152), activations are fp16, each block's
-// product is exact-integer-weighted and the block's fp16 scale is applied in
-// fp32 (acc += s_b * D_b).  This keeps the VALU cost per weight near one
-// operation so the kernel stays on the HBM roofline for 1..64 tokens.
+// int8: 0x6400|(q+128) minus 1152); activations are rounded to fp16 once,
+// when a workgroup stages them in LDS; each block's exact-integer-weighted
+// product is scaled by the block's fp16 scale in fp32 (acc += s_b * D_b).
 //
-// Work items are (active expert or shared expert) x (row strip), grid-strided
-// over a device-side count, so no host synchronisation is needed.
+// gate/up: work item = (expert, 16 rows of f); the four wavefronts of a
+// workgroup split the reduction, each issuing all of its weight loads before
+// any math, and meet in LDS (fixed order, deterministic) to form
+// h = silu(g) * u in fp16.  down: work item = (expert, 64 output rows); each
+// wavefront holds the whole reduction length of its 16 rows in registers.
+// Activations / h rows of the current 16-token tile are staged once per
+// workgroup in LDS with 16-byte loads (d <= 2048 keeps 16 rows within 64 KiB).
+// Items are grid-strided over device-side counts: no host synchronisation.
 #include "common.hpp"
 
 namespace moe {
-
-constexpr int kMT = 4;  // m-tiles (16 tokens each) per pass
 
 __device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
 
@@ -43,141 +46,234 @@ __device__ __forceinline__ half8 dequant_block(const uint4v& w, int b) {
     return r;
 }
 
+// fp16 scale of block b of a packed tile, from its raw 32-bit words
 template <int WFMT>
-__device__ __forceinline__ void load_scales(const uint8_t* p, float* s) {
-    constexpr int NB = WFMT == MOE_WFMT_I4B32 ? 4 : 2;
-    if constexpr (NB == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        s[0] = (float)as_h2(v.x).x; s[1] = (float)as_h2(v.x).y;
-        s[2] = (float)as_h2(v.y).x; s[3] = (float)as_h2(v.y).y;
+__device__ __forceinline__ float scale_of(const uint2& raw, int b) {
+    if constexpr (WFMT == MOE_WFMT_I4B32) {
+        const uint32_t w = b < 2 ? raw.x : raw.y;
+        return (float)((b & 1) ? as_h2(w).y : as_h2(w).x);
     } else {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
-        s[0] = (float)as_h2(v).x; s[1] = (float)as_h2(v).y;
+        return (float)((b & 1) ? as_h2(raw.x).y : as_h2(raw.x).x);
     }
 }
 
-__device__ __forceinline__ half8 load_frag(const _Float16* p) {
-    return __builtin_bit_cast(half8, *reinterpret_cast<const uint4v*>(p));
+template <int WFMT>
+__device__ __forceinline__ uint2 load_scale_raw(const uint8_t* p) {
+    if constexpr (WFMT == MOE_WFMT_I4B32) return *reinterpret_cast<const uint2*>(p);
+    else return make_uint2(*reinterpret_cast<const uint32_t*>(p), 0u);
 }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
-// x (f32 or bf16) -> fp16 copy used as the A operand.
-template <typename XT>
-__global__ __launch_bounds__(256) void to_f16(const XT* __restrict__ x, long n, _Float16* __restrict__ out) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    if constexpr (sizeof(XT) == 4) out[i] = (_Float16)x[i];
-    else out[i] = (_Float16)bf16_bits_to_float(x[i]);
+constexpr int kChunkK = 512;       // k held in registers per wavefront and matrix (4 int4 / 8 int8 tiles)
+
+struct SlotInfo {
+    const uint8_t* blob;
+    int c, p0;
+    bool routed;
+};
+
+__device__ __forceinline__ SlotInfo slot_info(int a, int n_active, const int32_t* active,
+                                              const void* const* expert_ptrs, const uint8_t* shared_blob,
+                                              const int32_t* counts, const int32_t* offsets, int T, int k) {
+    SlotInfo s;
+    if (a < n_active) {
+        const int e = active[1 + a];
+        s.blob = (const uint8_t*)expert_ptrs[e];
+        s.c = counts[e];
+        s.p0 = offsets[e];
+        s.routed = true;
+    } else {
+        s.blob = shared_blob;
+        s.c = T;
+        s.p0 = T * k;
+        s.routed = false;
+    }
+    return s;
 }
 
-// gate/up + SwiGLU.  One workgroup (4 wavefronts) per item = 16 rows of f;
-// the 4 wavefronts split the k tiles and reduce through LDS.
-template <int WFMT>
-__global__ __launch_bounds__(256) void ffn_float_gateup(const _Float16* __restrict__ x16, int T, int d, int f, int k,
+// 8 consecutive activations as fp16 (x is fp32 or bf16; 16-byte aligned runs)
+template <typename XT>
+__device__ __forceinline__ half8 load8_h(const XT* p) {
+    half8 v;
+    if constexpr (sizeof(XT) == 4) {
+        const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+        v = half8{(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w,
+                  (_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
+    } else {
+        const uint4 r = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = (_Float16)__uint_as_float(w[j] << 16);
+            v[2 * j + 1] = (_Float16)__uint_as_float(w[j] & 0xFFFF0000u);
+        }
+    }
+    return v;
+}
+
+// Registers of one wavefront's weight chunk: NT packed tiles of two matrices.
+template <int NT>
+struct WChunk {
+    uint4v q0[NT], q1[NT];
+    uint2 s0[NT], s1[NT];
+};
+
+template <int WFMT, int NT>
+__device__ __forceinline__ void load_chunk(WChunk<NT>& w, const uint8_t* blob, const MatLayout& M0,
+                                           const MatLayout& M1, bool two, size_t tile0, int t_lo, int nt, int lane) {
+    constexpr int STB = (WFMT == MOE_WFMT_I4B32 ? 4 : 2) * 32;
+    constexpr int NB = STB / 32;
+    const uint4v* q0 = reinterpret_cast<const uint4v*>(blob + M0.qoff + tile0 * 1024) + lane;
+    const uint4v* q1 = reinterpret_cast<const uint4v*>(blob + M1.qoff + tile0 * 1024) + lane;
+    const uint8_t* s0 = blob + M0.soff + tile0 * STB + (lane & 15) * NB * 2;
+    const uint8_t* s1 = blob + M1.soff + tile0 * STB + (lane & 15) * NB * 2;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        if (i < nt) {
+            w.q0[i] = q0[(size_t)(t_lo + i) * 64];
+            w.s0[i] = load_scale_raw<WFMT>(s0 + (size_t)(t_lo + i) * STB);
+            if (two) {
+                w.q1[i] = q1[(size_t)(t_lo + i) * 64];
+                w.s1[i] = load_scale_raw<WFMT>(s1 + (size_t)(t_lo + i) * STB);
+            }
+        }
+    }
+}
+
+// products of one gate/up weight chunk with the staged 16-token tile
+template <int WFMT, int NT>
+__device__ __forceinline__ void gu_chunk(const WChunk<NT>& w, int c0, int nt, const uint4* xs4, int XC, bool ok,
+                                         int lane, float4v& accg, float4v& accu) {
+    constexpr int NB = WFMT == MOE_WFMT_I4B32 ? 4 : 2;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        if (i >= nt) break;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const half8 Bg = dequant_block<WFMT>(w.q0[i], b);
+            const half8 Bu = dequant_block<WFMT>(w.q1[i], b);
+            const int kk = ((c0 + i) * NB + b) * 32 + 8 * (lane >> 4);
+            const int rr = lane & 15;
+            const half8 A = ok ? __builtin_bit_cast(half8, xs4[rr * XC + ((kk >> 3) ^ rr)]) : half8{};
+            const float4v dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bg, float4v{0, 0, 0, 0}, 0, 0, 0);
+            const float4v du = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bu, float4v{0, 0, 0, 0}, 0, 0, 0);
+            const float sg = scale_of<WFMT>(w.s0[i], b), su = scale_of<WFMT>(w.s1[i], b);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                accg[r] = fmaf(sg, dg[r], accg[r]);
+                accu[r] = fmaf(su, du[r], accu[r]);
+            }
+        }
+    }
+}
+
+// products of one down weight chunk with the staged 16-row h tile
+template <int WFMT, int NT>
+__device__ __forceinline__ void dn_chunk(const WChunk<NT>& w, int c0, int nt, const uint4* hs4, int HC, bool ok,
+                                         int lane, float4v& acc) {
+    constexpr int NB = WFMT == MOE_WFMT_I4B32 ? 4 : 2;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        if (i >= nt) break;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const half8 Bw = dequant_block<WFMT>(w.q0[i], b);
+            const int kk = ((c0 + i) * NB + b) * 32 + 8 * (lane >> 4);
+            const int rr = lane & 15;
+            const half8 A = ok ? __builtin_bit_cast(half8, hs4[rr * HC + ((kk >> 3) ^ rr)]) : half8{};
+            const float4v dv = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bw, float4v{0, 0, 0, 0}, 0, 0, 0);
+            const float sc = scale_of<WFMT>(w.s0[i], b);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, dv[r], acc[r]);
+        }
+    }
+}
+
+// gate/up + SwiGLU.  Workgroup = (slot, 16 rows of f); wavefront w covers the
+// w-th quarter of the packed k tiles; activations of the current 16-token
+// tile are staged once in LDS as fp16; the four partial sums meet in LDS and
+// h = silu(g) * u is written as fp16.
+template <int WFMT, typename XT>
+__global__ __launch_bounds__(256) void ffn_float_gateup(const XT* __restrict__ x, int T, int d, int f, int k,
                                                         const void* const* __restrict__ expert_ptrs,
                                                         const uint8_t* __restrict__ shared_blob,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ sorted_idx,
                                                         const int32_t* __restrict__ active, _Float16* __restrict__ h) {
-    constexpr int NB = WFMT == MOE_WFMT_I4B32 ? 4 : 2;
-    constexpr int STB = NB * 32;  // scale-tile bytes: 16 rows x NB fp16
-    __shared__ float red[4][2][kMT][4][64];
+    constexpr int KPT = WFMT == MOE_WFMT_I4B32 ? 128 : 64;
+    constexpr int NB = KPT / 32;
+    constexpr int kMaxT = kChunkK / KPT;
+    // LDS: 16 activation rows of d fp16, 16-byte chunk c of row r stored at
+    // chunk (c ^ r) so the 16 rows read by one MFMA operand hit distinct banks;
+    // after the products, the same space holds the split-k partial sums.
+    extern __shared__ __align__(16) uint4 xs4[];  // [16][d / 8]
+    float(*red)[2][4][64] = reinterpret_cast<float(*)[2][4][64]>(xs4);  // [4][2][4][64]
+    const int XC = d / 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_strips = f / 16;
+    const int nkt = d / KPT;
+    const int kt_lo = (wave * nkt) / 4, kt_hi = ((wave + 1) * nkt) / 4;
+    const int nt0 = min(kMaxT, kt_hi - kt_lo);
     const int n_active = active[0];
     const int n_items = (n_active + (shared_blob ? 1 : 0)) * n_strips;
     const ExpertLayout L = expert_layout(WFMT, d, f);
-    const int nkt = L.g.nkt;
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int a = item / n_strips, strip = item % n_strips;
-        const uint8_t* blob;
-        int c, p0;
-        bool routed;
-        if (a < n_active) {
-            const int e = active[1 + a];
-            blob = (const uint8_t*)expert_ptrs[e];
-            c = counts[e];
-            p0 = offsets[e];
-            routed = true;
-        } else {
-            blob = shared_blob;
-            c = T;
-            p0 = T * k;
-            routed = false;
-        }
-        const uint4v* gq = reinterpret_cast<const uint4v*>(blob + L.g.qoff + (size_t)strip * nkt * 1024) + lane;
-        const uint4v* uq = reinterpret_cast<const uint4v*>(blob + L.u.qoff + (size_t)strip * nkt * 1024) + lane;
-        const uint8_t* gs = blob + L.g.soff + (size_t)strip * nkt * STB + (lane & 15) * NB * 2;
-        const uint8_t* us = blob + L.u.soff + (size_t)strip * nkt * STB + (lane & 15) * NB * 2;
-        for (int m0 = 0; m0 < c; m0 += 16 * kMT) {
-            const _Float16* xrow[kMT];
-            bool ok[kMT];
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) {
-                const int m = m0 + mt * 16 + (lane & 15);
-                ok[mt] = m < c;
-                const int t = ok[mt] ? (routed ? sorted_idx[p0 + m] / k : m) : 0;
-                xrow[mt] = x16 + (size_t)t * d + 8 * (lane >> 4);
-            }
-            float4v accg[kMT], accu[kMT];
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) { accg[mt] = float4v{0, 0, 0, 0}; accu[mt] = float4v{0, 0, 0, 0}; }
-            for (int kt = wave; kt < nkt; kt += 4) {
-                const uint4v wg = gq[(size_t)kt * 64];
-                const uint4v wu = uq[(size_t)kt * 64];
-                float sg[NB], su[NB];
-                load_scales<WFMT>(gs + (size_t)kt * STB, sg);
-                load_scales<WFMT>(us + (size_t)kt * STB, su);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const half8 Bg = dequant_block<WFMT>(wg, b);
-                    const half8 Bu = dequant_block<WFMT>(wu, b);
-                    const int kk = (kt * NB + b) * 32;
-#pragma unroll
-                    for (int mt = 0; mt < kMT; ++mt) {
-                        if (m0 + mt * 16 >= c) break;
-                        const half8 A = ok[mt] ? load_frag(xrow[mt] + kk) : half8{};
-                        const float4v dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bg, float4v{0, 0, 0, 0}, 0, 0, 0);
-                        const float4v du = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bu, float4v{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            accg[mt][r] = fmaf(sg[b], dg[r], accg[mt][r]);
-                            accu[mt][r] = fmaf(su[b], du[r], accu[mt][r]);
-                        }
+        const int strip = item % n_strips;
+        const SlotInfo S = slot_info(item / n_strips, n_active, active, expert_ptrs, shared_blob, counts, offsets,
+                                     T, k);
+        const size_t tile0 = (size_t)strip * nkt;
+        for (int m0 = 0; m0 < S.c; m0 += 16) {
+            const int nrow = min(16, S.c - m0);
+            float4v accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+            const bool ok = (lane & 15) < nrow;
+            for (int c0 = kt_lo; c0 < kt_hi; c0 += kMaxT) {
+                // weight chunk in flight before (on the first chunk) the activations are staged
+                const int nt = min(kMaxT, kt_hi - c0);
+                WChunk<kMaxT> w;
+                load_chunk<WFMT, kMaxT>(w, S.blob, L.g, L.u, true, tile0, c0, nt, lane);
+                if (c0 == kt_lo) {
+                    __syncthreads();
+                    const int per_row = d / 8;
+                    for (int idx = threadIdx.x; idx < nrow * per_row; idx += 256) {
+                        const int r = idx / per_row, c8 = (idx % per_row) * 8;
+                        const int m = m0 + r;
+                        const int t = S.routed ? sorted_idx[S.p0 + m] / k : m;
+                        xs4[r * XC + ((c8 >> 3) ^ r)] = __builtin_bit_cast(uint4, load8_h(x + (size_t)t * d + c8));
                     }
+                    __syncthreads();
                 }
+                gu_chunk<WFMT, kMaxT>(w, c0, nt, xs4, XC, ok, lane, accg, accu);
             }
+            if (kt_lo == kt_hi) {  // no k tiles for this wavefront (small d): join the staging barriers
+                __syncthreads();
+                __syncthreads();
+            }
+            __syncthreads();  // all products done before the staging space is reused
 #pragma unroll
-            for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    red[wave][0][mt][r][lane] = accg[mt][r];
-                    red[wave][1][mt][r][lane] = accu[mt][r];
-                }
+            for (int r = 0; r < 4; ++r) {
+                red[wave][0][r][lane] = accg[r];
+                red[wave][1][r][lane] = accu[r];
+            }
             __syncthreads();
+            // wavefront w finalises accumulator row r = w (tokens 4*(lane/16) + w)
             {
-                const int mt = wave;  // wavefront w finalises m-tile w
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + mt * 16 + 4 * (lane >> 4) + r;
-                    if (m < c) {
-                        const float g = red[0][0][mt][r][lane] + red[1][0][mt][r][lane] + red[2][0][mt][r][lane] +
-                                        red[3][0][mt][r][lane];
-                        const float u = red[0][1][mt][r][lane] + red[1][1][mt][r][lane] + red[2][1][mt][r][lane] +
-                                        red[3][1][mt][r][lane];
-                        const int n = strip * 16 + (lane & 15);
-                        h[(size_t)(p0 + m) * f + n] = (_Float16)(silu_f(g) * u);
-                    }
+                const int r = wave;
+                const int m = m0 + 4 * (lane >> 4) + r;
+                if (m < S.c) {
+                    const float g = red[0][0][r][lane] + red[1][0][r][lane] + red[2][0][r][lane] + red[3][0][r][lane];
+                    const float u = red[0][1][r][lane] + red[1][1][r][lane] + red[2][1][r][lane] + red[3][1][r][lane];
+                    h[(size_t)(S.p0 + m) * f + strip * 16 + (lane & 15)] = (_Float16)(silu_f(g) * u);
                 }
             }
-            __syncthreads();
         }
     }
 }
 
-// down projection.  One wavefront per 16 output rows; 4 strips per workgroup.
+// down projection: workgroup = (slot, 64 output rows), 16 rows per
+// wavefront; the reduction over f runs in chunks of kChunkK held in
+// registers; h rows of the current 16-token tile are staged in LDS.
 template <int WFMT, typename YT>
 __global__ __launch_bounds__(256) void ffn_float_down(const _Float16* __restrict__ h, int T, int d, int f, int k,
                                                       const void* const* __restrict__ expert_ptrs,
@@ -186,109 +282,95 @@ __global__ __launch_bounds__(256) void ffn_float_down(const _Float16* __restrict
                                                       const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ active, YT* __restrict__ y_perm,
                                                       float* __restrict__ y_shared) {
-    constexpr int NB = WFMT == MOE_WFMT_I4B32 ? 4 : 2;
-    constexpr int STB = NB * 32;
+    constexpr int KPT = WFMT == MOE_WFMT_I4B32 ? 128 : 64;
+    constexpr int NB = KPT / 32;
+    constexpr int kMaxT = kChunkK / KPT;
+    extern __shared__ __align__(16) uint4 hs4[];  // [16][f / 8], chunk c of row r at (c ^ r)
+    const int HC = f / 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_groups = d / 64;
     const int n_active = active[0];
     const int n_items = (n_active + (shared_blob ? 1 : 0)) * n_groups;
     const ExpertLayout L = expert_layout(WFMT, d, f);
     const int nkt = L.dn.nkt;
+    const int nt0 = min(kMaxT, nkt);
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int a = item / n_groups, strip = (item % n_groups) * 4 + wave;
-        const uint8_t* blob;
-        int c, p0;
-        bool routed;
-        if (a < n_active) {
-            const int e = active[1 + a];
-            blob = (const uint8_t*)expert_ptrs[e];
-            c = counts[e];
-            p0 = offsets[e];
-            routed = true;
-        } else {
-            blob = shared_blob;
-            c = T;
-            p0 = T * k;
-            routed = false;
-        }
-        const uint4v* dq = reinterpret_cast<const uint4v*>(blob + L.dn.qoff + (size_t)strip * nkt * 1024) + lane;
-        const uint8_t* ds = blob + L.dn.soff + (size_t)strip * nkt * STB + (lane & 15) * NB * 2;
-        for (int m0 = 0; m0 < c; m0 += 16 * kMT) {
-            const _Float16* hrow[kMT];
-            bool ok[kMT];
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) {
-                const int m = m0 + mt * 16 + (lane & 15);
-                ok[mt] = m < c;
-                hrow[mt] = h + (size_t)(p0 + (ok[mt] ? m : 0)) * f + 8 * (lane >> 4);
-            }
-            float4v acc[kMT];
-#pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
-            for (int kt = 0; kt < nkt; ++kt) {
-                const uint4v wq = dq[(size_t)kt * 64];
-                float s[NB];
-                load_scales<WFMT>(ds + (size_t)kt * STB, s);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const half8 B = dequant_block<WFMT>(wq, b);
-                    const int kk = (kt * NB + b) * 32;
-#pragma unroll
-                    for (int mt = 0; mt < kMT; ++mt) {
-                        if (m0 + mt * 16 >= c) break;
-                        const half8 A = ok[mt] ? load_frag(hrow[mt] + kk) : half8{};
-                        const float4v dv = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, float4v{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[mt][r] = fmaf(s[b], dv[r], acc[mt][r]);
+        const int grp = item % n_groups;
+        const SlotInfo S = slot_info(item / n_groups, n_active, active, expert_ptrs, shared_blob, counts, offsets,
+                                     T, k);
+        const int strip = grp * 4 + wave;
+        const size_t tile0 = (size_t)strip * nkt;
+        for (int m0 = 0; m0 < S.c; m0 += 16) {
+            const int nrow = min(16, S.c - m0);
+            const bool ok = (lane & 15) < nrow;
+            float4v acc = {0, 0, 0, 0};
+            for (int c0 = 0; c0 < nkt; c0 += kMaxT) {
+                const int nt = min(kMaxT, nkt - c0);
+                WChunk<kMaxT> w;
+                load_chunk<WFMT, kMaxT>(w, S.blob, L.dn, L.dn, false, tile0, c0, nt, lane);
+                if (c0 == 0) {
+                    __syncthreads();
+                    for (int idx = threadIdx.x; idx < nrow * HC; idx += 256) {
+                        const int r = idx / HC, c = idx % HC;
+                        hs4[r * HC + (c ^ r)] = *reinterpret_cast<const uint4*>(h + (size_t)(S.p0 + m0 + r) * f + 8 * c);
                     }
+                    __syncthreads();
                 }
+                dn_chunk<WFMT, kMaxT>(w, c0, nt, hs4, HC, ok, lane, acc);
             }
             const int o = strip * 16 + (lane & 15);
 #pragma unroll
-            for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + mt * 16 + 4 * (lane >> 4) + r;
-                    if (m >= c) continue;
-                    if (routed) y_perm[(size_t)(p0 + m) * d + o] = (YT)acc[mt][r];
-                    else y_shared[(size_t)m * d + o] = acc[mt][r];
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 4 * (lane >> 4) + r;
+                if (m >= S.c) continue;
+                if (S.routed) y_perm[(size_t)(S.p0 + m) * d + o] = (YT)acc[r];
+                else y_shared[(size_t)m * d + o] = acc[r];
+            }
         }
     }
 }
 
-template <int WFMT>
+size_t float_h_bytes(int T, int f, int k) { return ((size_t)T * k + T) * (size_t)f * sizeof(_Float16); }
+
+template <int WFMT, typename XT>
 static int run_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
-    const long n = (long)a->T * a->d;
-    _Float16* x16 = w.x16;
-    const int cgrid = (int)((n + 255) / 256);
-    if (a->x_dtype == MOE_DT_F32) to_f16<float><<<cgrid, 256, 0, s>>>((const float*)a->x, n, x16);
-    else to_f16<uint16_t><<<cgrid, 256, 0, s>>>((const uint16_t*)a->x, n, x16);
-    int rc = check_launch();
-    if (rc) return rc;
     const int max_active = a->E < a->T * a->k ? a->E : a->T * a->k;
     const int slots = max_active + (a->shared_blob ? 1 : 0);
-    const int g1 = (int)std::min<long>((long)slots * (a->f / 16), 8192);
+    const int rows_lds = std::min(16, a->T);
     _Float16* h = reinterpret_cast<_Float16*>(w.h);
-    ffn_float_gateup<WFMT><<<g1, 256, 0, s>>>(x16, a->T, a->d, a->f, a->k, a->expert_ptrs,
-                                              (const uint8_t*)a->shared_blob, a->counts, a->offsets, a->sorted_idx,
-                                              a->active, h);
-    rc = check_launch();
-    if (rc) return rc;
-    const int g2 = (int)std::min<long>((long)slots * (a->d / 64), 8192);
+    int dev = 0, n_cu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    const int g1 = (int)std::min<long>((long)slots * (a->f / 16), (long)n_cu * 64);
+    const size_t lds1 = std::max<size_t>((size_t)rows_lds * a->d * sizeof(_Float16), 4 * 2 * 4 * 64 * sizeof(float));
+    if (a->phase != 2) {
+        ffn_float_gateup<WFMT, XT><<<g1, 256, lds1, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs,
+                                                         (const uint8_t*)a->shared_blob, a->counts, a->offsets,
+                                                         a->sorted_idx, a->active, h);
+        const int rc = check_launch();
+        if (rc || a->phase == 1) return rc;
+    }
+    const int g2 = (int)std::min<long>((long)slots * (a->d / 64), (long)n_cu * 64);
+    const size_t lds2 = (size_t)rows_lds * a->f * sizeof(_Float16);
     if (a->y_dtype == MOE_DT_F32)
-        ffn_float_down<WFMT, float><<<g2, 256, 0, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
-                                                       (const uint8_t*)a->shared_blob, a->counts, a->offsets,
-                                                       a->active, (float*)a->y_perm, a->y_shared);
-    else
-        ffn_float_down<WFMT, _Float16><<<g2, 256, 0, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
+        ffn_float_down<WFMT, float><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
                                                           (const uint8_t*)a->shared_blob, a->counts, a->offsets,
-                                                          a->active, (_Float16*)a->y_perm, a->y_shared);
+                                                          a->active, (float*)a->y_perm, a->y_shared);
+    else
+        ffn_float_down<WFMT, _Float16><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
+                                                             (const uint8_t*)a->shared_blob, a->counts, a->offsets,
+                                                             a->active, (_Float16*)a->y_perm, a->y_shared);
     return check_launch();
 }
 
 int launch_ffn_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
-    return a->wfmt == MOE_WFMT_I4B32 ? run_float<MOE_WFMT_I4B32>(a, w, s) : run_float<MOE_WFMT_I8B32>(a, w, s);
+    // LDS holds 16 activation rows of d (fp16) in gate/up; registers hold all f in down
+    if ((size_t)std::min(16, a->T) * a->d * 2 > 64 * 1024 || a->f / 8 < 16 || a->d / 8 < 16)
+        return MOE_ERR_UNSUPPORTED;
+    if (a->wfmt == MOE_WFMT_I4B32)
+        return a->x_dtype == MOE_DT_F32 ? run_float<MOE_WFMT_I4B32, float>(a, w, s)
+                                        : run_float<MOE_WFMT_I4B32, uint16_t>(a, w, s);
+    return a->x_dtype == MOE_DT_F32 ? run_float<MOE_WFMT_I8B32, float>(a, w, s)
+                                    : run_float<MOE_WFMT_I8B32, uint16_t>(a, w, s);
 }
 
 }  // namespace moe

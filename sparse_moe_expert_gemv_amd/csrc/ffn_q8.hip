@@ -329,18 +329,23 @@ template <int WFMT>
 static int run_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     int2* tiles = reinterpret_cast<int2*>(w.tiles);
     int32_t* n_tiles = w.tiles + 2 * q8_tile_capacity(a->T, a->k, a->E);
-    q8_plan<<<1, 1024, 0, s>>>(a->counts, a->active, a->E, a->T, a->shared_blob ? 1 : 0, tiles, n_tiles);
-    int rc = check_launch();
-    if (rc) return rc;
+    int rc;
+    if (a->phase != 2) {
+        q8_plan<<<1, 1024, 0, s>>>(a->counts, a->active, a->E, a->T, a->shared_blob ? 1 : 0, tiles, n_tiles);
+        rc = check_launch();
+        if (rc) return rc;
+    }
     const long max_tiles = (long)std::min(a->E, a->T * a->k) + (long)a->T * a->k / kMG + (a->shared_blob ? a->T / kMG + 1 : 0);
     const size_t smem = sizeof(Q8Smem);
     int8_t* hq = reinterpret_cast<int8_t*>(w.h);
     const int g1 = (int)std::min<long>(max_tiles * (a->f / 64), 4096);
-    ffn_q8_gateup<WFMT><<<g1, 256, smem, s>>>(a->xq, a->sx, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs,
-                                              (const uint8_t*)a->shared_blob, a->counts, a->offsets, a->sorted_idx,
-                                              tiles, n_tiles, hq, w.hs);
-    rc = check_launch();
-    if (rc) return rc;
+    if (a->phase != 2) {
+        ffn_q8_gateup<WFMT><<<g1, 256, smem, s>>>(a->xq, a->sx, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs,
+                                                  (const uint8_t*)a->shared_blob, a->counts, a->offsets,
+                                                  a->sorted_idx, tiles, n_tiles, hq, w.hs);
+        rc = check_launch();
+        if (rc || a->phase == 1) return rc;
+    }
     const int g2 = (int)std::min<long>(max_tiles * (a->d / kRows), 4096);
     if (a->y_dtype == MOE_DT_F32)
         ffn_q8_down<WFMT, float><<<g2, 256, smem, s>>>(hq, w.hs, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs,

@@ -4,52 +4,351 @@
 // probabilities, follows the router description of the Strata pages ("single
 // RTX 5090 runs a 125B model": a light gating network picks the top-K
 // experts per token; the others do not compute).
+//
+// Small and moderate batches: every wavefront computes one router row against
+// a group of up to 8 tokens staged in LDS; for small batches a single
+// workgroup then selects the top-k of every token and, when asked, also groups
+// the routing slots by expert (the moe_permute outputs), so decode routing is
+// two launches.  A device-wide last-workgroup election would need an
+// agent-scope release per workgroup, which on this multi-die part writes back
+// the L2 each time; the kernel boundary is cheaper.
 #include <float.h>
 
+#include <algorithm>
+
 #include "common.hpp"
+#include "wave.hpp"
 
 namespace moe {
 
 template <typename XT>
-__device__ __forceinline__ double load_x(const XT* x, size_t i);
+__device__ __forceinline__ float load_xf(const XT* x, size_t i);
 template <>
-__device__ __forceinline__ double load_x<float>(const float* x, size_t i) { return (double)x[i]; }
+__device__ __forceinline__ float load_xf<float>(const float* x, size_t i) { return x[i]; }
 template <>
-__device__ __forceinline__ double load_x<uint16_t>(const uint16_t* x, size_t i) {
-    return (double)bf16_bits_to_float(x[i]);
+__device__ __forceinline__ float load_xf<uint16_t>(const uint16_t* x, size_t i) { return bf16_bits_to_float(x[i]); }
+
+// ---------------------------------------------------------------- top-k ----
+constexpr int kMaxPerLane = 16;  // E <= 1024
+
+// Iterative wave argmax: k rounds of (lane best, wave best).  Exact; used when
+// the threshold filter below leaves more than 64 candidates.
+template <int NPL>
+__device__ void topk_iterative(double (&v)[NPL], int E, int k, int32_t* zi, double* zv) {
+    const int lane = threadIdx.x & 63;
+    for (int j = 0; j < k; ++j) {
+        double bv = -DBL_MAX;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+        }
+        wave_argmax(bv, bi);
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+            if (lane + 64 * i == bi) v[i] = -DBL_MAX;
+        if (lane == 0) { zi[j] = bi; zv[j] = bv; }
+    }
 }
 
-// Small T: one wavefront per expert row, all T tokens; Wr is read once,
-// coalesced (lane l reads features 2l + 128 i).
-template <typename XT, int TMAX>
-__global__ __launch_bounds__(256) void route_logits_rowdot(const XT* __restrict__ x, int T, int d,
-                                                           const float* __restrict__ Wr,
-                                                           const float* __restrict__ bias, int E,
-                                                           double* __restrict__ logits) {
+// One wavefront selects the top-k of z[0..E) by (value desc, index asc).
+//  1. every lane's maximum over its values; tau = the k-th best lane maximum
+//     (ranked by counting), so at least k values are >= tau;
+//  2. the values >= tau (usually k..2k) are compacted into LDS;
+//  3. each candidate's exact rank among the candidates is counted.
+// scratch: LDS for 64 (value, index) pairs plus k selected pairs.
+template <int NPL>
+__device__ void topk_wave(const double* __restrict__ z, int E, int k, int32_t* __restrict__ ids,
+                          float* __restrict__ gates, int32_t* s_ids, double* cv, int32_t* ci) {
     const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
-    double acc[TMAX];
+    double v[NPL];
+    double lm = -DBL_MAX;
+    int li = 0x7fffffff;
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) acc[t] = 0.0;
-    const float* w = Wr + (size_t)e * d;
-    for (int i = 2 * lane; i < d; i += 128) {
-        const float2 wv = *reinterpret_cast<const float2*>(w + i);
-        const double w0 = wv.x, w1 = wv.y;
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? z[e] : -DBL_MAX;
+        if (e < E && (v[i] > lm || (v[i] == lm && e < li))) { lm = v[i]; li = e; }
+    }
+    // rank of each lane maximum among the 64 (lanes with no value rank last)
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+        const double oj = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(lm), j),
+                                           __builtin_amdgcn_readlane(__double2loint(lm), j));
+        const int oi = __builtin_amdgcn_readlane(li, j);
+        rank += better(lm, li, oj, oi) ? 1 : 0;
+    }
+    const int nlanes = E < 64 ? E : 64;
+    const int kk = k < nlanes ? k : nlanes;  // with fewer lanes than k, take the weakest lane maximum
+    const unsigned long long sel = __ballot(lane < nlanes && rank == kk - 1);
+    const int src = __builtin_ffsll((long long)sel) - 1;
+    const double tau = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(lm), src),
+                                        __builtin_amdgcn_readlane(__double2loint(lm), src));
+    // candidates: every value >= tau (for E < 64*... all values >= tau are kept)
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int base = 0;
+    bool overflow = false;
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            if (t < T) {
-                acc[t] = fma(load_x(x, (size_t)t * d + i), w0, acc[t]);
-                acc[t] = fma(load_x(x, (size_t)t * d + i + 1), w1, acc[t]);
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        const bool c = e < E && v[i] >= tau;
+        const unsigned long long b = __ballot(c);
+        const int pos = base + __popcll(b & lt);
+        if (c && pos < 64) { cv[pos] = v[i]; ci[pos] = e; }
+        base += __popcll(b);
+    }
+    overflow = base > 64;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
+    double* zv = cv + 64;  // selected values [k]
+    int32_t* zi = ci + 64; // selected indices [k]
+    if (!overflow) {
+        const int nc = base;
+        if (lane < nc) {
+            const double mv = cv[lane];
+            const int mi = ci[lane];
+            int r = 0;
+            for (int j = 0; j < nc; ++j) r += better(mv, mi, cv[j], ci[j]) ? 1 : 0;
+            if (r < k) { zv[r] = mv; zi[r] = mi; }
+        }
+    } else {
+        topk_iterative<NPL>(v, E, k, zi, zv);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
+    double zsel = 0.0;
+    if (lane < k) {
+        zsel = zv[lane];
+        ids[lane] = zi[lane];
+        if (s_ids) s_ids[lane] = zi[lane];
+    }
+    const double z0 = zv[0];
+    const double p = lane < k ? exp(zsel - z0) : 0.0;
+    const double ssum = wave_sum_d(p);
+    if (lane < k) gates[lane] = (float)(p / ssum);
+}
+
+// per-wavefront LDS scratch of topk_wave: 64 + 64 candidates/selected pairs
+struct TopkScratch {
+    double v[128];
+    int32_t i[128];
+};
+
+template <int NPL>
+__device__ void topk_token(const double* z, int E, int k, int32_t* ids, float* gates, int32_t* s_ids,
+                           TopkScratch& S) {
+    topk_wave<NPL>(z, E, k, ids, gates, s_ids, S.v, S.i);
+}
+
+__device__ void topk_dispatch(const double* z, int E, int k, int32_t* ids, float* gates, int32_t* s_ids,
+                              TopkScratch& S) {
+    if (E <= 64) topk_token<1>(z, E, k, ids, gates, s_ids, S);
+    else if (E <= 128) topk_token<2>(z, E, k, ids, gates, s_ids, S);
+    else if (E <= 256) topk_token<4>(z, E, k, ids, gates, s_ids, S);
+    else if (E <= 512) topk_token<8>(z, E, k, ids, gates, s_ids, S);
+    else topk_token<16>(z, E, k, ids, gates, s_ids, S);
+}
+
+__global__ __launch_bounds__(256) void route_topk(const double* __restrict__ logits, int T, int E, int k,
+                                                  int32_t* __restrict__ ids, float* __restrict__ gates) {
+    __shared__ TopkScratch sc[4];
+    const int wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    topk_dispatch(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, nullptr, sc[wave]);
+}
+
+// ------------------------------------------------- block-level permutation ----
+// Stable grouping of n <= kSmallSlots slots held in LDS (s_ids) by one
+// 256-thread workgroup.  Same outputs as the multi-workgroup path.
+constexpr int kSmallSlots = 512;
+
+__device__ void block_permute(const int32_t* s_ids, int n, int E, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_idx, int32_t* dest, int32_t* active, int32_t* s_cnt, int32_t* s_part,
+                              int32_t* s_flag) {
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
+    __syncthreads();
+    for (int f = tid; f < n; f += 256) {
+        const int id = s_ids[f];
+        if ((unsigned)id < (unsigned)E) atomicAdd(&s_cnt[id], 1);
+    }
+    __syncthreads();
+    // exclusive scan of counts (and of active flags): 4 experts per thread, then 256 partials
+    int c4[4], p = 0, fl = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        c4[i] = e < E ? s_cnt[e] : 0;
+        p += c4[i];
+        fl += c4[i] > 0;
+    }
+    s_part[tid] = p;
+    s_flag[tid] = fl;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int a = tid >= off ? s_part[tid - off] : 0;
+        const int b = tid >= off ? s_flag[tid - off] : 0;
+        __syncthreads();
+        s_part[tid] += a;
+        s_flag[tid] += b;
+        __syncthreads();
+    }
+    int run = s_part[tid] - p, frun = s_flag[tid] - fl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid * 4 + i;
+        if (e < E) {
+            counts[e] = c4[i];
+            offsets[e] = run;
+            s_cnt[e] = run;  // becomes the running position of expert e
+            if (c4[i] > 0) active[1 + frun++] = e;
+            run += c4[i];
+        }
+    }
+    if (tid == 255) {
+        offsets[E] = s_part[255];
+        active[0] = s_flag[255];
+    }
+    __syncthreads();
+    // stable scatter by wavefront 0, slots in ascending order
+    if (tid < 64) {
+        const int lane = tid;
+        int nbits = 0;
+        while ((1 << nbits) < E) ++nbits;
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        for (int f0 = 0; f0 < n; f0 += 64) {
+            const int f = f0 + lane;
+            const int raw = f < n ? s_ids[f] : -1;
+            const bool valid = (unsigned)raw < (unsigned)E;
+            const int id = valid ? raw : 0;
+            unsigned long long peers = __ballot(valid);
+            for (int b = 0; b < nbits; ++b) {
+                const unsigned long long on = __ballot(valid && ((id >> b) & 1));
+                peers &= ((id >> b) & 1) ? on : ~on;
+            }
+            const int rank = __popcll(peers & lt);
+            const int cnt = __popcll(peers);
+            const int pos = valid ? s_cnt[id] + rank : 0;
+            __builtin_amdgcn_wave_barrier();
+            if (valid && rank == 0) s_cnt[id] += cnt;
+            __builtin_amdgcn_wave_barrier();
+            if (valid) {
+                sorted_idx[pos] = f;
+                dest[f] = pos;
             }
         }
     }
+}
+
+// ------------------------------------------------------ row-dot logits ----
+// grid = (ceil(E / 4), ceil(T / kTG)); wavefront w of workgroup (b, g) computes
+// router row e = 4b + w for the kTG tokens of group g, staged in LDS as fp32.
+// Wr rows are read with coalesced 16-byte loads, all issued before any math.
+constexpr int kTG = 8;
+template <typename XT>
+__global__ __launch_bounds__(256) void route_logits_rows(const XT* __restrict__ x, int T, int d,
+                                                         const float* __restrict__ Wr, const float* __restrict__ bias,
+                                                         int E, double* __restrict__ logits) {
+    extern __shared__ __align__(16) float xs[];  // [kTG][d]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.y * kTG;
+    const int nt = min(kTG, T - t0);
+    const int e = blockIdx.x * 4 + wave;
+    // router row loads first (8 x 16 bytes per lane per 2048 features)
+    const float4* w = reinterpret_cast<const float4*>(Wr + (size_t)(e < E ? e : 0) * d);
+    const int nq = d / 4;
+    // stage x (8 elements per thread-iteration, loads issued before the stores)
+    const int n8 = nt * d / 8;
+    for (int i0 = tid; i0 < n8; i0 += 256 * 4) {
+        float v[4][8];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        double v = acc[t];
-        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-        if (lane == 0 && t < T) logits[(size_t)t * E + e] = v + (bias ? (double)bias[e] : 0.0);
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * 256;
+            if (i < n8) {
+                const size_t g = (size_t)t0 * d + (size_t)i * 8;
+                if constexpr (sizeof(XT) == 4) {
+                    const float4 a = reinterpret_cast<const float4*>(x + g)[0];
+                    const float4 b = reinterpret_cast<const float4*>(x + g)[1];
+                    v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+                    v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
+                } else {
+                    const uint4 r = *reinterpret_cast<const uint4*>(x + g);
+                    const uint32_t wv[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v[u][2 * j] = __uint_as_float(wv[j] << 16);
+                        v[u][2 * j + 1] = __uint_as_float(wv[j] & 0xFFFF0000u);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * 256;
+            if (i < n8) {
+                float4* dst = reinterpret_cast<float4*>(xs + (size_t)i * 8);
+                dst[0] = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+                dst[1] = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+            }
+        }
     }
+    __syncthreads();
+    if (e >= E) return;
+    double acc[kTG];
+#pragma unroll
+    for (int t = 0; t < kTG; ++t) acc[t] = 0.0;
+    for (int q0 = 0; q0 < nq; q0 += 64 * 8) {
+        float4 wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int q = q0 + u * 64 + lane;
+            wv[u] = q < nq ? w[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int q = q0 + u * 64 + lane;
+            if (q >= nq) break;
+#pragma unroll
+            for (int t = 0; t < kTG; ++t) {
+                if (t >= nt) break;
+                const float4 xv = reinterpret_cast<const float4*>(xs + (size_t)t * d)[q];
+                acc[t] = fma((double)xv.x, (double)wv[u].x, acc[t]);
+                acc[t] = fma((double)xv.y, (double)wv[u].y, acc[t]);
+                acc[t] = fma((double)xv.z, (double)wv[u].z, acc[t]);
+                acc[t] = fma((double)xv.w, (double)wv[u].w, acc[t]);
+            }
+        }
+    }
+    const double b = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+    for (int t = 0; t < kTG; ++t) {
+        if (t >= nt) break;
+        const double s = wave_sum_d(acc[t]);
+        if (lane == 0) logits[(size_t)(t0 + t) * E + e] = s + b;
+    }
+}
+
+// One workgroup: top-k of every token (T <= kSmallSlots / k) and, when asked,
+// the grouping of the routing slots by expert.
+__global__ __launch_bounds__(256) void route_select_small(const double* __restrict__ logits, int T, int E, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                          int do_permute, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_idx,
+                                                          int32_t* __restrict__ dest, int32_t* __restrict__ active) {
+    __shared__ TopkScratch sc[4];
+    __shared__ int32_t s_ids[kSmallSlots];
+    __shared__ int32_t s_cnt[1024];
+    __shared__ int32_t s_part[256], s_flag[256];
+    const int wave = threadIdx.x >> 6;
+    for (int t = wave; t < T; t += 4)
+        topk_dispatch(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, s_ids + t * k,
+                      sc[wave]);
+    __syncthreads();
+    if (do_permute)
+        block_permute(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_cnt, s_part, s_flag);
 }
 
 // General T: 64 tokens x 64 experts per workgroup, 4x4 outputs per thread,
@@ -73,7 +372,7 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const XT* __restrict__
         for (int idx = threadIdx.x; idx < RK * RT; idx += 256) {
             const int kk = idx % RK, r = idx / RK;
             const int t = t0 + r, e = e0 + r;
-            xs[kk][r] = t < T ? load_x(x, (size_t)t * d + k0 + kk) : 0.0;
+            xs[kk][r] = t < T ? (double)load_xf(x, (size_t)t * d + k0 + kk) : 0.0;
             ws[kk][r] = e < E ? (double)Wr[(size_t)e * d + k0 + kk] : 0.0;
         }
         __syncthreads();
@@ -103,61 +402,17 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const XT* __restrict__
     }
 }
 
-// One wavefront per token: iterated wave argmax over the token's E logits
-// (lane l holds experts l, l+64, ...), then softmax over the k winners.
-constexpr int kMaxPerLane = 16;  // E <= 1024
-__global__ __launch_bounds__(256) void route_topk(const double* __restrict__ logits, int T, int E, int k,
-                                                  int32_t* __restrict__ ids, float* __restrict__ gates) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const double* z = logits + (size_t)t * E;
-    double v[kMaxPerLane];
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? z[e] : -DBL_MAX;
-    }
-    double zsel_mine = 0.0, z0 = 0.0;
-    for (int j = 0; j < k; ++j) {
-        // local best: highest value, lowest index on ties (slots scanned in ascending index)
-        double bv = -DBL_MAX;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
-        }
-        for (int off = 32; off > 0; off >>= 1) {
-            const double ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
-        if ((bi & 63) == lane) {
-#pragma unroll
-            for (int i = 0; i < kMaxPerLane; ++i)
-                if (lane + 64 * i == bi) v[i] = -DBL_MAX;  // finite logits always beat a taken slot
-        }
-        if (j == 0) z0 = bv;
-        if (lane == j) zsel_mine = bv;
-        if (lane == 0) ids[(size_t)t * k + j] = bi;
-    }
-    // softmax over the selected logits, max-shifted by the first (largest)
-    const double p = lane < k ? exp(zsel_mine - z0) : 0.0;
-    double s = p;
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane < k) gates[(size_t)t * k + lane] = (float)(p / s);
-}
+bool route_small_ok(int T, int d, int k) { return T <= 64 && (size_t)T * k <= kSmallSlots && (size_t)kTG * d * 4 <= 64 * 1024; }
 
-int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
-                 int32_t* ids, float* gates, double* logits, hipStream_t s) {
-    if (T == 0) return MOE_OK;
-    if (T <= 8) {
-        dim3 grid((E + 3) / 4);
+static int launch_logits(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E,
+                         double* logits, hipStream_t s) {
+    if (T <= 256 && (size_t)kTG * d * 4 <= 64 * 1024) {
+        const dim3 grid((E + 3) / 4, (T + kTG - 1) / kTG);
+        const size_t lds = (size_t)std::min(T, kTG) * d * sizeof(float);
         if (x_dtype == MOE_DT_F32)
-            route_logits_rowdot<float, 8><<<grid, 256, 0, s>>>((const float*)x, T, d, Wr, bias, E, logits);
+            route_logits_rows<float><<<grid, 256, lds, s>>>((const float*)x, T, d, Wr, bias, E, logits);
         else
-            route_logits_rowdot<uint16_t, 8><<<grid, 256, 0, s>>>((const uint16_t*)x, T, d, Wr, bias, E, logits);
+            route_logits_rows<uint16_t><<<grid, 256, lds, s>>>((const uint16_t*)x, T, d, Wr, bias, E, logits);
     } else {
         dim3 grid((E + RE - 1) / RE, (T + RT - 1) / RT);
         if (x_dtype == MOE_DT_F32)
@@ -165,7 +420,26 @@ int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, cons
         else
             route_logits_tiled<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)x, T, d, Wr, bias, E, logits);
     }
-    int rc = check_launch();
+    return check_launch();
+}
+
+int launch_route_small(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
+                       int32_t* ids, float* gates, double* logits, bool do_permute, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_idx, int32_t* dest, int32_t* active, hipStream_t s) {
+    int rc = launch_logits(x, x_dtype, T, d, Wr, bias, E, logits, s);
+    if (rc) return rc;
+    route_select_small<<<1, 256, 0, s>>>(logits, T, E, k, ids, gates, do_permute, counts, offsets, sorted_idx,
+                                         dest, active);
+    return check_launch();
+}
+
+int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
+                 int32_t* ids, float* gates, double* logits, hipStream_t s) {
+    if (T == 0) return MOE_OK;
+    if (route_small_ok(T, d, k))
+        return launch_route_small(x, x_dtype, T, d, Wr, bias, E, k, ids, gates, logits, false, nullptr, nullptr,
+                                  nullptr, nullptr, nullptr, s);
+    int rc = launch_logits(x, x_dtype, T, d, Wr, bias, E, logits, s);
     if (rc) return rc;
     route_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, ids, gates);
     return check_launch();

@@ -94,9 +94,9 @@ class MoELayer:
         k, E = self.k, self.E
         ws = self._ws_for(T)
         ids, gates = self.ids[:T], self.gates[:T]
-        B.moe_route(x, self.Wr, self.bias, k, ids, gates, ws, stream)
         n = T * k
-        B.moe_permute(ids, E, self.counts, self.offsets, self.sorted_idx[:n], self.dest[:n], self.active, ws, stream)
+        B.moe_route_permute(x, self.Wr, self.bias, k, ids, gates, self.counts, self.offsets, self.sorted_idx[:n],
+                            self.dest[:n], self.active, ws, stream)
         common = dict(T=T, d=self.d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
                       expert_ptrs=self.expert_ptrs if expert_ptrs is None else expert_ptrs,
                       counts=self.counts, offsets=self.offsets, sorted_idx=self.sorted_idx[:n],

@@ -226,3 +226,82 @@ def test_zero_tokens_is_noop():
     out = G.forward(xt)
     torch.cuda.synchronize()
     assert out.shape == (0, L.cfg.d)
+
+
+@pytest.mark.parametrize("name", ["decode_t4", "tiny"])
+def test_graph_replays_match_eager(name):
+    """The whole layer captured in a HIP graph: several replays, with eager
+    work and synchronisation between them, each bit-identical to the eager
+    result."""
+    L = _layer(name)
+    G = gpu_layer(L)
+    xt = x_tensor(L)
+    eager = host(G.forward(xt)).copy()
+    ids_eager = host(G.ids[:L.cfg.T]).copy()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            G.forward(xt)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        G.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(G.out[:L.cfg.T]), eager)
+        assert np.array_equal(host(G.ids[:L.cfg.T]), ids_eager)
+        junk = torch.randn(1024, device=DEV).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del junk
+
+
+def test_route_permute_fused_equals_separate_calls():
+    """moe_route_permute (selection and grouping in one workgroup for small T)
+    equals moe_route followed by moe_permute."""
+    L = _layer("decode_t4")
+    G = gpu_layer(L)
+    xt = x_tensor(L)
+    T, k, E = L.cfg.T, L.cfg.k, L.cfg.E
+    ws = G._ws_for(T)
+    B.moe_route_permute(xt, G.Wr, G.bias, k, G.ids[:T], G.gates[:T], G.counts, G.offsets, G.sorted_idx[:T * k],
+                        G.dest[:T * k], G.active, ws)
+    torch.cuda.synchronize()
+    a = routing_state(G, T)
+    a = {kk: v.copy() for kk, v in a.items()}
+    B.moe_route(xt, G.Wr, G.bias, k, G.ids[:T], G.gates[:T], ws)
+    B.moe_permute(G.ids[:T], E, G.counts, G.offsets, G.sorted_idx[:T * k], G.dest[:T * k], G.active, ws)
+    torch.cuda.synchronize()
+    b = routing_state(G, T)
+    for kk in a:
+        if kk == "active":
+            n = a[kk][0]
+            assert np.array_equal(a[kk][:n + 1], b[kk][:n + 1])
+        else:
+            assert np.array_equal(a[kk], b[kk]), kk
+
+
+@pytest.mark.parametrize("name", ["decode_t4", "tiny"])
+def test_ffn_phases_equal_whole_call(name):
+    """moe_expert_ffn with phase 1 (gate/up) then phase 2 (down) on the same
+    workspace gives bit-identical outputs to phase 0."""
+    L = _layer(name)
+    G = gpu_layer(L)
+    xt = x_tensor(L)
+    T, k = L.cfg.T, L.cfg.k
+    G.forward(xt)
+    torch.cuda.synchronize()
+    y0 = host(G.y_perm[:T * k]).copy()
+    ys0 = host(G.y_shared[:T]).copy() if G.shared is not None else None
+    G.y_perm.zero_()
+    G.y_shared.zero_()
+    common = dict(T=T, d=L.cfg.d, f=L.cfg.f, E=L.cfg.E, k=k, wfmt=L.cfg.wfmt, act_mode=G.act_mode,
+                  expert_ptrs=G.expert_ptrs, counts=G.counts, offsets=G.offsets, sorted_idx=G.sorted_idx[:T * k],
+                  active=G.active, y_perm=G.y_perm[:T * k], ws=G._ws_for(T), shared_blob=G.shared,
+                  y_shared=G.y_shared[:T] if G.shared is not None else None, x=xt)
+    B.moe_expert_ffn(phase=1, **common)
+    B.moe_expert_ffn(phase=2, **common)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(G.y_perm[:T * k]), y0)
+    if ys0 is not None:
+        assert np.array_equal(host(G.y_shared[:T]), ys0)

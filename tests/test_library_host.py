@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert B.moe_version() == 10000
+    assert B.moe_version() == 10100
     assert B.lib().moe_status_string(B.MOE_ERR_CACHE_CAPACITY) == b"MOE_ERR_CACHE_CAPACITY"
 
 
