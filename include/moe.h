@@ -154,6 +154,15 @@ int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_
  */
 int moe_quantize_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float* sx, moe_stream_t stream);
 
+/*
+ * Pre-norm of a stacked layer's input: out[t] = x[t] / sqrt(mean_i x[t,i]^2 + eps)
+ * (no learned gain), sums and scale in double, rounded once to fp32.
+ * x, out [T, d] fp32 (may alias).  The pages do not describe the block around
+ * the MoE layer; a stack of layers joined by a residual add, h + MoE(norm(h)),
+ * needs this normalisation to stay finite.
+ */
+int moe_rmsnorm(const float* x, int T, int d, float eps, float* out, moe_stream_t stream);
+
 /* Arguments of moe_expert_ffn. */
 typedef struct moe_ffn_args {
     int T, d, f, E, k;

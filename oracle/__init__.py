@@ -64,6 +64,7 @@ def _load():
         lib.orc_route.argtypes = [P, i, i, P, P, i, i, P, P, P]
         lib.orc_permute.argtypes = [P, i, i, i, P, P, P, P]
         lib.orc_quant8.argtypes = [P, i, i, P, P]
+        lib.orc_rmsnorm.argtypes = [P, i, i, C.c_double, P]
         lib.orc_expert_ffn.argtypes = [P, i, i, i, P, i, i, P, P, P]
         lib.orc_moe_layer.argtypes = [P, i, i, i, i, i, P, P, P, P, i, i, P, P, i, P, P, P, P, P, P, P]
         lib.orc_num_threads.restype = i
@@ -125,6 +126,14 @@ def permute(ids, E: int):
     dest = np.empty(T * k, dtype=np.int32)
     _check(_load().orc_permute(_p(ids), T, k, E, _p(counts), _p(offsets), _p(sorted_idx), _p(dest)), "permute")
     return counts, offsets, sorted_idx, dest
+
+
+def rmsnorm(x, eps: float = 1e-6):
+    x = _f32(x)
+    T, d = x.shape
+    out = np.empty((T, d), dtype=np.float32)
+    _check(_load().orc_rmsnorm(_p(x), T, d, eps, _p(out)), "rmsnorm")
+    return out
 
 
 def quant8(x):

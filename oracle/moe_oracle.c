@@ -226,6 +226,23 @@ int orc_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_
     return ORC_OK;
 }
 
+/* ---- pre-norm of a layer's input (layer stack) ---------------------------- */
+
+/* out[t,i] = x[t,i] / sqrt(mean_i(x[t,i]^2) + eps), in double, stored fp32.
+ * The pages do not describe the block around the MoE layer; a stack of layers
+ * with a residual add needs the usual pre-norm to stay finite (reading taken:
+ * RMSNorm without a learned gain). */
+int orc_rmsnorm(const float* x, int T, int d, double eps, float* out) {
+    if (T < 0 || d <= 0 || (T && (!x || !out))) return ORC_EINVAL;
+    for (int t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int i = 0; i < d; ++i) ss += (double)x[(size_t)t * d + i] * (double)x[(size_t)t * d + i];
+        double r = 1.0 / sqrt(ss / (double)d + eps);
+        for (int i = 0; i < d; ++i) out[(size_t)t * d + i] = (float)((double)x[(size_t)t * d + i] * r);
+    }
+    return ORC_OK;
+}
+
 /* ---- int8 activation quantisation -------------------------------------- */
 
 static void quant8_row(const float* x, int K, int8_t* q, float* s) {

@@ -27,7 +27,7 @@ MOE_ACT_FLOAT, MOE_ACT_Q8 = 0, 1
 EXPORTED = [
     "moe_version", "moe_last_hip_error", "moe_status_string", "moe_expert_bytes", "moe_pack_experts",
     "moe_unpack_experts", "moe_workspace_size", "moe_route", "moe_route_permute", "moe_permute", "moe_quantize_act",
-    "moe_expert_ffn",
+    "moe_expert_ffn", "moe_rmsnorm",
     "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
     "moe_cache_stage",
 ]
@@ -76,6 +76,7 @@ def lib():
             "moe_permute": ([P, I, I, I, P, P, P, P, P, P, S, P], I),
             "moe_route_permute": ([P, I, I, I, P, P, I, I, P, P, P, P, P, P, P, P, S, P], I),
             "moe_quantize_act": ([P, I, I, I, P, P, P], I),
+            "moe_rmsnorm": ([P, I, I, C.c_float, P, P], I),
             "moe_expert_ffn": ([C.POINTER(FfnArgs), P], I),
             "moe_combine": ([P, I, P, P, P, P, I, I, I, P, P], I),
             "moe_cache_create": ([C.POINTER(P), I, I, I, S, P, P, I, I], I),
@@ -174,6 +175,11 @@ def moe_permute(ids, E, counts, offsets, sorted_idx, dest, active, ws, stream=No
                                             _stream(stream)))
 
 
+def moe_rmsnorm(x, out, eps=1e-6, stream=None):
+    T, d = x.shape
+    _check("moe_rmsnorm", lib().moe_rmsnorm(_ptr(x), T, d, eps, _ptr(out), _stream(stream)))
+
+
 def moe_quantize_act(x, xq, sx, stream=None):
     T, d = x.shape
     _check("moe_quantize_act", lib().moe_quantize_act(_ptr(x), _xdtype(x), T, d, _ptr(xq), _ptr(sx),
@@ -234,10 +240,17 @@ class SlotCache:
         return list(hit[:nh.value]), list(miss[:nm.value])
 
     def stage(self, layer, buf, host_ptrs, dev_table, stream=None, done_event=None):
+        """Stage one layer on `stream`; done_event (a torch.cuda.Event) is recorded after it.
+
+        torch creates an event's HIP handle lazily on its first record, so the
+        event is recorded here through torch rather than handed to the library.
+        """
+        import torch
         src = (C.c_void_p * self.E)(*[int(p) for p in host_ptrs])
-        ev = None if done_event is None else C.c_void_p(done_event.cuda_event)
-        _check("moe_cache_stage", lib().moe_cache_stage(self.h, layer, buf, src, _ptr(dev_table), _stream(stream),
-                                                        ev))
+        st = stream if stream is not None else torch.cuda.current_stream()
+        _check("moe_cache_stage", lib().moe_cache_stage(self.h, layer, buf, src, _ptr(dev_table), _stream(st), None))
+        if done_event is not None:
+            done_event.record(st)
 
     def close(self):
         if self.h:

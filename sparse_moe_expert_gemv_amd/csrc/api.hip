@@ -141,6 +141,13 @@ int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_
     return launch_permute(ids, T, k, E, counts, offsets, sorted_idx, dest, active, w.hist, as_stream(s));
 }
 
+int moe_rmsnorm(const float* x, int T, int d, float eps, float* out, moe_stream_t s) {
+    if (T < 0 || d <= 0 || d % 4 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!x || !out) return MOE_ERR_INVALID_ARG;
+    return launch_rmsnorm(x, T, d, eps, out, as_stream(s));
+}
+
 int moe_quantize_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float* sx, moe_stream_t s) {
     if (T < 0 || d <= 0 || d % 32 || (x_dtype != MOE_DT_F32 && x_dtype != MOE_DT_BF16)) return MOE_ERR_INVALID_ARG;
     if (T == 0) return MOE_OK;

@@ -1,5 +1,7 @@
-// Activation quantisation (int8 per 32 features) and the weighted combine.
+// Activation quantisation (int8 per 32 features), the weighted combine and
+// the pre-norm of a stacked layer's input.
 #include "common.hpp"
+#include "wave.hpp"
 
 namespace moe {
 
@@ -99,6 +101,37 @@ __global__ __launch_bounds__(256) void combine(const YT* __restrict__ y, const i
         }
     }
     *reinterpret_cast<float4*>(out + (size_t)t * d + o) = acc;
+}
+
+// out[t] = x[t] / sqrt(mean(x[t]^2) + eps): one wavefront per row, sums of
+// squares and the scale in double, result rounded once to fp32.
+__global__ __launch_bounds__(256) void rmsnorm(const float* __restrict__ x, int T, int d, double eps,
+                                               float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)t * d);
+    float4* orow = reinterpret_cast<float4*>(out + (size_t)t * d);
+    double ss = 0.0;
+    for (int q = lane; q < d / 4; q += 64) {
+        const float4 v = xr[q];
+        ss = fma((double)v.x, (double)v.x, ss);
+        ss = fma((double)v.y, (double)v.y, ss);
+        ss = fma((double)v.z, (double)v.z, ss);
+        ss = fma((double)v.w, (double)v.w, ss);
+    }
+    ss = wave_sum_d(ss);
+    const double r = 1.0 / sqrt(ss / (double)d + eps);
+    for (int q = lane; q < d / 4; q += 64) {
+        const float4 v = xr[q];
+        orow[q] = make_float4((float)(v.x * r), (float)(v.y * r), (float)(v.z * r), (float)(v.w * r));
+    }
+}
+
+int launch_rmsnorm(const float* x, int T, int d, float eps, float* out, hipStream_t s) {
+    if (T == 0) return MOE_OK;
+    rmsnorm<<<(T + 3) / 4, 256, 0, s>>>(x, T, d, (double)eps, out);
+    return check_launch();
 }
 
 int launch_combine(const void* y_perm, int y_dtype, const int32_t* dest, const float* gates, const float* y_shared,

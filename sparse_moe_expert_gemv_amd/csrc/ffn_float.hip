@@ -223,6 +223,7 @@ __global__ __launch_bounds__(256) void ffn_float_gateup(const XT* __restrict__ x
         const int strip = item % n_strips;
         const SlotInfo S = slot_info(item / n_strips, n_active, active, expert_ptrs, shared_blob, counts, offsets,
                                      T, k);
+        if (S.blob == nullptr) continue;  // no weights behind this expert: leave its rows untouched
         const size_t tile0 = (size_t)strip * nkt;
         for (int m0 = 0; m0 < S.c; m0 += 16) {
             const int nrow = min(16, S.c - m0);
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(256) void ffn_float_down(const _Float16* __restrict
         const int grp = item % n_groups;
         const SlotInfo S = slot_info(item / n_groups, n_active, active, expert_ptrs, shared_blob, counts, offsets,
                                      T, k);
+        if (S.blob == nullptr) continue;  // no weights behind this expert: leave its rows untouched
         const int strip = grp * 4 + wave;
         const size_t tile0 = (size_t)strip * nkt;
         for (int m0 = 0; m0 < S.c; m0 += 16) {

@@ -182,6 +182,7 @@ __global__ __launch_bounds__(256) void ffn_q8_gateup(const int8_t* __restrict__ 
         const int fg = item % n_fg;
         const bool routed = tl.x < E;
         const uint8_t* blob = routed ? (const uint8_t*)expert_ptrs[tl.x] : shared_blob;
+        if (blob == nullptr) continue;  // no weights behind this expert (uniform per workgroup)
         const int c = routed ? counts[tl.x] : T;
         const int p0 = routed ? offsets[tl.x] : T * k;  // first h row of the slot
         const int m0 = tl.y;
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(256) void ffn_q8_down(const int8_t* __restrict__ hq
         const int og = item % n_og;
         const bool routed = tl.x < E;
         const uint8_t* blob = routed ? (const uint8_t*)expert_ptrs[tl.x] : shared_blob;
+        if (blob == nullptr) continue;  // no weights behind this expert (uniform per workgroup)
         const int c = routed ? counts[tl.x] : T;
         const int p0 = routed ? offsets[tl.x] : T * k;
         const int m0 = tl.y;

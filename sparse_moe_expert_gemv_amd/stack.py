@@ -1,0 +1,182 @@
+"""Multi-layer MoE stack with an HBM expert slot pool and per-layer miss staging.
+
+The Strata pages keep the most-used ~4,500 experts resident in GPU memory,
+chosen by a prebuilt usage ranking ("How Strata works", adaptive expert cache
+section), and stream the next layer's experts over PCIe while the current
+layer computes ("Strata benchmarks", prefill optimisation table).  Here:
+
+* a caller-chosen set of global expert ids (layer * E + e) occupies the slots
+  of a device pool (``moe_cache_set_resident``);
+* every other expert of a layer is copied from pinned host memory into one of
+  two device staging buffers on a side stream (``moe_cache_stage``), which also
+  rewrites that layer's device pointer table; layer l + 2 is staged into the
+  buffer of layer l as soon as layer l has finished;
+* the compute stream waits for layer l's staging event, then runs
+  rmsnorm -> route -> permute -> quantise -> expert FFN (through the pointer
+  table) -> combine with the residual: h_{l+1} = h_l + MoE_l(norm(h_l)).  The
+  pages leave the block around the MoE layer open; without the pre-norm a
+  stack of random-weight layers joined by a residual add diverges within a
+  few layers.
+
+All device memory comes from PyTorch; all computation is in libmoe.so.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .layer import pack_blobs
+
+
+class ExpertStack:
+    def __init__(self, routers, shared_blobs, host_store: torch.Tensor, host_index: np.ndarray, resident_ids,
+                 *, d, f, k, wfmt, act_mode, max_T, staging_slots=None, device="cuda", eps=1e-6):
+        """
+        routers      list of L fp32 arrays [E, d]
+        shared_blobs [L, bytes] canonical uint8 (numpy) or None
+        host_store   pinned host uint8 tensor [n_blobs, bytes] of PACKED expert blobs
+        host_index   int array [L, E]: row of host_store holding expert (l, e)
+        resident_ids global ids (l * E + e) kept in the slot pool
+        """
+        self.device = torch.device(device)
+        self.d, self.f, self.k, self.wfmt, self.act_mode = d, f, k, wfmt, act_mode
+        self.eps = eps
+        self.L = len(routers)
+        self.E = routers[0].shape[0]
+        self.eb = B.moe_expert_bytes(wfmt, d, f)
+        assert host_store.is_pinned() and host_store.shape[1] == self.eb
+        self.host_store = host_store
+        self.host_index = np.asarray(host_index, dtype=np.int64)
+        base = host_store.data_ptr()
+        self.host_ptrs = [[base + int(self.host_index[l, e]) * self.eb for e in range(self.E)] for l in range(self.L)]
+        self.Wr = [torch.as_tensor(np.ascontiguousarray(w, np.float32)).to(self.device) for w in routers]
+        self.shared = None
+        if shared_blobs is not None:
+            sh = torch.from_numpy(np.ascontiguousarray(shared_blobs, dtype=np.uint8)).to(self.device)
+            self.shared = pack_blobs(sh, wfmt, d, f)
+        resident_ids = [int(g) for g in resident_ids]
+        self.n_slots = len(resident_ids)
+        self.pool = torch.empty((max(self.n_slots, 1), self.eb), dtype=torch.uint8, device=self.device)
+        res_per_layer = np.bincount(np.asarray(resident_ids, dtype=np.int64) // self.E, minlength=self.L)
+        need = int(self.E - res_per_layer.min()) if self.n_slots else self.E
+        self.staging_slots = need if staging_slots is None else staging_slots
+        self.staging = torch.empty((2, max(self.staging_slots, 1), self.eb), dtype=torch.uint8, device=self.device)
+        self.tables = torch.zeros((self.L, self.E), dtype=torch.int64, device=self.device)
+        self.cache = B.SlotCache(self.L, self.E, self.n_slots, self.eb, self.pool, self.staging, 2,
+                                 self.staging_slots)
+        self.cache.set_resident(resident_ids, [self.host_ptrs[g // self.E][g % self.E] for g in resident_ids])
+        torch.cuda.synchronize()
+        self.side = torch.cuda.Stream(device=self.device)
+        self.staged = [torch.cuda.Event() for _ in range(self.L)]
+        self.done = [torch.cuda.Event() for _ in range(self.L)]
+        self._alloc(max_T)
+
+    def _alloc(self, T):
+        dev, d, f, E, k = self.device, self.d, self.f, self.E, self.k
+        self.max_T = T
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.ids = torch.empty((T, k), **i32)
+        self.gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.sorted_idx = torch.empty(T * k, **i32)
+        self.dest = torch.empty(T * k, **i32)
+        self.active = torch.empty(E + 1, **i32)
+        self.xq = torch.empty((T, d), dtype=torch.int8, device=dev)
+        self.sx = torch.empty((T, d // 32), dtype=torch.float32, device=dev)
+        ydt = torch.float16 if self.act_mode == B.MOE_ACT_Q8 else torch.float32
+        self.y_perm = torch.empty((T * k, d), dtype=ydt, device=dev)
+        self.y_shared = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.hbuf = [torch.empty((T, d), dtype=torch.float32, device=dev) for _ in range(2)]
+        self.xn = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(B.moe_workspace_size(T, d, f, E, k, self.act_mode), dtype=torch.uint8, device=dev)
+
+    def misses(self, layer):
+        return self.cache.lookup(layer)[1]
+
+    def stage(self, layer):
+        """Enqueue the staging of one layer on the side stream (records staged[layer])."""
+        self.cache.stage(layer, layer % 2, self.host_ptrs[layer], self.tables[layer], stream=self.side,
+                         done_event=self.staged[layer])
+
+    def layer(self, l, h, out, stream=None, table=None):
+        """out = h + MoE_l(rmsnorm(h)); the normalised input stays in self.xn."""
+        T = h.shape[0]
+        k, E, n = self.k, self.E, h.shape[0] * self.k
+        xn = self.xn[:T]
+        B.moe_rmsnorm(h, xn, self.eps, stream)
+        B.moe_route_permute(xn, self.Wr[l], None, k, self.ids[:T], self.gates[:T], self.counts, self.offsets,
+                            self.sorted_idx[:n], self.dest[:n], self.active, self.ws, stream)
+        common = dict(T=T, d=self.d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
+                      expert_ptrs=self.tables[l] if table is None else table, counts=self.counts,
+                      offsets=self.offsets, sorted_idx=self.sorted_idx[:n], active=self.active,
+                      y_perm=self.y_perm[:n], ws=self.ws,
+                      shared_blob=None if self.shared is None else self.shared[l],
+                      y_shared=None if self.shared is None else self.y_shared[:T], stream=stream)
+        if self.act_mode == B.MOE_ACT_Q8:
+            B.moe_quantize_act(xn, self.xq[:T], self.sx[:T], stream)
+            B.moe_expert_ffn(xq=self.xq[:T], sx=self.sx[:T], **common)
+        else:
+            B.moe_expert_ffn(x=xn, **common)
+        B.moe_combine(self.y_perm[:n], self.dest[:n], self.gates[:T],
+                      None if self.shared is None else self.y_shared[:T], h, out, stream)
+
+    def forward(self, x: torch.Tensor, keep=(), copy_only=False, compute_only_tables=None):
+        """Run all layers on x ([T, d] fp32).  Returns (h_L, {l: (h_l, norm(h_l)) for l in keep}).
+
+        copy_only: only the staging (timing aid); compute_only_tables: run the
+        compute with these pointer tables [L, E] instead of staging (timing aid).
+        """
+        T = x.shape[0]
+        if T > self.max_T:
+            self._alloc(T)
+        comp = torch.cuda.current_stream(self.device)
+        kept = {}
+        h = x
+        outs = self.hbuf
+        if compute_only_tables is None:
+            self.side.wait_stream(comp)
+            for l in range(min(2, self.L)):
+                self.stage(l)
+        for l in range(self.L):
+            if compute_only_tables is None:
+                comp.wait_event(self.staged[l])
+            out = outs[l % 2]
+            if not copy_only:
+                self.layer(l, h, out, table=None if compute_only_tables is None else compute_only_tables[l])
+                if l in keep:
+                    kept[l] = (h.clone(), self.xn[:T].clone())
+                h = out
+            self.done[l].record(comp)
+            if compute_only_tables is None and l + 2 < self.L:
+                self.side.wait_event(self.done[l])
+                self.stage(l + 2)
+        return h, kept
+
+    def close(self):
+        self.cache.close()
+
+
+def build_host_store(pool_canonical: np.ndarray, wfmt: int, d: int, f: int, device="cuda") -> torch.Tensor:
+    """Pack canonical blobs on the device and return them in pinned host memory."""
+    n, nb = pool_canonical.shape
+    store = torch.empty((n, nb), dtype=torch.uint8, pin_memory=True)
+    step = 256
+    for i in range(0, n, step):
+        j = min(n, i + step)
+        dev = torch.from_numpy(np.ascontiguousarray(pool_canonical[i:j])).to(device)
+        store[i:j].copy_(pack_blobs(dev, wfmt, d, f).cpu())
+    torch.cuda.synchronize()
+    return store
+
+
+def time_pass(fn, reps=1):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps

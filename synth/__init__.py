@@ -250,3 +250,41 @@ def stack_blob_map(seed: int, n_layers: int, E: int, n_blobs: int):
 def stack_pool(seed: int, cfg: LayerConfig, out: np.ndarray | None = None) -> np.ndarray:
     """The distinct expert blobs backing the layer stack, [n_pool_blobs, expert_bytes]."""
     return gen_expert_blobs(seed, cfg.cfg_id, 0, _T_POOL, cfg.n_pool_blobs, cfg.d, cfg.f, cfg.wfmt, out=out)
+
+
+@dataclass
+class Stack:
+    cfg: LayerConfig
+    x: np.ndarray            # [T, d] layer-0 input (bf16 bits)
+    routers: list            # L arrays [E, d] fp32
+    pool: np.ndarray         # [n_pool_blobs, expert_bytes] canonical blobs
+    index: np.ndarray        # [L, E] pool row of routed expert (l, e)
+    shared_index: np.ndarray  # [L] pool row of layer l's shared expert
+    resident: np.ndarray     # global ids (l * E + e) kept resident, best rank first
+
+    def expert_blob(self, layer: int, e: int) -> np.ndarray:
+        return self.pool[self.index[layer, e]]
+
+    def layer_experts(self, layer: int) -> np.ndarray:
+        return self.pool[self.index[layer]]
+
+    def shared_blobs(self) -> np.ndarray:
+        return self.pool[self.shared_index]
+
+
+def make_stack(seed: int = 0, name: str = "stack", overrides: dict | None = None, T: int | None = None) -> Stack:
+    """The layer stack: per-layer routers, a pool of distinct expert blobs that
+    back every (layer, expert) through a seeded map, and the resident set =
+    the n_resident best ranks of a seeded Zipf(1.1) usage profile."""
+    cfg = CONFIGS[name]
+    if overrides:
+        cfg = LayerConfig(**{**cfg.__dict__, **overrides})
+    if T is not None:
+        cfg = LayerConfig(**{**cfg.__dict__, "T": T})
+    x = gen_x(seed, cfg)
+    routers = [gen_router(seed, cfg, layer=l)[0] for l in range(cfg.n_layers)]
+    pool = gen_expert_blobs(seed, cfg.cfg_id, 0, _T_POOL, cfg.n_pool_blobs, cfg.d, cfg.f, cfg.wfmt)
+    index, shared_index = stack_blob_map(seed, cfg.n_layers, cfg.E, cfg.n_pool_blobs)
+    rank = stack_profile(seed, cfg.n_layers, cfg.E)
+    resident = np.argsort(rank, kind="stable")[:cfg.n_resident]
+    return Stack(cfg, x, routers, pool, index, shared_index, resident)

@@ -1,0 +1,169 @@
+"""GPU parity of the layer stack with the expert slot pool and miss staging.
+
+Each layer computes h_{l+1} = h_l + MoE_l(rmsnorm(h_l)).  It is checked
+teacher-forced: the oracle receives the GPU's fp32 residual h_l and normalised
+input rmsnorm(h_l) of that layer, computes the MoE layer on the canonical blobs
+of that layer's experts, and its ids/permutation must match bit for bit and its
+output within the float tolerance; the GPU norm itself is checked against the
+oracle's to fp32 rounding.  Staged (missed) experts and pool
+(resident) experts must give bit-identical results to a plain device copy of
+the same weights.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import refmath as R
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from sparse_moe_expert_gemv_amd import binding as B  # noqa: E402
+from sparse_moe_expert_gemv_amd.layer import pack_blobs, pointer_table  # noqa: E402
+from sparse_moe_expert_gemv_amd.stack import ExpertStack, build_host_store  # noqa: E402
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    oracle.build(force=False)
+
+
+def _stack_gpu(S):
+    c = S.cfg
+    store = build_host_store(S.pool, c.wfmt, c.d, c.f)
+    mode = B.MOE_ACT_Q8 if c.act_mode == "q8" else B.MOE_ACT_FLOAT
+    return ExpertStack(S.routers, S.shared_blobs() if c.has_shared else None, store, S.index, S.resident,
+                       d=c.d, f=c.f, k=c.k, wfmt=c.wfmt, act_mode=mode, max_T=c.T)
+
+
+def _x0(S):
+    return torch.from_numpy(synth.bf16_bits_to_f32(S.x)).to(DEV)
+
+
+def _check_layer(S, l, h_in, xn_in, tokens=None):
+    c = S.cfg
+    om = oracle.ACT_Q8 if c.act_mode == "q8" else oracle.ACT_FLOAT
+    ref_norm = oracle.rmsnorm(h_in, 1e-6)
+    assert np.max(np.abs(xn_in - ref_norm)) <= 1e-6 * (1 + np.max(np.abs(ref_norm)))
+    o = oracle.moe_layer(xn_in, S.routers[l], None, S.layer_experts(l),
+                         S.shared_blobs()[l] if c.has_shared else None, c.wfmt, c.f, c.k, act_mode=om,
+                         residual=h_in, tokens=tokens)
+    return o
+
+
+SMALL = dict(T=300, d=256, E=64, k=4, f=128, wfmt=synth.WFMT_I8B32, has_shared=True, act_mode="q8", n_layers=4,
+             n_resident=100, n_pool_blobs=40)
+
+
+def test_small_stack_teacher_forced_and_pool_vs_staging_bitexact():
+    S = synth.make_stack(overrides=SMALL)
+    G = _stack_gpu(S)
+    x = _x0(S)
+    hL, kept = G.forward(x, keep=range(S.cfg.n_layers))
+    torch.cuda.synchronize()
+    hs = [kept[l][0].cpu().numpy() for l in range(S.cfg.n_layers)] + [hL.cpu().numpy()]
+    xns = [kept[l][1].cpu().numpy() for l in range(S.cfg.n_layers)]
+    for l in range(S.cfg.n_layers):
+        hit, miss = G.cache.lookup(l)
+        assert sorted(hit + miss) == list(range(S.cfg.E))
+        resident_l = sorted(int(g) % S.cfg.E for g in S.resident if int(g) // S.cfg.E == l)
+        assert hit == resident_l
+        o = _check_layer(S, l, hs[l], xns[l])
+        # routing of this layer as the GPU computed it, from the layer's own run
+        ok, rel, mx = R.within_tolerance(hs[l + 1], o["out"])
+        assert ok, "layer %d: rel %.3e max %.3e" % (l, rel, mx)
+    # the last layer through a plain contiguous copy of its experts: bit-identical
+    l = S.cfg.n_layers - 1
+    c = S.cfg
+    plain = pack_blobs(torch.from_numpy(S.layer_experts(l)).to(DEV), c.wfmt, c.d, c.f)
+    table = pointer_table(plain)
+    out_a = torch.empty_like(x)
+    out_b = torch.empty_like(x)
+    h_in = torch.from_numpy(hs[l]).to(DEV)
+    G.layer(l, h_in, out_a)  # through the cache's table (last staged state of layer l)
+    G.layer(l, h_in, out_b, table=table)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    assert np.array_equal(out_a.cpu().numpy(), hs[l + 1])
+    G.close()
+
+
+def test_small_stack_ids_and_permutation_bitexact_per_layer():
+    S = synth.make_stack(overrides=SMALL)
+    G = _stack_gpu(S)
+    x = _x0(S)
+    h = x
+    out = torch.empty_like(x)
+    for l in range(S.cfg.n_layers):
+        G.stage(l)
+        torch.cuda.current_stream().wait_event(G.staged[l])
+        G.layer(l, h, out)
+        torch.cuda.synchronize()
+        T = S.cfg.T
+        h_np = h.cpu().numpy()
+        o = _check_layer(S, l, h_np, G.xn[:T].cpu().numpy())
+        assert np.array_equal(G.ids[:T].cpu().numpy(), o["ids"])
+        assert np.array_equal(G.counts.cpu().numpy(), o["counts"])
+        assert np.array_equal(G.sorted_idx[:T * S.cfg.k].cpu().numpy(), o["sorted_idx"])
+        assert np.array_equal(G.dest[:T * S.cfg.k].cpu().numpy(), o["dest"])
+        h, out = out, h
+    G.close()
+
+
+def test_cache_capacity_error_when_staging_too_small():
+    S = synth.make_stack(overrides=SMALL)
+    c = S.cfg
+    store = build_host_store(S.pool, c.wfmt, c.d, c.f)
+    G = ExpertStack(S.routers, None, store, S.index, S.resident, d=c.d, f=c.f, k=c.k, wfmt=c.wfmt,
+                    act_mode=B.MOE_ACT_Q8, max_T=c.T, staging_slots=8)
+    with pytest.raises(B.MoeError) as ei:
+        G.stage(0)
+    assert ei.value.status == B.MOE_ERR_CACHE_CAPACITY
+    G.close()
+
+
+def test_full_stack_48_layers_sampled():
+    """The 48-layer, 24,576-expert stack at T=8192 with 4,500 resident slots:
+    teacher-forced ids/permutation on every token and outputs on 24 sampled
+    tokens for the first, a middle and the last layer."""
+    S = synth.make_stack()
+    c = S.cfg
+    assert c.n_layers * c.E == 24576 and len(S.resident) == 4500
+    G = _stack_gpu(S)
+    x = _x0(S)
+    check = [0, 23, 47]
+    hL, kept = G.forward(x, keep=check)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(21))
+    tokens = np.sort(rng.choice(c.T, 24, replace=False)).astype(np.int32)
+    for l in check:
+        h_in = kept[l][0].cpu().numpy()
+        # recompute layer l from its recorded input; its staging buffer has been
+        # reused by later layers, so stage it again first
+        G.stage(l)
+        torch.cuda.current_stream().wait_event(G.staged[l])
+        out = torch.empty_like(x)
+        G.layer(l, kept[l][0], out)
+        torch.cuda.synchronize()
+        h_out = out.cpu().numpy()
+        ids_gpu = G.ids[:c.T].cpu().numpy()
+        perm_gpu = G.sorted_idx[:c.T * c.k].cpu().numpy()
+        xn = G.xn[:c.T].cpu().numpy()
+        assert np.array_equal(xn, kept[l][1].cpu().numpy())
+        assert np.all(np.isfinite(h_out))
+        o = _check_layer(S, l, h_in, xn, tokens=tokens)
+        assert np.array_equal(ids_gpu, o["ids"])
+        assert np.array_equal(perm_gpu, o["sorted_idx"])
+        ok, rel, mx = R.within_tolerance(h_out[tokens], o["out"])
+        assert ok, "layer %d: rel %.3e max %.3e" % (l, rel, mx)
+    # the pass itself produced the same final output as the recomputed last layer
+    assert np.array_equal(hL.cpu().numpy(), h_out)
+    hit, miss = G.cache.lookup(0)
+    assert len(hit) + len(miss) == c.E
+    G.close()

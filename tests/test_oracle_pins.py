@@ -353,3 +353,21 @@ def test_layer_token_subset_matches_full():
     sub = [31, 0, 7]
     part = oracle.moe_layer(x, L.Wr, None, L.experts, L.shared, L.cfg.wfmt, L.cfg.f, L.cfg.k, tokens=sub)
     assert np.array_equal(part["out"], full["out"][sub])
+
+
+def test_rmsnorm_closed_forms():
+    """Constant row c: output is c / sqrt(c^2 + eps); output rows have mean
+    square 1 up to eps; scale invariance; zero row stays zero (catches a
+    missing square root, mean over the wrong axis, eps outside the root)."""
+    d = 64
+    x = np.zeros((4, d), np.float32)
+    x[0] = 3.0
+    x[1] = np.arange(d, dtype=np.float32) - 20
+    x[2] = 1e3 * x[1]
+    out = oracle.rmsnorm(x, eps=1e-6)
+    assert abs(out[0, 0] - 3.0 / math.sqrt(9.0 + 1e-6)) < 1e-7
+    ms = (x[1].astype(np.float64) ** 2).mean()
+    assert np.allclose(out[1], x[1] / math.sqrt(ms + 1e-6), rtol=1e-7)
+    assert abs((out[1].astype(np.float64) ** 2).mean() - ms / (ms + 1e-6)) < 1e-6
+    assert np.allclose(out[2], out[1], rtol=1e-6)
+    assert np.all(out[3] == 0.0)
