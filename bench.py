@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA, TOPS
-WORKLOADS = ("decode_t4", "decode_t1", "prefill", "skew", "tiny", "stack")
+WORKLOADS = ("decode_t4", "decode_t1", "prefill", "skew", "tiny", "stack", "copy")
 
 
 def parse():
@@ -50,6 +50,25 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=0)
     return p.parse_args()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, if one exists for this workload and the
+    kernel source has not changed since the counters were taken; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "ffn_float_gateup_%s_hbm_counters.md" % workload)
+    src = os.path.join(ROOT, "sparse_moe_expert_gemv_amd", "csrc", "ffn_float.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            key, val = line.split(":", 1)
+            fields[key] = val.strip()
+    if fields.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in fields else None
 
 
 def gateup_algorithmic(cfg, n_active: int, T: int):
@@ -91,6 +110,8 @@ def main():
     name = a.workload
     if name == "stack":
         return bench_stack(a)
+    if name == "copy":
+        return bench_copy(a)
     big = name == "prefill"
     steps = a.steps if a.steps is not None else (20 if big else 200)
     warmup = a.warmup if a.warmup is not None else (3 if big else 20)
@@ -216,7 +237,7 @@ def main():
     else:
         achieved = alg_bytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name)}
     roof["kernel"] = "ffn_%s_gateup (moe_expert_ffn phase 1)" % ("q8" if mode == B.MOE_ACT_Q8 else "float")
     roof["kernel_ms"] = round(gu_ms, 5)
     roof["algorithmic_bytes_per_launch"] = int(alg_bytes)
@@ -303,6 +324,25 @@ def bench_stack(a):
     }
     G.close()
     print(json.dumps(line), flush=True)
+
+
+def bench_copy(a):
+    """Calibration aid for HBM byte counters: a plain device-to-device copy of
+    exactly 1 GiB (reads 1 GiB, writes 1 GiB), repeated --steps times."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    steps = a.steps if a.steps is not None else 5
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"workload": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "ms_per_copy": round(dt * 1e3, 3), "GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}),
+          flush=True)
 
 
 def time_it(fn, reps=1):
