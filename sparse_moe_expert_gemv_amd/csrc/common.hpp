@@ -73,6 +73,15 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int16v __attribute__((ext_vector_type(16)));
 typedef unsigned uint4v __attribute__((ext_vector_type(4)));
+typedef unsigned uint2v __attribute__((ext_vector_type(2)));
+
+// Load through a global-address-space pointer.  Pointers read from memory
+// (expert blob tables) are generic; without the cast the compiler emits flat
+// loads, which also count against the LDS counter and force extra waits.
+template <typename V>
+__device__ __forceinline__ V gload(const V* p) {
+    return *(const __attribute__((address_space(1))) V*)p;
+}
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 

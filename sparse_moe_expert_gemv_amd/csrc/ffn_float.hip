@@ -332,6 +332,186 @@ __global__ __launch_bounds__(256) void ffn_float_down(const _Float16* __restrict
     }
 }
 
+// ---- small batches, int4 weights: token-dense gate/up ------------------------
+// For T <= 16 every token is a row of the MFMA A operand (rows >= T repeat the
+// last token and are discarded), so a work item needs no gather and the token
+// tile is staged once per workgroup.  Work item = (slot, 16-row strip of f);
+// two wavefronts split its reduction (NT tiles each) and software-pipeline
+// their quant tiles two ahead, so that loads of later tiles overlap the
+// products of earlier ones.  Each block of 8 weights becomes (q - 8) * s in
+// fp16 with one rounding: the low nibbles of a byte through the 0x6400 magic
+// (1024 + q), the high nibbles in place (1024 + 16 q) rescaled by an exact
+// fma, then one multiply by the block scale; the MFMA then accumulates the
+// scaled products of all blocks in fp32.
+
+// (q - 8) * s for the 8 nibbles of one int4 dword ([k0 k2 k4 k6 k1 k3 k5 k7])
+__device__ __forceinline__ half8 dequant4_scaled(uint32_t v, half2v s2, uint32_t mlo, uint32_t mhi,
+                                                 uint32_t magic) {
+    const half2v m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half2v r16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2v m72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t v8 = v >> 8;
+    const half2v p0 = as_h2((v & mlo) | magic) + m1032;                               // k0, k1
+    const half2v p1 = __builtin_elementwise_fma(as_h2((v & mhi) | magic), r16, m72);  // k2, k3
+    const half2v p2 = as_h2((v8 & mlo) | magic) + m1032;                              // k4, k5
+    const half2v p3 = __builtin_elementwise_fma(as_h2((v8 & mhi) | magic), r16, m72); // k6, k7
+    const half2v q0 = p0 * s2, q1 = p1 * s2, q2 = p2 * s2, q3 = p3 * s2;
+    return half8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+}
+
+// fp16 scale of block b (of 4) of an int4 tile row, broadcast to both halves
+__device__ __forceinline__ half2v scale_pair(const uint2v& raw, int b) {
+    const uint32_t w = b < 2 ? raw[0] : raw[1];
+    const uint32_t hb = (b & 1) ? (w >> 16) : (w & 0xFFFFu);
+    return as_h2(hb | (hb << 16));
+}
+
+constexpr int kTokMax = 16;   // tokens of the token-dense kernels
+constexpr int kPipe = 2;      // quant tiles in flight ahead of the products
+
+template <int NT, typename XT>
+__global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x, int T, int d, int f, int k,
+                                                        const void* const* __restrict__ expert_ptrs,
+                                                        const uint8_t* __restrict__ shared_blob,
+                                                        const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ sorted_idx,
+                                                        const int32_t* __restrict__ active, _Float16* __restrict__ h) {
+    extern __shared__ __align__(16) uint4 xs4[];  // [T][d / 8] fp16, chunk c of row r at (c ^ r); later [4][2][4][64] f32
+    const int XC = d / 8;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int part = wave & 1;
+    const int n_strips = f / 16;
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 2 + (wave >> 1));
+    const int n_active = active[0];
+    const int n_slots = n_active + (shared_blob ? 1 : 0);
+    const int a = item / n_strips, strip = item % n_strips;
+    const uint8_t* blob = nullptr;
+    int e = -1;
+    if (a < n_active) {
+        e = active[1 + a];
+        blob = (const uint8_t*)expert_ptrs[e];
+    } else if (a < n_slots) {
+        blob = shared_blob;
+    }
+    // tokens -> LDS as fp16, four 8-element chunks per thread per round
+    const int nx = T * XC;
+    for (int base = 0; base < nx; base += 4 * 256) {
+        half8 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = min(base + (int)threadIdx.x + j * 256, nx - 1);
+            v[j] = load8_h(x + (size_t)idx * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = base + (int)threadIdx.x + j * 256;
+            if (idx < nx) {
+                const int r = idx / XC, c = idx % XC;
+                xs4[r * XC + (c ^ r)] = __builtin_bit_cast(uint4, v[j]);
+            }
+        }
+    }
+    __syncthreads();
+    const bool work = blob != nullptr;  // no weights behind this expert: leave its rows untouched
+    float4v accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+    if (work) {
+        const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
+        const size_t tile0 = (size_t)strip * (2 * NT) + part * NT;
+        const uint4v* pg = reinterpret_cast<const uint4v*>(blob + L.g.qoff + tile0 * 1024) + lane;
+        const uint4v* pu = reinterpret_cast<const uint4v*>(blob + L.u.qoff + tile0 * 1024) + lane;
+        const uint2v* psg = reinterpret_cast<const uint2v*>(blob + L.g.soff + tile0 * 128 + (lane & 15) * 8);
+        const uint2v* psu = reinterpret_cast<const uint2v*>(blob + L.u.soff + tile0 * 128 + (lane & 15) * 8);
+        uint4v qg[NT], qu[NT];
+        uint2v sg[NT], su[NT];
+#pragma unroll
+        for (int i = 0; i < kPipe && i < NT; ++i) {
+            sg[i] = gload(psg + i * 16);
+            su[i] = gload(psu + i * 16);
+            qg[i] = gload(pg + i * 64);
+            qu[i] = gload(pu + i * 64);
+        }
+        const int rr = min(lane & 15, T - 1);
+        // bit masks and magic in registers so that each extraction is one v_and_or_b32
+        uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+        asm volatile("" : "+s"(mlo), "+s"(mhi), "+v"(magic));
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            if (i + kPipe < NT) {
+                sg[i + kPipe] = gload(psg + (i + kPipe) * 16);
+                su[i + kPipe] = gload(psu + (i + kPipe) * 16);
+                qg[i + kPipe] = gload(pg + (i + kPipe) * 64);
+                qu[i + kPipe] = gload(pu + (i + kPipe) * 64);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const half8 Bg = dequant4_scaled(qg[i][b], scale_pair(sg[i], b), mlo, mhi, magic);
+                const half8 Bu = dequant4_scaled(qu[i][b], scale_pair(su[i], b), mlo, mhi, magic);
+                const int kk = ((part * NT + i) * 4 + b) * 32 + 8 * (lane >> 4);
+                const half8 A = __builtin_bit_cast(half8, xs4[rr * XC + ((kk >> 3) ^ rr)]);
+                accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bg, accg, 0, 0, 0);
+                accu = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bu, accu, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the two halves of the reduction meet in LDS (the token tile is no longer read)
+    __syncthreads();
+    float(*red)[2][4][64] = reinterpret_cast<float(*)[2][4][64]>(xs4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        red[wave][0][r][lane] = accg[r];
+        red[wave][1][r][lane] = accu[r];
+    }
+    __syncthreads();
+    if (!work) return;
+    const int w0 = wave & ~1;
+    int c = T, p0 = T * k;
+    if (e >= 0) {
+        c = counts[e];
+        p0 = offsets[e];
+    }
+    // accumulator row r holds token 4 * (lane / 16) + r; wavefront `part` writes rows r = part, part + 2
+#pragma unroll
+    for (int r = part; r < 4; r += 2) {
+        const int t = 4 * (lane >> 4) + r;
+        if (t >= T) continue;
+        int p = -1;
+        if (e < 0) {
+            p = p0 + t;
+        } else {
+            for (int m = 0; m < c; ++m)
+                if (sorted_idx[p0 + m] / k == t) p = p0 + m;
+        }
+        if (p < 0) continue;  // token t is not routed to this expert
+        const float g = red[w0][0][r][lane] + red[w0 + 1][0][r][lane];
+        const float u = red[w0][1][r][lane] + red[w0 + 1][1][r][lane];
+        h[(size_t)p * f + strip * 16 + (lane & 15)] = (_Float16)(silu_f(g) * u);
+    }
+}
+
+template <typename XT>
+static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, hipStream_t s) {
+    const int nkt = a->d / 128;
+    const int items = slots * (a->f / 16);
+    const dim3 grid((items + 1) / 2);
+    const size_t lds = std::max<size_t>((size_t)a->T * a->d * sizeof(_Float16), 4 * 2 * 4 * 64 * sizeof(float));
+#define MOE_GU16(NT)                                                                                           \
+    ffn_gateup_tok16<NT, XT><<<grid, 256, lds, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs,   \
+                                                    (const uint8_t*)a->shared_blob, a->counts, a->offsets,      \
+                                                    a->sorted_idx, a->active, h)
+    switch (nkt) {
+    case 4: MOE_GU16(2); return true;
+    case 8: MOE_GU16(4); return true;
+    case 16: MOE_GU16(8); return true;
+    case 32: MOE_GU16(16); return true;
+    default: return false;
+    }
+#undef MOE_GU16
+}
+
 size_t float_h_bytes(int T, int f, int k) { return ((size_t)T * k + T) * (size_t)f * sizeof(_Float16); }
 
 template <int WFMT, typename XT>
@@ -345,9 +525,12 @@ static int run_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     const int g1 = (int)std::min<long>((long)slots * (a->f / 16), (long)n_cu * 64);
     const size_t lds1 = std::max<size_t>((size_t)rows_lds * a->d * sizeof(_Float16), 4 * 2 * 4 * 64 * sizeof(float));
     if (a->phase != 2) {
-        ffn_float_gateup<WFMT, XT><<<g1, 256, lds1, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs,
-                                                         (const uint8_t*)a->shared_blob, a->counts, a->offsets,
-                                                         a->sorted_idx, a->active, h);
+        // token-dense kernel for small int4 batches; the token tile of d fp16 values per token fits in LDS
+        const bool tok16 = WFMT == MOE_WFMT_I4B32 && a->T <= kTokMax && (size_t)a->T * a->d * 2 <= 64 * 1024;
+        if (!(tok16 && launch_gateup_tok16<XT>(a, h, slots, s)))
+            ffn_float_gateup<WFMT, XT><<<g1, 256, lds1, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs,
+                                                             (const uint8_t*)a->shared_blob, a->counts, a->offsets,
+                                                             a->sorted_idx, a->active, h);
         const int rc = check_launch();
         if (rc || a->phase == 1) return rc;
     }
