@@ -473,22 +473,21 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
         c = counts[e];
         p0 = offsets[e];
     }
-    // accumulator row r holds token 4 * (lane / 16) + r; wavefront `part` writes rows r = part, part + 2
+    // accumulator row r holds token 4 * (lane / 16) + r; wavefront `part` writes rows r = part, part + 2,
+    // to every position of the slot that token t occupies (a token listed twice gets two rows)
 #pragma unroll
     for (int r = part; r < 4; r += 2) {
         const int t = 4 * (lane >> 4) + r;
         if (t >= T) continue;
-        int p = -1;
-        if (e < 0) {
-            p = p0 + t;
-        } else {
-            for (int m = 0; m < c; ++m)
-                if (sorted_idx[p0 + m] / k == t) p = p0 + m;
-        }
-        if (p < 0) continue;  // token t is not routed to this expert
         const float g = red[w0][0][r][lane] + red[w0 + 1][0][r][lane];
         const float u = red[w0][1][r][lane] + red[w0 + 1][1][r][lane];
-        h[(size_t)p * f + strip * 16 + (lane & 15)] = (_Float16)(silu_f(g) * u);
+        const _Float16 hv = (_Float16)(silu_f(g) * u);
+        if (e < 0) {
+            h[(size_t)(p0 + t) * f + strip * 16 + (lane & 15)] = hv;
+        } else {
+            for (int m = 0; m < c; ++m)
+                if (sorted_idx[p0 + m] / k == t) h[(size_t)(p0 + m) * f + strip * 16 + (lane & 15)] = hv;
+        }
     }
 }
 
@@ -510,6 +509,136 @@ static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, h
     default: return false;
     }
 #undef MOE_GU16
+}
+
+// Down projection for small batches (int4): work item = (slot, 16 output
+// rows), one wavefront per item over the whole reduction, four items of one
+// slot per workgroup sharing the slot's h rows staged in LDS (16 rows at a
+// time); the first kPipe quant tiles are requested before the h rows, the
+// rest pipelined.
+template <int NKT, typename YT>
+__global__ __launch_bounds__(256) void ffn_down_tok16(const _Float16* __restrict__ h, int T, int d, int f, int k,
+                                                      const void* const* __restrict__ expert_ptrs,
+                                                      const uint8_t* __restrict__ shared_blob,
+                                                      const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ active, YT* __restrict__ y_perm,
+                                                      float* __restrict__ y_shared) {
+    extern __shared__ __align__(16) uint4 hs4[];  // [16][f / 8], chunk c of row r at (c ^ r)
+    const int HC = f / 8;
+    const int lane = threadIdx.x & 63;
+    const int n_strips = d / 16;  // a multiple of 4: the four items of a workgroup share one slot
+    const int item0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 4);
+    const int strip = (item0 % n_strips) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int a = item0 / n_strips;
+    const int n_active = active[0];
+    const uint8_t* blob = nullptr;
+    int c = 0, p0 = 0;
+    bool routed = false;
+    if (a < n_active) {
+        const int e = active[1 + a];
+        blob = (const uint8_t*)expert_ptrs[e];
+        c = counts[e];
+        p0 = offsets[e];
+        routed = true;
+    } else if (a == n_active && shared_blob) {
+        blob = shared_blob;
+        c = T;
+        p0 = T * k;
+    }
+    if (blob == nullptr || c == 0) return;  // uniform over the workgroup
+    const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
+    const size_t tile0 = (size_t)strip * NKT;
+    const uint4v* pq = reinterpret_cast<const uint4v*>(blob + L.dn.qoff + tile0 * 1024) + lane;
+    const uint2v* ps = reinterpret_cast<const uint2v*>(blob + L.dn.soff + tile0 * 128 + (lane & 15) * 8);
+    uint4v q[NKT];
+    uint2v sc[NKT];
+#pragma unroll
+    for (int i = 0; i < kPipe && i < NKT; ++i) {
+        sc[i] = gload(ps + i * 16);
+        q[i] = gload(pq + i * 64);
+    }
+    const int rr0 = lane & 15;
+    uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+    asm volatile("" : "+s"(mlo), "+s"(mhi), "+v"(magic));
+    const int o = strip * 16 + (lane & 15);
+    // rows of the slot in tiles of 16 (more than one tile only when a token lists an expert twice)
+    for (int m0 = 0; m0 < c; m0 += 16) {
+        const int nr = min(16, c - m0);
+        if (m0 > 0) {
+            __syncthreads();  // the previous tile's rows are no longer read
+#pragma unroll
+            for (int i = 0; i < kPipe && i < NKT; ++i) {
+                sc[i] = gload(ps + i * 16);
+                q[i] = gload(pq + i * 64);
+            }
+        }
+        // the tile's h rows -> LDS, two 16-byte chunks per thread per round
+        const int nh = nr * HC;
+        for (int base = 0; base < nh; base += 512) {
+            uint4v v[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int idx = min(base + (int)threadIdx.x + j * 256, nh - 1);
+                v[j] = gload(reinterpret_cast<const uint4v*>(h + (size_t)(p0 + m0 + idx / HC) * f) + idx % HC);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int idx = base + (int)threadIdx.x + j * 256;
+                if (idx < nh) {
+                    const int r = idx / HC, cc = idx % HC;
+                    hs4[r * HC + (cc ^ r)] = __builtin_bit_cast(uint4, v[j]);
+                }
+            }
+        }
+        __syncthreads();
+        const int rr = min(rr0, nr - 1);
+        float4v acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) {
+            if (i + kPipe < NKT) {
+                sc[i + kPipe] = gload(ps + (i + kPipe) * 16);
+                q[i + kPipe] = gload(pq + (i + kPipe) * 64);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const half8 B = dequant4_scaled(q[i][b], scale_pair(sc[i], b), mlo, mhi, magic);
+                const int kk = (i * 4 + b) * 32 + 8 * (lane >> 4);
+                const half8 A = __builtin_bit_cast(half8, hs4[rr * HC + ((kk >> 3) ^ rr)]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * (lane >> 4) + r;
+            if (m >= nr) continue;
+            if (routed) y_perm[(size_t)(p0 + m0 + m) * d + o] = (YT)acc[r];
+            else y_shared[(size_t)(m0 + m) * d + o] = acc[r];
+        }
+    }
+}
+
+template <typename YT>
+static bool launch_down_tok16(const moe_ffn_args* a, const _Float16* h, int slots, hipStream_t s) {
+    if (a->d % 64) return false;
+    const dim3 grid(slots * (a->d / 64));
+    const size_t lds = (size_t)kTokMax * a->f * sizeof(_Float16);
+#define MOE_DN16(NKT)                                                                                            \
+    ffn_down_tok16<NKT, YT><<<grid, 256, lds, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,                    \
+                                                   (const uint8_t*)a->shared_blob, a->counts, a->offsets, a->active, \
+                                                   (YT*)a->y_perm, a->y_shared)
+    switch (a->f / 128) {
+    case 2: MOE_DN16(2); return true;
+    case 4: MOE_DN16(4); return true;
+    case 6: MOE_DN16(6); return true;
+    case 8: MOE_DN16(8); return true;
+    case 12: MOE_DN16(12); return true;
+    case 16: MOE_DN16(16); return true;
+    default: return false;
+    }
+#undef MOE_DN16
 }
 
 size_t float_h_bytes(int T, int f, int k) { return ((size_t)T * k + T) * (size_t)f * sizeof(_Float16); }
@@ -536,14 +665,19 @@ static int run_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     }
     const int g2 = (int)std::min<long>((long)slots * (a->d / 64), (long)n_cu * 64);
     const size_t lds2 = (size_t)rows_lds * a->f * sizeof(_Float16);
-    if (a->y_dtype == MOE_DT_F32)
-        ffn_float_down<WFMT, float><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
-                                                          (const uint8_t*)a->shared_blob, a->counts, a->offsets,
-                                                          a->active, (float*)a->y_perm, a->y_shared);
-    else
-        ffn_float_down<WFMT, _Float16><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
-                                                             (const uint8_t*)a->shared_blob, a->counts, a->offsets,
-                                                             a->active, (_Float16*)a->y_perm, a->y_shared);
+    // every slot has at most T <= 16 rows: one wavefront per 16 output rows
+    const bool tok16 = WFMT == MOE_WFMT_I4B32 && a->T <= kTokMax && (size_t)kTokMax * a->f * 2 <= 64 * 1024;
+    if (a->y_dtype == MOE_DT_F32) {
+        if (!(tok16 && launch_down_tok16<float>(a, h, slots, s)))
+            ffn_float_down<WFMT, float><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
+                                                              (const uint8_t*)a->shared_blob, a->counts, a->offsets,
+                                                              a->active, (float*)a->y_perm, a->y_shared);
+    } else {
+        if (!(tok16 && launch_down_tok16<_Float16>(a, h, slots, s)))
+            ffn_float_down<WFMT, _Float16><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
+                                                                 (const uint8_t*)a->shared_blob, a->counts, a->offsets,
+                                                                 a->active, (_Float16*)a->y_perm, a->y_shared);
+    }
     return check_launch();
 }
 
