@@ -35,7 +35,7 @@ void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* bas
     w->hist = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * std::max<size_t>(nch, 1) * E));
     w->permute_bytes = off;
     if (act_mode == MOE_ACT_Q8) {
-        w->tiles = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (2 * q8_tile_capacity(T, k, E) + 4)));
+        w->tiles = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (4 * q8_tile_capacity(T, k, E) + 4)));
         w->h = take(rows * (size_t)f);
         w->hs = reinterpret_cast<float*>(take(sizeof(float) * rows * (size_t)(f / 32)));
     } else {

@@ -327,11 +327,304 @@ __global__ __launch_bounds__(256) void ffn_q8_down(const int8_t* __restrict__ hq
     }
 }
 
+// ---- int4 weights: token tiles of up to 192 rows staged in LDS ---------------
+// A work item is (tile, 128 weight rows): gate/up takes 64 features of f (their
+// 64 gate rows and 64 up rows), down takes 128 output rows.  Every k-chunk of
+// 128 (one packed int4 tile per strip, four 32-blocks) stages the tile's int8
+// activation rows, the 128 weight rows (int4 -> int8) and both sets of block
+// scales in LDS; wavefront w multiplies m-tiles 3 (w / 2) .. +2 (32 tokens
+// each) by n-tiles (w & 1) and 2 + (w & 1) (gate and up rows of the same 32
+// features, or two halves of the output rows), so SwiGLU needs no exchange.
+// Work items of one tile share blockIdx % 8, i.e. one XCD and its L2, which
+// then serves the tile's activation rows to all of them.  The per-block
+// arithmetic (magic-seeded int32 MFMA, t = sw * P, acc += sa * t, blocks in
+// order) is the same as above, so the results are identical.
+constexpr int kTM = 6;     // m-tiles of 32 tokens per tile (192 rows)
+constexpr int kTKC = 128;  // k per chunk
+
+struct TileSmem {
+    uint4 a[kTM * 32][kTKC / 16];   // int8 rows, 16-byte chunk c of row r at (c ^ (r & 7))
+    uint4 w[128][kTKC / 16];        // int8 weight rows, same swizzle
+    float sa[kTKC / 32][kTM * 32];  // activation block scales
+    float sw[kTKC / 32][128];       // weight block scales
+};
+
+// Tiles of <= kTM * 32 rows, balanced per expert: (slot, m0, rows, 0) with
+// slot = position in the active list, or n_active for the shared expert.
+__global__ __launch_bounds__(1024) void q8_tile_plan(const int32_t* __restrict__ counts,
+                                                     const int32_t* __restrict__ active, int T, int has_shared,
+                                                     int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+    __shared__ int32_t sc[1024];
+    constexpr int cap = kTM * 32;
+    const int a = threadIdx.x;
+    const int n_active = active[0];
+    const int c = a < n_active ? counts[active[1 + a]] : 0;
+    const int nt = (c + cap - 1) / cap;
+    sc[a] = nt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int v = a >= off ? sc[a - off] : 0;
+        __syncthreads();
+        sc[a] += v;
+        __syncthreads();
+    }
+    const int start = sc[a] - nt;
+    if (nt > 0) {
+        const int per = ((c + nt - 1) / nt + 15) / 16 * 16;
+        for (int i = 0; i < nt; ++i) tiles[start + i] = make_int4(a, i * per, min(per, c - i * per), 0);
+    }
+    if (a == 1023) {
+        int total = sc[1023];
+        if (has_shared) {  // the shared expert: slot n_active, all T tokens
+            const int ns = (T + cap - 1) / cap;
+            const int per = ((T + ns - 1) / ns + 15) / 16 * 16;
+            for (int i = 0; i < ns; ++i) tiles[total + i] = make_int4(n_active, i * per, min(per, T - i * per), 0);
+            total += ns;
+        }
+        n_tiles[0] = total;
+    }
+}
+
+// 16 bytes of a packed int4 lane word (one 32-block per dword) -> signed int8, k order
+__device__ __forceinline__ void int4_word_to_i8(uint32_t v, uint32_t& w0, uint32_t& w1) {
+    const uint32_t lo = v & 0x0F0F0F0Fu;         // bytes: k0 k4 k1 k5
+    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;  // bytes: k2 k6 k3 k7
+    w0 = (lo & 0xFFu) | ((lo >> 8) & 0xFF00u) | ((hi & 0xFFu) << 16) | ((hi << 8) & 0xFF000000u);
+    w1 = ((lo >> 8) & 0xFFu) | ((lo >> 16) & 0xFF00u) | ((hi << 8) & 0xFF0000u) | (hi & 0xFF000000u);
+    w0 = (w0 + 0x78787878u) ^ 0x80808080u;
+    w1 = (w1 + 0x78787878u) ^ 0x80808080u;
+}
+
+// MODE 0: gate/up, A = x (int8 per 32-block), output h requantised; MODE 1: down, A = h, output y
+template <int MODE, typename YT>
+__global__ __launch_bounds__(256) void ffn_q8_tiled(const int8_t* __restrict__ aq, const float* __restrict__ as_,
+                                                    int T, int d, int f, int k,
+                                                    const void* const* __restrict__ expert_ptrs,
+                                                    const uint8_t* __restrict__ shared_blob,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ sorted_idx,
+                                                    const int32_t* __restrict__ active,
+                                                    const int4* __restrict__ tiles,
+                                                    const int32_t* __restrict__ n_tiles_p, int8_t* __restrict__ hq,
+                                                    float* __restrict__ hs, YT* __restrict__ y_perm,
+                                                    float* __restrict__ y_shared) {
+    __shared__ TileSmem S;
+    __shared__ int32_t s_row[kTM * 32];  // source row of each tile row (token for gate/up, h row for down)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K = MODE == 0 ? d : f;
+    const int n_groups = MODE == 0 ? f / 64 : d / 128;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int ti = (j / n_groups) * 8 + xcd, grp = j % n_groups;
+    if (ti >= n_tiles_p[0]) return;
+    const int4 tl = tiles[ti];
+    const int n_active = active[0];
+    const bool routed = tl.x < n_active;
+    const int e = routed ? active[1 + tl.x] : -1;
+    const uint8_t* blob = routed ? (const uint8_t*)expert_ptrs[e] : shared_blob;
+    if (blob == nullptr) return;  // no weights behind this expert (uniform per workgroup)
+    const int p0 = routed ? offsets[e] : T * k;
+    const int m0 = tl.y, mc = tl.z;
+    const int nmt = (mc + 31) >> 5;
+    for (int i = threadIdx.x; i < kTM * 32; i += 256) {
+        const int m = min(i, mc - 1);  // rows past the tile repeat its last row (results discarded)
+        if (MODE == 0) s_row[i] = routed ? sorted_idx[p0 + m0 + m] / k : m0 + m;
+        else s_row[i] = p0 + m0 + m;
+    }
+    const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
+    const int nkt = K / 128;
+    const int nb = K / 32;
+    __syncthreads();
+    // staging registers: activations 6 x 16 B, weights 2 lane words, weight scales 8 B, activation scales 16 B
+    uint4v ra[6];
+    uint4v rw[2];
+    uint2v rsw = {0u, 0u};
+    float4v rsa = {0.f, 0.f, 0.f, 0.f};
+    auto load_chunk = [&](int c) {
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+            const int idx = threadIdx.x + q * 256, row = idx >> 3, ch = idx & 7;
+            ra[q] = gload(reinterpret_cast<const uint4v*>(aq + (size_t)s_row[row] * K + c * kTKC) + ch);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int idx = threadIdx.x + q * 256, st = idx >> 6, ll = idx & 63;
+            const MatLayout& M = MODE == 0 ? (st < 4 ? L.g : L.u) : L.dn;
+            const int strip = MODE == 0 ? grp * 4 + (st & 3) : grp * 8 + st;
+            rw[q] = gload(reinterpret_cast<const uint4v*>(blob + M.qoff + ((size_t)strip * nkt + c) * 1024) + ll);
+        }
+        if (threadIdx.x < 128) {
+            const int st = threadIdx.x >> 4, rr = threadIdx.x & 15;
+            const MatLayout& M = MODE == 0 ? (st < 4 ? L.g : L.u) : L.dn;
+            const int strip = MODE == 0 ? grp * 4 + (st & 3) : grp * 8 + st;
+            rsw = gload(reinterpret_cast<const uint2v*>(blob + M.soff + ((size_t)strip * nkt + c) * 128 + rr * 8));
+        }
+        if (threadIdx.x < kTM * 32)
+            rsa = gload(reinterpret_cast<const float4v*>(as_ + (size_t)s_row[threadIdx.x] * nb + c * 4));
+    };
+    auto store_chunk = [&]() {
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+            const int idx = threadIdx.x + q * 256, row = idx >> 3, ch = idx & 7;
+            S.a[row][ch ^ (row & 7)] = __builtin_bit_cast(uint4, ra[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int idx = threadIdx.x + q * 256, st = idx >> 6, ll = idx & 63;
+            const int row = st * 16 + (ll & 15), kq = ll >> 4;  // bytes 8 kq .. 8 kq + 7 of each block
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                uint32_t w0, w1;
+                int4_word_to_i8(rw[q][b], w0, w1);
+                const int ch = 2 * b + (kq >> 1);
+                uint2* dst = reinterpret_cast<uint2*>(&S.w[row][ch ^ (row & 7)]) + (kq & 1);
+                *dst = make_uint2(w0, w1);
+            }
+        }
+        if (threadIdx.x < 128) {
+            // fp16 scales by integer extraction (a bit cast of a vector element to a half pair is avoided)
+            const int row = threadIdx.x;
+            const uint32_t w01 = rsw[0], w23 = rsw[1];
+            S.sw[0][row] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w01 & 0xFFFFu));
+            S.sw[1][row] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w01 >> 16));
+            S.sw[2][row] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w23 & 0xFFFFu));
+            S.sw[3][row] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w23 >> 16));
+        }
+        if (threadIdx.x < kTM * 32) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) S.sa[b][threadIdx.x] = rsa[b];
+        }
+    };
+    const int mt0 = 3 * (wave >> 1);
+    const int nt0 = MODE == 0 ? (wave & 1) : 2 * (wave & 1);
+    const int nt1 = MODE == 0 ? 2 + (wave & 1) : 2 * (wave & 1) + 1;
+    const int16v cmagic = {(int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
+                           (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
+                           (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
+                           (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits};
+    float16v acc[3][2];
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+    const int nkc = K / kTKC;
+    for (int c = 0; c < nkc; ++c) {
+        if (c > 0) __syncthreads();  // the previous chunk is no longer read
+        load_chunk(c);
+        store_chunk();
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int kq = 2 * b + (lane >> 5);  // 16-byte chunk holding this lane's 16 k of block b
+            int4v B[2];
+            float sw[2], nc[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int row = (n == 0 ? nt0 : nt1) * 32 + (lane & 31);
+                B[n] = __builtin_bit_cast(int4v, S.w[row][kq ^ (row & 7)]);
+                sw[n] = S.sw[b][row];
+                nc[n] = -kMagic * sw[n];
+            }
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                if (mt0 + m >= nmt) continue;
+                const int row = (mt0 + m) * 32 + (lane & 31);
+                const int4v A = __builtin_bit_cast(int4v, S.a[row][kq ^ (row & 7)]);
+                float sa[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *reinterpret_cast<const float4*>(&S.sa[b][(mt0 + m) * 32 + 8 * q + 4 * (lane >> 5)]);
+                    sa[4 * q + 0] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+                }
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const int16v D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[n], cmagic, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float t = fmaf(__int_as_float(D[r]), sw[n], nc[n]);
+                        acc[m][n][r] = fmaf(t, sa[r], acc[m][n][r]);
+                    }
+                }
+            }
+        }
+    }
+    if (MODE == 0) {
+        // h = silu(g) * u, requantised per (token, 32 features of this wavefront)
+        const int feat = grp * 64 + (wave & 1) * 32 + (lane & 31);
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            if (mt0 + m >= nmt) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float hv = silu_q(acc[m][0][r]) * acc[m][1][r];
+                float amax = fabsf(hv);
+#pragma unroll
+                for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+                const float sc = amax / 127.0f;
+                int q = 0;
+                if (sc != 0.0f) q = (int)fminf(fmaxf(rintf(hv / sc), -127.0f), 127.0f);
+                const int mrow = (mt0 + m) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (mrow < mc) {
+                    const size_t hrow = (size_t)(p0 + m0 + mrow);
+                    hq[hrow * f + feat] = (int8_t)q;
+                    if ((lane & 31) == 0) hs[hrow * (f / 32) + grp * 2 + (wave & 1)] = sc;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            if (mt0 + m >= nmt) continue;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int o = grp * 128 + (n == 0 ? nt0 : nt1) * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int mrow = (mt0 + m) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (mrow >= mc) continue;
+                    if (routed) y_perm[(size_t)(p0 + m0 + mrow) * d + o] = (YT)acc[m][n][r];
+                    else y_shared[(size_t)(m0 + mrow) * d + o] = acc[m][n][r];
+                }
+            }
+        }
+    }
+}
+
 template <int WFMT>
 static int run_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     int2* tiles = reinterpret_cast<int2*>(w.tiles);
-    int32_t* n_tiles = w.tiles + 2 * q8_tile_capacity(a->T, a->k, a->E);
+    const size_t cap = q8_tile_capacity(a->T, a->k, a->E);
+    int32_t* n_tiles = w.tiles + 4 * cap;  // after the tile list (room for cap int4 or int2 entries)
+    int8_t* hq = reinterpret_cast<int8_t*>(w.h);
     int rc;
+    if constexpr (WFMT == MOE_WFMT_I4B32) {
+        // tiles of <= 192 rows; work items of one tile on one XCD (grid rounded to 8 tiles)
+        int4* t4 = reinterpret_cast<int4*>(w.tiles);
+        const long max_tiles = (long)std::min(a->E, a->T * a->k) + (long)a->T * a->k / (kTM * 32) +
+                               (a->shared_blob ? a->T / (kTM * 32) + 1 : 0);
+        const long gt = (max_tiles + 7) / 8 * 8;
+        if (a->phase != 2) {
+            q8_tile_plan<<<1, 1024, 0, s>>>(a->counts, a->active, a->T, a->shared_blob ? 1 : 0, t4, n_tiles);
+            rc = check_launch();
+            if (rc) return rc;
+            ffn_q8_tiled<0, float><<<(unsigned)(gt * (a->f / 64)), 256, 0, s>>>(
+                a->xq, a->sx, a->T, a->d, a->f, a->k, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->offsets,
+                a->sorted_idx, a->active, t4, n_tiles, hq, w.hs, nullptr, nullptr);
+            rc = check_launch();
+            if (rc || a->phase == 1) return rc;
+        }
+        if (a->y_dtype == MOE_DT_F32)
+            ffn_q8_tiled<1, float><<<(unsigned)(gt * (a->d / 128)), 256, 0, s>>>(
+                hq, w.hs, a->T, a->d, a->f, a->k, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->offsets,
+                a->sorted_idx, a->active, t4, n_tiles, nullptr, nullptr, (float*)a->y_perm, a->y_shared);
+        else
+            ffn_q8_tiled<1, _Float16><<<(unsigned)(gt * (a->d / 128)), 256, 0, s>>>(
+                hq, w.hs, a->T, a->d, a->f, a->k, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->offsets,
+                a->sorted_idx, a->active, t4, n_tiles, nullptr, nullptr, (_Float16*)a->y_perm, a->y_shared);
+        return check_launch();
+    }
     if (a->phase != 2) {
         q8_plan<<<1, 1024, 0, s>>>(a->counts, a->active, a->E, a->T, a->shared_blob ? 1 : 0, tiles, n_tiles);
         rc = check_launch();
@@ -339,7 +632,6 @@ static int run_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     }
     const long max_tiles = (long)std::min(a->E, a->T * a->k) + (long)a->T * a->k / kMG + (a->shared_blob ? a->T / kMG + 1 : 0);
     const size_t smem = sizeof(Q8Smem);
-    int8_t* hq = reinterpret_cast<int8_t*>(w.h);
     const int g1 = (int)std::min<long>(max_tiles * (a->f / 64), 4096);
     if (a->phase != 2) {
         ffn_q8_gateup<WFMT><<<g1, 256, smem, s>>>(a->xq, a->sx, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs,
