@@ -336,9 +336,10 @@ __global__ __launch_bounds__(256) void ffn_float_down(const _Float16* __restrict
 // For T <= 16 every token is a row of the MFMA A operand (rows >= T repeat the
 // last token and are discarded), so a work item needs no gather and the token
 // tile is staged once per workgroup.  Work item = (slot, 16-row strip of f);
-// two wavefronts split its reduction (NT tiles each) and software-pipeline
-// their quant tiles two ahead, so that loads of later tiles overlap the
-// products of earlier ones.  Each block of 8 weights becomes (q - 8) * s in
+// S wavefronts (2 or 4) split its reduction (NT tiles each) and
+// software-pipeline their quant tiles two ahead, so that loads of later tiles
+// overlap the products of earlier ones.  S = 4 when few experts are active,
+// so that enough loads are in flight.  Each block of 8 weights becomes (q - 8) * s in
 // fp16 with one rounding: the low nibbles of a byte through the 0x6400 magic
 // (1024 + q), the high nibbles in place (1024 + 16 q) rescaled by an exact
 // fma, then one multiply by the block scale; the MFMA then accumulates the
@@ -369,7 +370,7 @@ __device__ __forceinline__ half2v scale_pair(const uint2v& raw, int b) {
 constexpr int kTokMax = 16;   // tokens of the token-dense kernels
 constexpr int kPipe = 2;      // quant tiles in flight ahead of the products
 
-template <int NT, typename XT>
+template <int NT, int S, typename XT>
 __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x, int T, int d, int f, int k,
                                                         const void* const* __restrict__ expert_ptrs,
                                                         const uint8_t* __restrict__ shared_blob,
@@ -381,9 +382,9 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
     const int XC = d / 8;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int part = wave & 1;
+    const int part = wave % S;
     const int n_strips = f / 16;
-    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 2 + (wave >> 1));
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * (4 / S) + wave / S);
     const int n_active = active[0];
     const int n_slots = n_active + (shared_blob ? 1 : 0);
     const int a = item / n_strips, strip = item % n_strips;
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
     float4v accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
     if (work) {
         const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
-        const size_t tile0 = (size_t)strip * (2 * NT) + part * NT;
+        const size_t tile0 = (size_t)strip * (S * NT) + part * NT;
         const uint4v* pg = reinterpret_cast<const uint4v*>(blob + L.g.qoff + tile0 * 1024) + lane;
         const uint4v* pu = reinterpret_cast<const uint4v*>(blob + L.u.qoff + tile0 * 1024) + lane;
         const uint2v* psg = reinterpret_cast<const uint2v*>(blob + L.g.soff + tile0 * 128 + (lane & 15) * 8);
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // the two halves of the reduction meet in LDS (the token tile is no longer read)
+    // the parts of the reduction meet in LDS (the token tile is no longer read)
     __syncthreads();
     float(*red)[2][4][64] = reinterpret_cast<float(*)[2][4][64]>(xs4);
 #pragma unroll
@@ -467,20 +468,24 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
     }
     __syncthreads();
     if (!work) return;
-    const int w0 = wave & ~1;
+    const int w0 = wave - part;
     int c = T, p0 = T * k;
     if (e >= 0) {
         c = counts[e];
         p0 = offsets[e];
     }
-    // accumulator row r holds token 4 * (lane / 16) + r; wavefront `part` writes rows r = part, part + 2,
+    // accumulator row r holds token 4 * (lane / 16) + r; wavefront `part` writes rows r = part, part + S, ..
     // to every position of the slot that token t occupies (a token listed twice gets two rows)
 #pragma unroll
-    for (int r = part; r < 4; r += 2) {
+    for (int r = part; r < 4; r += S) {
         const int t = 4 * (lane >> 4) + r;
         if (t >= T) continue;
-        const float g = red[w0][0][r][lane] + red[w0 + 1][0][r][lane];
-        const float u = red[w0][1][r][lane] + red[w0 + 1][1][r][lane];
+        float g = red[w0][0][r][lane], u = red[w0][1][r][lane];
+#pragma unroll
+        for (int q = 1; q < S; ++q) {
+            g += red[w0 + q][0][r][lane];
+            u += red[w0 + q][1][r][lane];
+        }
         const _Float16 hv = (_Float16)(silu_f(g) * u);
         if (e < 0) {
             h[(size_t)(p0 + t) * f + strip * 16 + (lane & 15)] = hv;
@@ -495,17 +500,27 @@ template <typename XT>
 static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, hipStream_t s) {
     const int nkt = a->d / 128;
     const int items = slots * (a->f / 16);
-    const dim3 grid((items + 1) / 2);
+    // few items (a single token routes to k + 1 slots): four wavefronts per item
+    const bool four = items < 1024 && nkt % 4 == 0;
+    const dim3 grid(four ? items : (items + 1) / 2);
     const size_t lds = std::max<size_t>((size_t)a->T * a->d * sizeof(_Float16), 4 * 2 * 4 * 64 * sizeof(float));
-#define MOE_GU16(NT)                                                                                           \
-    ffn_gateup_tok16<NT, XT><<<grid, 256, lds, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs,   \
-                                                    (const uint8_t*)a->shared_blob, a->counts, a->offsets,      \
-                                                    a->sorted_idx, a->active, h)
+#define MOE_GU16(NT, S)                                                                                         \
+    ffn_gateup_tok16<NT, S, XT><<<grid, 256, lds, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs, \
+                                                       (const uint8_t*)a->shared_blob, a->counts, a->offsets,    \
+                                                       a->sorted_idx, a->active, h)
+    if (four) {
+        switch (nkt) {
+        case 8: MOE_GU16(2, 4); return true;
+        case 16: MOE_GU16(4, 4); return true;
+        case 32: MOE_GU16(8, 4); return true;
+        default: return false;
+        }
+    }
     switch (nkt) {
-    case 4: MOE_GU16(2); return true;
-    case 8: MOE_GU16(4); return true;
-    case 16: MOE_GU16(8); return true;
-    case 32: MOE_GU16(16); return true;
+    case 4: MOE_GU16(2, 2); return true;
+    case 8: MOE_GU16(4, 2); return true;
+    case 16: MOE_GU16(8, 2); return true;
+    case 32: MOE_GU16(16, 2); return true;
     default: return false;
     }
 #undef MOE_GU16
