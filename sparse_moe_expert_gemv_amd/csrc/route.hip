@@ -52,81 +52,107 @@ __device__ void topk_iterative(double (&v)[NPL], int E, int k, int32_t* zi, doub
     }
 }
 
+// (v1, i1) ranks before (v2, i2): larger logit, then lower index
+__device__ __forceinline__ bool ranks_before(double v1, int i1, double v2, int i2) {
+    return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// One compare-exchange step of a bitonic sort across the wavefront (lane pairs
+// l, l ^ J inside blocks of SIZE lanes; the last stage sorts all 64 into rank order).
+template <int SIZE, int J>
+__device__ __forceinline__ void bitonic_step(double& v, int& i) {
+    const int lane = threadIdx.x & 63;
+    const double pv = lane_xor_d<J>(v);
+    const int pi = (int)lane_xor<J>((uint32_t)i);
+    const bool first = (lane & J) == 0;
+    const bool best_first = SIZE == 64 || (lane & SIZE) == 0;
+    if ((first == best_first) == ranks_before(pv, pi, v, i)) {
+        v = pv;
+        i = pi;
+    }
+}
+
+// Sort one (value, index) pair per lane into rank order (lane 0 = best); indices distinct.
+__device__ __forceinline__ void wave_rank_sort(double& v, int& i) {
+    bitonic_step<2, 1>(v, i);
+    bitonic_step<4, 2>(v, i); bitonic_step<4, 1>(v, i);
+    bitonic_step<8, 4>(v, i); bitonic_step<8, 2>(v, i); bitonic_step<8, 1>(v, i);
+    bitonic_step<16, 8>(v, i); bitonic_step<16, 4>(v, i); bitonic_step<16, 2>(v, i); bitonic_step<16, 1>(v, i);
+    bitonic_step<32, 16>(v, i); bitonic_step<32, 8>(v, i); bitonic_step<32, 4>(v, i); bitonic_step<32, 2>(v, i);
+    bitonic_step<32, 1>(v, i);
+    bitonic_step<64, 32>(v, i); bitonic_step<64, 16>(v, i); bitonic_step<64, 8>(v, i); bitonic_step<64, 4>(v, i);
+    bitonic_step<64, 2>(v, i); bitonic_step<64, 1>(v, i);
+}
+
 // One wavefront selects the top-k of z[0..E) by (value desc, index asc).
-//  1. every lane's maximum over its values; tau = the k-th best lane maximum
-//     (ranked by counting), so at least k values are >= tau;
-//  2. the values >= tau (usually k..2k) are compacted into LDS;
-//  3. each candidate's exact rank among the candidates is counted.
+//  1. every lane's maximum over its values; the lane maxima are sorted across
+//     the wavefront and tau = the kk-th of them, so that every value of the
+//     top k ranks at or before tau;
+//  2. the values ranking at or before tau (usually k..2k) are compacted into LDS;
+//  3. they are sorted across the wavefront; lanes 0..k-1 hold the result.
+// More than 64 candidates (heavy ties) fall back to k rounds of wave argmax.
 // scratch: LDS for 64 (value, index) pairs plus k selected pairs.
 template <int NPL>
 __device__ void topk_wave(const double* __restrict__ z, int E, int k, int32_t* __restrict__ ids,
                           float* __restrict__ gates, int32_t* s_ids, double* cv, int32_t* ci) {
     const int lane = threadIdx.x & 63;
     double v[NPL];
-    double lm = -DBL_MAX;
-    int li = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
         v[i] = e < E ? z[e] : -DBL_MAX;
-        if (e < E && (v[i] > lm || (v[i] == lm && e < li))) { lm = v[i]; li = e; }
     }
-    // rank of each lane maximum among the 64 (lanes with no value rank last)
-    int rank = 0;
-    for (int j = 0; j < 64; ++j) {
-        const double oj = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(lm), j),
-                                           __builtin_amdgcn_readlane(__double2loint(lm), j));
-        const int oi = __builtin_amdgcn_readlane(li, j);
-        rank += better(lm, li, oj, oi) ? 1 : 0;
+    double lm = v[0];
+    int li = lane;
+#pragma unroll
+    for (int i = 1; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && v[i] > lm) { lm = v[i]; li = e; }  // strict: equal values keep the lower index
     }
+    if (lane >= E) { lm = -DBL_MAX; li = 0x40000000 + lane; }  // lanes without values rank last
+    wave_rank_sort(lm, li);
     const int nlanes = E < 64 ? E : 64;
     const int kk = k < nlanes ? k : nlanes;  // with fewer lanes than k, take the weakest lane maximum
-    const unsigned long long sel = __ballot(lane < nlanes && rank == kk - 1);
-    const int src = __builtin_ffsll((long long)sel) - 1;
-    const double tau = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(lm), src),
-                                        __builtin_amdgcn_readlane(__double2loint(lm), src));
-    // candidates: every value >= tau (for E < 64*... all values >= tau are kept)
+    const double tau = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(lm), kk - 1),
+                                        __builtin_amdgcn_readlane(__double2loint(lm), kk - 1));
+    const int taui = __builtin_amdgcn_readlane(li, kk - 1);
     const unsigned long long lt = (1ull << lane) - 1ull;
     int base = 0;
-    bool overflow = false;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
-        const bool c = e < E && v[i] >= tau;
+        const bool c = e < E && (e == taui || ranks_before(v[i], e, tau, taui));
         const unsigned long long b = __ballot(c);
         const int pos = base + __popcll(b & lt);
         if (c && pos < 64) { cv[pos] = v[i]; ci[pos] = e; }
         base += __popcll(b);
     }
-    overflow = base > 64;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_s_waitcnt(0);
-    double* zv = cv + 64;  // selected values [k]
-    int32_t* zi = ci + 64; // selected indices [k]
-    if (!overflow) {
-        const int nc = base;
-        if (lane < nc) {
-            const double mv = cv[lane];
-            const int mi = ci[lane];
-            int r = 0;
-            for (int j = 0; j < nc; ++j) r += better(mv, mi, cv[j], ci[j]) ? 1 : 0;
-            if (r < k) { zv[r] = mv; zi[r] = mi; }
-        }
+    double sv;
+    int si;
+    if (base <= 64) {
+        sv = lane < base ? cv[lane] : -DBL_MAX;
+        si = lane < base ? ci[lane] : 0x40000000 + lane;
+        wave_rank_sort(sv, si);
     } else {
+        double* zv = cv + 64;  // selected values [k]
+        int32_t* zi = ci + 64; // selected indices [k]
         topk_iterative<NPL>(v, E, k, zi, zv);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0);
+        sv = lane < k ? zv[lane] : -DBL_MAX;
+        si = lane < k ? zi[lane] : 0;
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
-    double zsel = 0.0;
+    const double z0 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(sv), 0),
+                                       __builtin_amdgcn_readlane(__double2loint(sv), 0));
+    const double p = lane < k ? exp(sv - z0) : 0.0;
+    const double ssum = wave_sum_xor_d(p);
     if (lane < k) {
-        zsel = zv[lane];
-        ids[lane] = zi[lane];
-        if (s_ids) s_ids[lane] = zi[lane];
+        ids[lane] = si;
+        gates[lane] = (float)(p / ssum);
+        if (s_ids) s_ids[lane] = si;
     }
-    const double z0 = zv[0];
-    const double p = lane < k ? exp(zsel - z0) : 0.0;
-    const double ssum = wave_sum_d(p);
-    if (lane < k) gates[lane] = (float)(p / ssum);
 }
 
 // per-wavefront LDS scratch of topk_wave: 64 + 64 candidates/selected pairs
@@ -330,6 +356,75 @@ __global__ __launch_bounds__(256) void route_logits_rows(const XT* __restrict__ 
     }
 }
 
+// ascending bitonic sort of one 32-bit key per lane
+template <int SIZE, int J>
+__device__ __forceinline__ void bitonic_step_u(uint32_t& v) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t pv = lane_xor<J>(v);
+    const bool first = (lane & J) == 0;
+    const bool asc = SIZE == 64 || (lane & SIZE) == 0;
+    const uint32_t lo = pv < v ? pv : v, hi = pv < v ? v : pv;
+    v = (first == asc) ? lo : hi;
+}
+__device__ __forceinline__ void wave_sort_u32(uint32_t& v) {
+    bitonic_step_u<2, 1>(v);
+    bitonic_step_u<4, 2>(v); bitonic_step_u<4, 1>(v);
+    bitonic_step_u<8, 4>(v); bitonic_step_u<8, 2>(v); bitonic_step_u<8, 1>(v);
+    bitonic_step_u<16, 8>(v); bitonic_step_u<16, 4>(v); bitonic_step_u<16, 2>(v); bitonic_step_u<16, 1>(v);
+    bitonic_step_u<32, 16>(v); bitonic_step_u<32, 8>(v); bitonic_step_u<32, 4>(v); bitonic_step_u<32, 2>(v);
+    bitonic_step_u<32, 1>(v);
+    bitonic_step_u<64, 32>(v); bitonic_step_u<64, 16>(v); bitonic_step_u<64, 8>(v); bitonic_step_u<64, 4>(v);
+    bitonic_step_u<64, 2>(v); bitonic_step_u<64, 1>(v);
+}
+
+// Stable grouping of n <= 64 slots (ids in LDS) by one 256-thread workgroup:
+// wavefront 0 sorts the keys (id << 10 | slot), which yields sorted_idx, dest
+// and the active list directly; then every thread counts, for its experts, the
+// sorted keys below each expert's key range (offsets) and inside it (counts).
+// Ids outside [0, E) are ignored.  Same outputs as block_permute.
+__device__ void small_permute64(const int32_t* s_ids, int n, int E, int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_idx, int32_t* dest, int32_t* active, uint32_t* s_keys) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int id = lane < n ? s_ids[lane] : -1;
+        const bool valid = (unsigned)id < (unsigned)E;
+        uint32_t key = valid ? ((uint32_t)id << 10) | (uint32_t)lane : 0xFFFFFFFFu;
+        wave_sort_u32(key);
+        s_keys[lane] = key;
+        const bool kv = key != 0xFFFFFFFFu;
+        if (kv) {
+            const int slot = (int)(key & 1023u);
+            sorted_idx[lane] = slot;
+            dest[slot] = lane;
+        }
+        const int kid = (int)(key >> 10);
+        const int pid = __shfl_up(kid, 1);
+        const bool first = kv && (lane == 0 || pid != kid);
+        const unsigned long long fb = __ballot(first);
+        if (first) active[1 + __popcll(fb & ((1ull << lane) - 1ull))] = kid;
+        if (lane == 0) active[0] = __popcll(fb);
+    }
+    __syncthreads();
+    uint32_t keys[64];
+#pragma unroll
+    for (int q = 0; q < 64; q += 4) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(&s_keys[q]);
+        keys[q] = kv.x; keys[q + 1] = kv.y; keys[q + 2] = kv.z; keys[q + 3] = kv.w;
+    }
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const uint32_t lo = (uint32_t)e << 10, hi = (uint32_t)(e + 1) << 10;
+        int below = 0, upto = 0;
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            below += keys[q] < lo;
+            upto += keys[q] < hi;
+        }
+        counts[e] = upto - below;
+        offsets[e] = below;
+        if (e == E - 1) offsets[E] = upto;
+    }
+}
+
 // One workgroup: top-k of every token (T <= kSmallSlots / k) and, when asked,
 // the grouping of the routing slots by expert.
 __global__ __launch_bounds__(256) void route_select_small(const double* __restrict__ logits, int T, int E, int k,
@@ -342,13 +437,18 @@ __global__ __launch_bounds__(256) void route_select_small(const double* __restri
     __shared__ int32_t s_ids[kSmallSlots];
     __shared__ int32_t s_cnt[1024];
     __shared__ int32_t s_part[256], s_flag[256];
+    __shared__ __align__(16) uint32_t s_keys[64];
     const int wave = threadIdx.x >> 6;
     for (int t = wave; t < T; t += 4)
         topk_dispatch(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, s_ids + t * k,
                       sc[wave]);
     __syncthreads();
-    if (do_permute)
-        block_permute(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_cnt, s_part, s_flag);
+    if (do_permute) {
+        if (T * k <= 64)
+            small_permute64(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_keys);
+        else
+            block_permute(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_cnt, s_part, s_flag);
+    }
 }
 
 // General T: 64 tokens x 64 experts per workgroup, 4x4 outputs per thread,
@@ -404,8 +504,87 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const XT* __restrict__
 
 bool route_small_ok(int T, int d, int k) { return T <= 64 && (size_t)T * k <= kSmallSlots && (size_t)kTG * d * 4 <= 64 * 1024; }
 
+// ------------------------------------------------ wavefront per row (T <= 8) ----
+// Decode batches: grid = E wavefronts, each computes one router row against all
+// T <= 8 tokens.  The lane's router values (float4 q = u * 64 + lane) and the
+// matching token values are loaded straight from global memory, all before any
+// arithmetic; no LDS and no barrier, so every wavefront runs on its own.
+template <typename XT, int TT, int NU>
+__global__ __launch_bounds__(64) void route_logits_wave(const XT* __restrict__ x, int T, int d,
+                                                        const float* __restrict__ Wr,
+                                                        const float* __restrict__ bias, int E,
+                                                        double* __restrict__ logits) {
+    const int lane = threadIdx.x;
+    const int e = blockIdx.x;
+    const int nq = d / 4;
+    const float4* w = reinterpret_cast<const float4*>(Wr + (size_t)e * d);
+    float4 wv[NU];
+    float4 xv[TT][NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) wv[u] = w[min(u * 64 + lane, nq - 1)];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const int tt = min(t, T - 1);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int q = min(u * 64 + lane, nq - 1);
+            if constexpr (sizeof(XT) == 4) {
+                xv[t][u] = reinterpret_cast<const float4*>(x + (size_t)tt * d)[q];
+            } else {
+                const uint2 r = reinterpret_cast<const uint2*>(x + (size_t)tt * d)[q];
+                xv[t][u] = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
+                                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
+            }
+        }
+    }
+    double acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = 0.0;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        if (u * 64 + lane >= nq) continue;
+        const double w0 = wv[u].x, w1 = wv[u].y, w2 = wv[u].z, w3 = wv[u].w;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            acc[t] = fma((double)xv[t][u].x, w0, acc[t]);
+            acc[t] = fma((double)xv[t][u].y, w1, acc[t]);
+            acc[t] = fma((double)xv[t][u].z, w2, acc[t]);
+            acc[t] = fma((double)xv[t][u].w, w3, acc[t]);
+        }
+    }
+    const double b = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const double sm = wave_sum_xor_d(acc[t]);
+        if (lane == 0 && t < T) logits[(size_t)t * E + e] = sm + b;
+    }
+}
+
+template <typename XT, int NU>
+static bool launch_logits_wave(const XT* x, int T, int d, const float* Wr, const float* bias, int E, double* logits,
+                               hipStream_t s) {
+    if (T <= 1) route_logits_wave<XT, 1, NU><<<E, 64, 0, s>>>(x, T, d, Wr, bias, E, logits);
+    else if (T <= 2) route_logits_wave<XT, 2, NU><<<E, 64, 0, s>>>(x, T, d, Wr, bias, E, logits);
+    else if (T <= 4) route_logits_wave<XT, 4, NU><<<E, 64, 0, s>>>(x, T, d, Wr, bias, E, logits);
+    else if (T <= 8) route_logits_wave<XT, 8, NU><<<E, 64, 0, s>>>(x, T, d, Wr, bias, E, logits);
+    else return false;
+    return true;
+}
+
 static int launch_logits(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E,
                          double* logits, hipStream_t s) {
+    if (T <= 8 && d <= 2048) {
+        // one wavefront per router row; NU float4 per lane cover d
+        const int nu = (d / 4 + 63) / 64;
+        bool ok;
+        if (x_dtype == MOE_DT_F32)
+            ok = nu <= 2 ? launch_logits_wave<float, 2>((const float*)x, T, d, Wr, bias, E, logits, s)
+                         : launch_logits_wave<float, 8>((const float*)x, T, d, Wr, bias, E, logits, s);
+        else
+            ok = nu <= 2 ? launch_logits_wave<uint16_t, 2>((const uint16_t*)x, T, d, Wr, bias, E, logits, s)
+                         : launch_logits_wave<uint16_t, 8>((const uint16_t*)x, T, d, Wr, bias, E, logits, s);
+        if (ok) return check_launch();
+    }
     if (T <= 256 && (size_t)kTG * d * 4 <= 64 * 1024) {
         const dim3 grid((E + 3) / 4, (T + kTG - 1) / kTG);
         const size_t lds = (size_t)std::min(T, kTG) * d * sizeof(float);

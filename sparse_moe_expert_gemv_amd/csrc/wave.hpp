@@ -48,6 +48,44 @@ __device__ __forceinline__ void wave_argmax(double& v, int& i) {
     i = bi;
 }
 
+// Value held by lane (lane ^ J), J in {1, 2, 4, 8, 16, 32}, with VALU lane
+// exchanges only: DPP within rows of 16 lanes (xor 4 from two row rotations),
+// v_permlane16_swap / v_permlane32_swap across rows.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (J == 1) return __builtin_amdgcn_update_dpp(v, v, kDppXor1, 0xF, 0xF, false);
+    else if constexpr (J == 2) return __builtin_amdgcn_update_dpp(v, v, kDppXor2, 0xF, 0xF, false);
+    else if constexpr (J == 4) {
+        const uint32_t a = __builtin_amdgcn_update_dpp(v, v, kDppRor4, 0xF, 0xF, false);   // lane - 4 (mod 16)
+        const uint32_t b = __builtin_amdgcn_update_dpp(v, v, 0x12C, 0xF, 0xF, false);      // lane + 4 (mod 16)
+        return (lane & 4) ? a : b;
+    } else if constexpr (J == 8) return __builtin_amdgcn_update_dpp(v, v, kDppRor8, 0xF, 0xF, false);
+    else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+
+template <int J>
+__device__ __forceinline__ double lane_xor_d(double v) {
+    return __hiloint2double((int)lane_xor<J>((uint32_t)__double2hiint(v)), (int)lane_xor<J>((uint32_t)__double2loint(v)));
+}
+
+// Sum over the 64 lanes, every lane gets the total (butterfly order).
+__device__ __forceinline__ double wave_sum_xor_d(double v) {
+    v += lane_xor_d<1>(v);
+    v += lane_xor_d<2>(v);
+    v += lane_xor_d<4>(v);
+    v += lane_xor_d<8>(v);
+    v += lane_xor_d<16>(v);
+    v += lane_xor_d<32>(v);
+    return v;
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
     return v;
