@@ -10,12 +10,14 @@ tiny).
 Layer weights are replicated into ``--rotate`` device copies and consecutive
 steps use consecutive copies with their own inputs, so each step streams its
 expert weights from HBM rather than from the 256 MB Infinity Cache.  Each
-copy's step is one captured HIP graph.  Two timed regions, both bracketed by a
-device synchronisation: (A) ``--steps`` whole-layer steps, which give
-``value`` and ``ms_per_step``; (B) ``--steps`` back-to-back launches of the
-dominant kernel alone (the expert gate/up projection, ``moe_expert_ffn``
-phase 1, rotating over the weight copies) between two HIP events on its launch
-stream, whose mean launch time gives the roofline figure.
+copy's step is captured in a HIP graph; one graph holds one step on every copy
+in turn, so that host launch overhead is paid once per ``--rotate`` steps.
+Two timed regions, both bracketed by a device synchronisation: (A) ``--steps``
+whole-layer steps, which give ``value`` and ``ms_per_step``; (B) ``--steps``
+back-to-back launches of the dominant kernel alone (the expert gate/up
+projection, ``moe_expert_ffn`` phase 1, rotating over the weight copies, also
+replayed from graphs) between two HIP events on its launch stream, whose mean
+launch time gives the roofline figure.
 
 Prints one JSON line (rank 0).  ``--gpus`` above 1 is not supported: this
 build runs on one GPU.
@@ -57,7 +59,7 @@ def measured_traffic(workload: str):
     FETCH_SIZE/WRITE_SIZE summary, if one exists for this workload and the
     kernel source has not changed since the counters were taken; else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "ffn_float_gateup_%s_hbm_counters.md" % workload)
+    path = os.path.join(ROOT, "profiles", "gateup_%s_hbm_counters.md" % workload)
     src = os.path.join(ROOT, "sparse_moe_expert_gemv_amd", "csrc", "ffn_float.hip")
     if not os.path.exists(path):
         return None
@@ -182,15 +184,15 @@ def main():
 
     use_graph = not a.no_graph
     stream = torch.cuda.Stream()
-    step_graphs = []
-    if use_graph:
+
+    def capture(fn_r, rs):
+        """One graph running fn_r(r) for every r in rs, in order."""
+        g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
-            for r in range(rotate):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    run_step(layers[r], xs[r])
-                step_graphs.append(g)
-        torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for r in rs:
+                    fn_r(r)
+        return g
 
     def timed(fn, n):
         with torch.cuda.stream(stream):
@@ -204,26 +206,36 @@ def main():
             torch.cuda.synchronize()
         return start.elapsed_time(end)
 
-    # region A: whole steps
-    def step_i(i):
-        r = i % rotate
-        if use_graph:
-            step_graphs[r].replay()
-        else:
-            run_step(layers[r], xs[r])
+    def run_all(fn_r, graphs, n):
+        """n launches of fn_r over the copies in order: whole rotations from the
+        all-copies graph, the remainder from single-copy graphs (eager without graphs)."""
+        if graphs is None:
+            for i in range(n):
+                fn_r(i % rotate)
+            return
+        chain, singles = graphs
+        for _ in range(n // rotate):
+            chain.replay()
+        for i in range(n % rotate):
+            singles[i].replay()
 
-    timed(step_i, rotate)  # one more pass over the copies
-    total_ms = timed(step_i, steps)
+    step_r = lambda r: run_step(layers[r], xs[r])
+    gu_r = lambda r: run_ffn(layers[r], xs[r], phase=1)
+    step_graphs = gu_graphs = None
+    if use_graph:
+        step_graphs = (capture(step_r, range(rotate)), [capture(step_r, [r]) for r in range(rotate)])
+        gu_graphs = (capture(gu_r, range(rotate)), [capture(gu_r, [r]) for r in range(rotate)])
+        torch.cuda.synchronize()
+
+    # region A: whole steps
+    timed(lambda i: run_all(step_r, step_graphs, rotate), 1)  # one more pass over the copies
+    total_ms = timed(lambda i: run_all(step_r, step_graphs, steps), 1)
     ms_step = total_ms / steps
 
     # region B: the dominant kernel (gate/up) alone: --steps back-to-back launches on
     # the stream, rotating over the weight copies, between two HIP events
-    def gu_i(i):
-        r = i % rotate
-        run_ffn(layers[r], xs[r], phase=1)
-
-    timed(gu_i, rotate)
-    gu_ms = timed(gu_i, steps) / steps
+    timed(lambda i: run_all(gu_r, gu_graphs, rotate), 1)
+    gu_ms = timed(lambda i: run_all(gu_r, gu_graphs, steps), 1) / steps
 
     # algorithmic work per gate/up launch, from each copy's routing (fixed input per copy)
     n_act = [int(G.active[0].item()) for G in layers]
@@ -238,7 +250,11 @@ def main():
         achieved = alg_bytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name)}
-    roof["kernel"] = "ffn_%s_gateup (moe_expert_ffn phase 1)" % ("q8" if mode == B.MOE_ACT_Q8 else "float")
+    if mode == B.MOE_ACT_Q8:
+        roof["kernel"] = "ffn_q8_tiled<0> (moe_expert_ffn phase 1)" if cfg.wfmt == 4 else "ffn_q8_gateup (moe_expert_ffn phase 1)"
+    else:
+        roof["kernel"] = ("ffn_gateup_tok16 (moe_expert_ffn phase 1)" if cfg.wfmt == 4 and T <= 16
+                          else "ffn_float_gateup (moe_expert_ffn phase 1)")
     roof["kernel_ms"] = round(gu_ms, 5)
     roof["algorithmic_bytes_per_launch"] = int(alg_bytes)
     roof["algorithmic_ops_per_launch"] = int(alg_ops)
