@@ -370,8 +370,53 @@ __device__ __forceinline__ half2v scale_pair(const uint2v& raw, int b) {
 constexpr int kTokMax = 16;   // tokens of the token-dense kernels
 constexpr int kPipe = 2;      // quant tiles in flight ahead of the products
 
+// Raw 16-byte token chunks, converted to fp16 only when stored to LDS, so that
+// the loads can be issued before anything else without waiting on them.
+template <typename XT> struct XChunk;
+template <> struct XChunk<uint16_t> {
+    uint4v r;
+    __device__ __forceinline__ void load(const uint16_t* p) { r = gload(reinterpret_cast<const uint4v*>(p)); }
+    __device__ __forceinline__ half8 cvt() const {
+        half8 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = (_Float16)__uint_as_float(r[j] << 16);
+            v[2 * j + 1] = (_Float16)__uint_as_float(r[j] & 0xFFFF0000u);
+        }
+        return v;
+    }
+};
+template <> struct XChunk<float> {
+    uint4v a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = gload(reinterpret_cast<const uint4v*>(p));
+        b = gload(reinterpret_cast<const uint4v*>(p) + 1);
+    }
+    __device__ __forceinline__ half8 cvt() const {
+        half8 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = (_Float16)__uint_as_float(a[j]);
+            v[4 + j] = (_Float16)__uint_as_float(b[j]);
+        }
+        return v;
+    }
+};
+
+// Buffer resource over [base, base + bytes): loads through it are bounds
+// checked and return zeros outside the range (bytes = 0: nothing is read).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Order of the start: token chunks requested first; slot metadata in two
+// dependent rounds (the list entry is read before the list length is known,
+// at a clamped index); then the first quant tiles and the slot's token list,
+// through buffer resources of size 0 when there is nothing to read, so that
+// the code stays straight-line and every wait is exact; only then the tokens
+// go to LDS.
 template <int NT, int S, typename XT>
-__global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x, int T, int d, int f, int k,
+__global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x, int T, int d, int f, int k, int E,
                                                         const void* const* __restrict__ expert_ptrs,
                                                         const uint8_t* __restrict__ shared_blob,
                                                         const int32_t* __restrict__ counts,
@@ -385,54 +430,67 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
     const int part = wave % S;
     const int n_strips = f / 16;
     const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * (4 / S) + wave / S);
-    const int n_active = active[0];
-    const int n_slots = n_active + (shared_blob ? 1 : 0);
     const int a = item / n_strips, strip = item % n_strips;
-    const uint8_t* blob = nullptr;
-    int e = -1;
-    if (a < n_active) {
-        e = active[1 + a];
-        blob = (const uint8_t*)expert_ptrs[e];
-    } else if (a < n_slots) {
-        blob = shared_blob;
-    }
-    // tokens -> LDS as fp16, four 8-element chunks per thread per round
     const int nx = T * XC;
-    for (int base = 0; base < nx; base += 4 * 256) {
-        half8 v[4];
+    XChunk<XT> xr[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int idx = min(base + (int)threadIdx.x + j * 256, nx - 1);
-            v[j] = load8_h(x + (size_t)idx * 8);
+    for (int j = 0; j < 4; ++j) xr[j].load(x + (size_t)min((int)threadIdx.x + j * 256, nx - 1) * 8);
+    const int n_active = active[0];
+    const int e_raw = active[1 + min(a, E - 1)];
+    const int e_c = min(max(e_raw, 0), E - 1);
+    const uint8_t* pe = (const uint8_t*)expert_ptrs[e_c];
+    const int ce = counts[e_c], oe = offsets[e_c];
+    const bool routed = a < n_active;
+    const uint8_t* blob = routed ? pe : (a == n_active ? shared_blob : nullptr);
+    const int e = routed ? e_raw : -1;
+    const int c = routed ? ce : T, p0 = routed ? oe : T * k;
+    const bool work = blob != nullptr;  // no weights behind this expert: leave its rows untouched
+    const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
+    const __amdgpu_buffer_rsrc_t wr = buf_rsrc(blob, work ? (uint32_t)L.total : 0u);
+    const __amdgpu_buffer_rsrc_t ir = buf_rsrc(sorted_idx, e >= 0 ? (uint32_t)(T * k * 4) : 0u);
+    // slot of each of the first 64 rows (row m of the slot belongs to token slot_of / k)
+    const int slot_of = __builtin_amdgcn_raw_buffer_load_b32(ir, (p0 + min(lane, max(c - 1, 0))) * 4, 0, 0);
+    const uint32_t tile0 = (uint32_t)(strip * (S * NT) + part * NT);
+    const uint32_t og = (uint32_t)L.g.qoff + tile0 * 1024 + lane * 16;
+    const uint32_t ou = (uint32_t)L.u.qoff + tile0 * 1024 + lane * 16;
+    const uint32_t osg = (uint32_t)L.g.soff + tile0 * 128 + (lane & 15) * 8;
+    const uint32_t osu = (uint32_t)L.u.soff + tile0 * 128 + (lane & 15) * 8;
+    auto ld2 = [&](uint32_t off) { return __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(wr, off, 0, 0)); };
+    auto ld4 = [&](uint32_t off) { return __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0)); };
+    uint4v qg[NT], qu[NT];
+    uint2v sg[NT], su[NT];
+#pragma unroll
+    for (int i = 0; i < kPipe && i < NT; ++i) {
+        sg[i] = ld2(osg + i * 128);
+        su[i] = ld2(osu + i * 128);
+        qg[i] = ld4(og + i * 1024);
+        qu[i] = ld4(ou + i * 1024);
+    }
+    // tokens -> LDS as fp16
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int idx = (int)threadIdx.x + j * 256;
+        if (idx < nx) {
+            const int r = idx / XC, cc = idx % XC;
+            xs4[r * XC + (cc ^ r)] = __builtin_bit_cast(uint4, xr[j].cvt());
         }
+    }
+    for (int base = 1024; base < nx; base += 1024) {
+        XChunk<XT> xq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xq[j].load(x + (size_t)min(base + (int)threadIdx.x + j * 256, nx - 1) * 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int idx = base + (int)threadIdx.x + j * 256;
             if (idx < nx) {
-                const int r = idx / XC, c = idx % XC;
-                xs4[r * XC + (c ^ r)] = __builtin_bit_cast(uint4, v[j]);
+                const int r = idx / XC, cc = idx % XC;
+                xs4[r * XC + (cc ^ r)] = __builtin_bit_cast(uint4, xq[j].cvt());
             }
         }
     }
     __syncthreads();
-    const bool work = blob != nullptr;  // no weights behind this expert: leave its rows untouched
     float4v accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-    if (work) {
-        const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
-        const size_t tile0 = (size_t)strip * (S * NT) + part * NT;
-        const uint4v* pg = reinterpret_cast<const uint4v*>(blob + L.g.qoff + tile0 * 1024) + lane;
-        const uint4v* pu = reinterpret_cast<const uint4v*>(blob + L.u.qoff + tile0 * 1024) + lane;
-        const uint2v* psg = reinterpret_cast<const uint2v*>(blob + L.g.soff + tile0 * 128 + (lane & 15) * 8);
-        const uint2v* psu = reinterpret_cast<const uint2v*>(blob + L.u.soff + tile0 * 128 + (lane & 15) * 8);
-        uint4v qg[NT], qu[NT];
-        uint2v sg[NT], su[NT];
-#pragma unroll
-        for (int i = 0; i < kPipe && i < NT; ++i) {
-            sg[i] = gload(psg + i * 16);
-            su[i] = gload(psu + i * 16);
-            qg[i] = gload(pg + i * 64);
-            qu[i] = gload(pu + i * 64);
-        }
+    {
         const int rr = min(lane & 15, T - 1);
         // bit masks and magic in registers so that each extraction is one v_and_or_b32
         uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
@@ -440,10 +498,11 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
             if (i + kPipe < NT) {
-                sg[i + kPipe] = gload(psg + (i + kPipe) * 16);
-                su[i + kPipe] = gload(psu + (i + kPipe) * 16);
-                qg[i + kPipe] = gload(pg + (i + kPipe) * 64);
-                qu[i + kPipe] = gload(pu + (i + kPipe) * 64);
+                const int n = i + kPipe;
+                sg[n] = ld2(osg + n * 128);
+                su[n] = ld2(osu + n * 128);
+                qg[n] = ld4(og + n * 1024);
+                qu[n] = ld4(ou + n * 1024);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -469,11 +528,7 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
     __syncthreads();
     if (!work) return;
     const int w0 = wave - part;
-    int c = T, p0 = T * k;
-    if (e >= 0) {
-        c = counts[e];
-        p0 = offsets[e];
-    }
+    const int col = strip * 16 + (lane & 15);
     // accumulator row r holds token 4 * (lane / 16) + r; wavefront `part` writes rows r = part, part + S, ..
     // to every position of the slot that token t occupies (a token listed twice gets two rows)
 #pragma unroll
@@ -488,10 +543,14 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
         }
         const _Float16 hv = (_Float16)(silu_f(g) * u);
         if (e < 0) {
-            h[(size_t)(p0 + t) * f + strip * 16 + (lane & 15)] = hv;
+            h[(size_t)(p0 + t) * f + col] = hv;
         } else {
-            for (int m = 0; m < c; ++m)
-                if (sorted_idx[p0 + m] / k == t) h[(size_t)(p0 + m) * f + strip * 16 + (lane & 15)] = hv;
+            const unsigned lo = (unsigned)(t * k);
+            const int cm = min(c, 64);
+            for (int m = 0; m < cm; ++m)
+                if ((unsigned)__builtin_amdgcn_readlane(slot_of, m) - lo < (unsigned)k) h[(size_t)(p0 + m) * f + col] = hv;
+            for (int m = 64; m < c; ++m)
+                if (sorted_idx[p0 + m] / k == t) h[(size_t)(p0 + m) * f + col] = hv;
         }
     }
 }
@@ -505,7 +564,7 @@ static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, h
     const dim3 grid(four ? items : (items + 1) / 2);
     const size_t lds = std::max<size_t>((size_t)a->T * a->d * sizeof(_Float16), 4 * 2 * 4 * 64 * sizeof(float));
 #define MOE_GU16(NT, S)                                                                                         \
-    ffn_gateup_tok16<NT, S, XT><<<grid, 256, lds, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs, \
+    ffn_gateup_tok16<NT, S, XT><<<grid, 256, lds, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs, \
                                                        (const uint8_t*)a->shared_blob, a->counts, a->offsets,    \
                                                        a->sorted_idx, a->active, h)
     if (four) {

@@ -52,98 +52,147 @@ __device__ void topk_iterative(double (&v)[NPL], int E, int k, int32_t* zi, doub
     }
 }
 
-// (v1, i1) ranks before (v2, i2): larger logit, then lower index
-__device__ __forceinline__ bool ranks_before(double v1, int i1, double v2, int i2) {
-    return v1 > v2 || (v1 == v2 && i1 < i2);
+// LDS-only synchronisation: orders LDS accesses without waiting for global
+// stores still in flight (a plain barrier would also wait for those).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+__device__ __forceinline__ void block_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One compare-exchange step of a bitonic sort across the wavefront (lane pairs
-// l, l ^ J inside blocks of SIZE lanes; the last stage sorts all 64 into rank order).
-template <int SIZE, int J>
-__device__ __forceinline__ void bitonic_step(double& v, int& i) {
-    const int lane = threadIdx.x & 63;
-    const double pv = lane_xor_d<J>(v);
-    const int pi = (int)lane_xor<J>((uint32_t)i);
-    const bool first = (lane & J) == 0;
-    const bool best_first = SIZE == 64 || (lane & SIZE) == 0;
-    if ((first == best_first) == ranks_before(pv, pi, v, i)) {
-        v = pv;
-        i = pi;
-    }
+// Order-preserving 64-bit key of a finite double: a larger value has a larger
+// key; -0.0 is folded onto +0.0 so that equal values have equal keys.
+__device__ __forceinline__ uint64_t order_key(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double key_value(uint64_t k) {
+    const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+    return __longlong_as_double((long long)b);
+}
+// (k1, i1) ranks before (k2, i2): larger key, then lower index
+__device__ __forceinline__ bool key_before(uint64_t k1, int i1, uint64_t k2, int i2) {
+    return k1 > k2 || (k1 == k2 && i1 < i2);
 }
 
-// Sort one (value, index) pair per lane into rank order (lane 0 = best); indices distinct.
-__device__ __forceinline__ void wave_rank_sort(double& v, int& i) {
-    bitonic_step<2, 1>(v, i);
-    bitonic_step<4, 2>(v, i); bitonic_step<4, 1>(v, i);
-    bitonic_step<8, 4>(v, i); bitonic_step<8, 2>(v, i); bitonic_step<8, 1>(v, i);
-    bitonic_step<16, 8>(v, i); bitonic_step<16, 4>(v, i); bitonic_step<16, 2>(v, i); bitonic_step<16, 1>(v, i);
-    bitonic_step<32, 16>(v, i); bitonic_step<32, 8>(v, i); bitonic_step<32, 4>(v, i); bitonic_step<32, 2>(v, i);
-    bitonic_step<32, 1>(v, i);
-    bitonic_step<64, 32>(v, i); bitonic_step<64, 16>(v, i); bitonic_step<64, 8>(v, i); bitonic_step<64, 4>(v, i);
-    bitonic_step<64, 2>(v, i); bitonic_step<64, 1>(v, i);
-}
+// per-wavefront LDS scratch of the top-k
+struct RankScratch {
+    uint64_t k[64];
+    int32_t i[64];
+    double v[64];
+};
 
-// One wavefront selects the top-k of z[0..E) by (value desc, index asc).
-//  1. every lane's maximum over its values; the lane maxima are sorted across
-//     the wavefront and tau = the kk-th of them, so that every value of the
+// One wavefront selects the top-k of z[0..E) by (value desc, index asc) and
+// forms the softmax over the selected values.  Every rank is found by counting
+// (how many entries rank before this one), which needs no sorting network:
+//  1. every lane's maximum over its values; tau = the k-th largest of the 16
+//     maxima of four-lane groups (or, for k > 16 or E < 64, the kk-th largest
+//     lane maximum).  Those maxima are distinct entries, so every value of the
 //     top k ranks at or before tau;
-//  2. the values ranking at or before tau (usually k..2k) are compacted into LDS;
-//  3. they are sorted across the wavefront; lanes 0..k-1 hold the result.
+//  2. the entries ranking at or before tau (usually 10..20) are compacted into LDS;
+//  3. each candidate counts the candidates ranking before it, which is its rank;
+//     lane r then holds the entry of rank r.
 // More than 64 candidates (heavy ties) fall back to k rounds of wave argmax.
-// scratch: LDS for 64 (value, index) pairs plus k selected pairs.
 template <int NPL>
-__device__ void topk_wave(const double* __restrict__ z, int E, int k, int32_t* __restrict__ ids,
-                          float* __restrict__ gates, int32_t* s_ids, double* cv, int32_t* ci) {
+__device__ void topk_rank(const double* __restrict__ z, int E, int k, int32_t* __restrict__ ids,
+                          float* __restrict__ gates, int32_t* s_ids, RankScratch& S) {
     const int lane = threadIdx.x & 63;
     double v[NPL];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? z[e] : -DBL_MAX;
-    }
-    double lm = v[0];
+    for (int i = 0; i < NPL; ++i) v[i] = z[min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+        if (lane + 64 * i >= E) v[i] = -DBL_MAX;
+    uint64_t key[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) key[i] = order_key(v[i]);
+    uint64_t lk = key[0];  // lane maximum; equal keys keep the lower index
     int li = lane;
 #pragma unroll
     for (int i = 1; i < NPL; ++i) {
         const int e = lane + 64 * i;
-        if (e < E && v[i] > lm) { lm = v[i]; li = e; }  // strict: equal values keep the lower index
+        if (e < E && key[i] > lk) { lk = key[i]; li = e; }
     }
-    if (lane >= E) { lm = -DBL_MAX; li = 0x40000000 + lane; }  // lanes without values rank last
-    wave_rank_sort(lm, li);
+    if (lane >= E) { lk = 0; li = 0x40000000 + lane; }  // lanes without values rank last
     const int nlanes = E < 64 ? E : 64;
-    const int kk = k < nlanes ? k : nlanes;  // with fewer lanes than k, take the weakest lane maximum
-    const double tau = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(lm), kk - 1),
-                                        __builtin_amdgcn_readlane(__double2loint(lm), kk - 1));
-    const int taui = __builtin_amdgcn_readlane(li, kk - 1);
+    uint64_t tk;
+    int ti;
+    if (k <= 16 && nlanes == 64) {
+        // maxima of the 16 groups of four lanes; tau = the k-th largest of them
+#pragma unroll
+        for (int J = 1; J <= 2; J <<= 1) {
+            const uint32_t ohi = J == 1 ? lane_xor<1>((uint32_t)(lk >> 32)) : lane_xor<2>((uint32_t)(lk >> 32));
+            const uint32_t olo = J == 1 ? lane_xor<1>((uint32_t)lk) : lane_xor<2>((uint32_t)lk);
+            const int oi = (int)(J == 1 ? lane_xor<1>((uint32_t)li) : lane_xor<2>((uint32_t)li));
+            const uint64_t ok = ((uint64_t)ohi << 32) | olo;
+            if (key_before(ok, oi, lk, li)) { lk = ok; li = oi; }
+        }
+        if ((lane & 3) == 0) { S.k[lane >> 2] = lk; S.i[lane >> 2] = li; }
+        wave_lds_sync();
+        int r = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) r += key_before(S.k[j], S.i[j], lk, li) ? 1 : 0;
+        const unsigned long long tb = __ballot((lane & 3) == 0 && r == k - 1);
+        const int tl = __builtin_ctzll(tb);
+        tk = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(lk >> 32), tl) << 32) |
+             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lk, tl);
+        ti = __builtin_amdgcn_readlane(li, tl);
+    } else {
+        S.k[lane] = lk;
+        S.i[lane] = li;
+        wave_lds_sync();
+        int r = 0;
+#pragma unroll 8
+        for (int j = 0; j < 64; ++j) r += key_before(S.k[j], S.i[j], lk, li) ? 1 : 0;
+        const int kk = k < nlanes ? k : nlanes;  // with fewer lanes than k, the weakest lane maximum
+        const unsigned long long tb = __ballot(r == kk - 1);
+        const int tl = __builtin_ctzll(tb);
+        tk = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(lk >> 32), tl) << 32) |
+             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lk, tl);
+        ti = __builtin_amdgcn_readlane(li, tl);
+    }
+    __builtin_amdgcn_wave_barrier();
     const unsigned long long lt = (1ull << lane) - 1ull;
     int base = 0;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
-        const bool c = e < E && (e == taui || ranks_before(v[i], e, tau, taui));
+        const bool c = e < E && !key_before(tk, ti, key[i], e);
         const unsigned long long b = __ballot(c);
         const int pos = base + __popcll(b & lt);
-        if (c && pos < 64) { cv[pos] = v[i]; ci[pos] = e; }
+        if (c && pos < 64) { S.k[pos] = key[i]; S.i[pos] = e; }
         base += __popcll(b);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
+    wave_lds_sync();
     double sv;
     int si;
     if (base <= 64) {
-        sv = lane < base ? cv[lane] : -DBL_MAX;
-        si = lane < base ? ci[lane] : 0x40000000 + lane;
-        wave_rank_sort(sv, si);
+        const uint64_t ck = lane < base ? S.k[lane] : 0;
+        const int ci = lane < base ? S.i[lane] : 0x40000000 + lane;
+        if (lane >= base) { S.k[lane] = 0; S.i[lane] = 0x40000000 + lane; }  // rank after every candidate
+        wave_lds_sync();
+        int cr = 0;
+        for (int j = 0; j < base; j += 4) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) cr += key_before(S.k[j + q], S.i[j + q], ck, ci) ? 1 : 0;
+        }
+        wave_lds_sync();
+        if (lane < base && cr < 64) { S.v[cr] = key_value(ck); S.i[cr] = ci; }
+        wave_lds_sync();
+        sv = lane < k ? S.v[lane] : -DBL_MAX;
+        si = lane < k ? S.i[lane] : 0;
     } else {
-        double* zv = cv + 64;  // selected values [k]
-        int32_t* zi = ci + 64; // selected indices [k]
-        topk_iterative<NPL>(v, E, k, zi, zv);
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_s_waitcnt(0);
-        sv = lane < k ? zv[lane] : -DBL_MAX;
-        si = lane < k ? zi[lane] : 0;
+        topk_iterative<NPL>(v, E, k, S.i, S.v);
+        wave_lds_sync();
+        sv = lane < k ? S.v[lane] : -DBL_MAX;
+        si = lane < k ? S.i[lane] : 0;
     }
+    // lane r holds rank r: the softmax terms are summed in rank order
     const double z0 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(sv), 0),
                                        __builtin_amdgcn_readlane(__double2loint(sv), 0));
     const double p = lane < k ? exp(sv - z0) : 0.0;
@@ -155,34 +204,17 @@ __device__ void topk_wave(const double* __restrict__ z, int E, int k, int32_t* _
     }
 }
 
-// per-wavefront LDS scratch of topk_wave: 64 + 64 candidates/selected pairs
-struct TopkScratch {
-    double v[128];
-    int32_t i[128];
-};
+// values per lane for E experts (E <= 1024)
+inline int topk_npl(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16; }
 
 template <int NPL>
-__device__ void topk_token(const double* z, int E, int k, int32_t* ids, float* gates, int32_t* s_ids,
-                           TopkScratch& S) {
-    topk_wave<NPL>(z, E, k, ids, gates, s_ids, S.v, S.i);
-}
-
-__device__ void topk_dispatch(const double* z, int E, int k, int32_t* ids, float* gates, int32_t* s_ids,
-                              TopkScratch& S) {
-    if (E <= 64) topk_token<1>(z, E, k, ids, gates, s_ids, S);
-    else if (E <= 128) topk_token<2>(z, E, k, ids, gates, s_ids, S);
-    else if (E <= 256) topk_token<4>(z, E, k, ids, gates, s_ids, S);
-    else if (E <= 512) topk_token<8>(z, E, k, ids, gates, s_ids, S);
-    else topk_token<16>(z, E, k, ids, gates, s_ids, S);
-}
-
 __global__ __launch_bounds__(256) void route_topk(const double* __restrict__ logits, int T, int E, int k,
                                                   int32_t* __restrict__ ids, float* __restrict__ gates) {
-    __shared__ TopkScratch sc[4];
+    __shared__ RankScratch sc[4];
     const int wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
-    topk_dispatch(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, nullptr, sc[wave]);
+    topk_rank<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, nullptr, sc[wave]);
 }
 
 // ------------------------------------------------- block-level permutation ----
@@ -356,69 +388,56 @@ __global__ __launch_bounds__(256) void route_logits_rows(const XT* __restrict__ 
     }
 }
 
-// ascending bitonic sort of one 32-bit key per lane
-template <int SIZE, int J>
-__device__ __forceinline__ void bitonic_step_u(uint32_t& v) {
-    const int lane = threadIdx.x & 63;
-    const uint32_t pv = lane_xor<J>(v);
-    const bool first = (lane & J) == 0;
-    const bool asc = SIZE == 64 || (lane & SIZE) == 0;
-    const uint32_t lo = pv < v ? pv : v, hi = pv < v ? v : pv;
-    v = (first == asc) ? lo : hi;
-}
-__device__ __forceinline__ void wave_sort_u32(uint32_t& v) {
-    bitonic_step_u<2, 1>(v);
-    bitonic_step_u<4, 2>(v); bitonic_step_u<4, 1>(v);
-    bitonic_step_u<8, 4>(v); bitonic_step_u<8, 2>(v); bitonic_step_u<8, 1>(v);
-    bitonic_step_u<16, 8>(v); bitonic_step_u<16, 4>(v); bitonic_step_u<16, 2>(v); bitonic_step_u<16, 1>(v);
-    bitonic_step_u<32, 16>(v); bitonic_step_u<32, 8>(v); bitonic_step_u<32, 4>(v); bitonic_step_u<32, 2>(v);
-    bitonic_step_u<32, 1>(v);
-    bitonic_step_u<64, 32>(v); bitonic_step_u<64, 16>(v); bitonic_step_u<64, 8>(v); bitonic_step_u<64, 4>(v);
-    bitonic_step_u<64, 2>(v); bitonic_step_u<64, 1>(v);
-}
-
 // Stable grouping of n <= 64 slots (ids in LDS) by one 256-thread workgroup:
-// wavefront 0 sorts the keys (id << 10 | slot), which yields sorted_idx, dest
-// and the active list directly; then every thread counts, for its experts, the
-// sorted keys below each expert's key range (offsets) and inside it (counts).
-// Ids outside [0, E) are ignored.  Same outputs as block_permute.
-__device__ void small_permute64(const int32_t* s_ids, int n, int E, int32_t* counts, int32_t* offsets,
-                                int32_t* sorted_idx, int32_t* dest, int32_t* active, uint32_t* s_keys) {
+// wavefront 0 ranks the keys (id << 10 | slot) by counting, which gives
+// sorted_idx, dest and the active list; then every thread finds, for its
+// experts, the bounds of each expert's key range in the sorted keys (binary
+// search): offsets and counts.  Ids outside [0, E) are ignored.  Same outputs
+// as block_permute.
+__device__ void permute_rank64(const int32_t* s_ids, int n, int E, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_idx, int32_t* dest, int32_t* active, uint32_t* s_keys,
+                               uint32_t* s_sorted) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         const int id = lane < n ? s_ids[lane] : -1;
         const bool valid = (unsigned)id < (unsigned)E;
-        uint32_t key = valid ? ((uint32_t)id << 10) | (uint32_t)lane : 0xFFFFFFFFu;
-        wave_sort_u32(key);
+        const uint32_t key = valid ? ((uint32_t)id << 10) | (uint32_t)lane : 0xFFFFFFFFu;
         s_keys[lane] = key;
-        const bool kv = key != 0xFFFFFFFFu;
-        if (kv) {
-            const int slot = (int)(key & 1023u);
-            sorted_idx[lane] = slot;
-            dest[slot] = lane;
+        s_sorted[lane] = 0xFFFFFFFFu;
+        s_sorted[64 + lane] = 0xFFFFFFFFu;
+        wave_lds_sync();
+        int pos = 0;  // keys of invalid slots are 0xFFFFFFFF and never count
+#pragma unroll
+        for (int j = 0; j < 64; j += 4) {
+            const uint4 kv = *reinterpret_cast<const uint4*>(&s_keys[j]);
+            pos += (kv.x < key) + (kv.y < key) + (kv.z < key) + (kv.w < key);
         }
-        const int kid = (int)(key >> 10);
-        const int pid = __shfl_up(kid, 1);
+        if (valid) {
+            sorted_idx[pos] = lane;
+            dest[lane] = pos;
+            s_sorted[pos] = key;
+        }
+        wave_lds_sync();
+        const uint32_t sk = s_sorted[lane];
+        const bool kv = sk != 0xFFFFFFFFu;
+        const int kid = (int)(sk >> 10);
+        const int pid = lane > 0 ? (int)(s_sorted[lane - 1] >> 10) : -1;
         const bool first = kv && (lane == 0 || pid != kid);
         const unsigned long long fb = __ballot(first);
         if (first) active[1 + __popcll(fb & ((1ull << lane) - 1ull))] = kid;
         if (lane == 0) active[0] = __popcll(fb);
     }
-    __syncthreads();
-    uint32_t keys[64];
+    block_lds_sync();
+    // lower bound of a key in the sorted keys (padded to 128 with 0xFFFFFFFF)
+    auto lower_bound = [&](uint32_t key) {
+        int pos = 0;
 #pragma unroll
-    for (int q = 0; q < 64; q += 4) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(&s_keys[q]);
-        keys[q] = kv.x; keys[q + 1] = kv.y; keys[q + 2] = kv.z; keys[q + 3] = kv.w;
-    }
+        for (int step = 64; step >= 1; step >>= 1) pos += s_sorted[pos + step - 1] < key ? step : 0;
+        return pos;
+    };
     for (int e = threadIdx.x; e < E; e += 256) {
-        const uint32_t lo = (uint32_t)e << 10, hi = (uint32_t)(e + 1) << 10;
-        int below = 0, upto = 0;
-#pragma unroll
-        for (int q = 0; q < 64; ++q) {
-            below += keys[q] < lo;
-            upto += keys[q] < hi;
-        }
+        const int below = lower_bound((uint32_t)e << 10);
+        const int upto = lower_bound((uint32_t)(e + 1) << 10);
         counts[e] = upto - below;
         offsets[e] = below;
         if (e == E - 1) offsets[E] = upto;
@@ -427,25 +446,27 @@ __device__ void small_permute64(const int32_t* s_ids, int n, int E, int32_t* cou
 
 // One workgroup: top-k of every token (T <= kSmallSlots / k) and, when asked,
 // the grouping of the routing slots by expert.
+template <int NPL>
 __global__ __launch_bounds__(256) void route_select_small(const double* __restrict__ logits, int T, int E, int k,
                                                           int32_t* __restrict__ ids, float* __restrict__ gates,
                                                           int do_permute, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_idx,
                                                           int32_t* __restrict__ dest, int32_t* __restrict__ active) {
-    __shared__ TopkScratch sc[4];
+    __shared__ RankScratch sc[4];
     __shared__ int32_t s_ids[kSmallSlots];
     __shared__ int32_t s_cnt[1024];
     __shared__ int32_t s_part[256], s_flag[256];
     __shared__ __align__(16) uint32_t s_keys[64];
+    __shared__ __align__(16) uint32_t s_sorted[128];
     const int wave = threadIdx.x >> 6;
     for (int t = wave; t < T; t += 4)
-        topk_dispatch(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, s_ids + t * k,
-                      sc[wave]);
-    __syncthreads();
+        topk_rank<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, s_ids + t * k,
+                       sc[wave]);
+    block_lds_sync();
     if (do_permute) {
         if (T * k <= 64)
-            small_permute64(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_keys);
+            permute_rank64(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_keys, s_sorted);
         else
             block_permute(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_cnt, s_part, s_flag);
     }
@@ -607,8 +628,17 @@ int launch_route_small(const void* x, int x_dtype, int T, int d, const float* Wr
                        int32_t* offsets, int32_t* sorted_idx, int32_t* dest, int32_t* active, hipStream_t s) {
     int rc = launch_logits(x, x_dtype, T, d, Wr, bias, E, logits, s);
     if (rc) return rc;
-    route_select_small<<<1, 256, 0, s>>>(logits, T, E, k, ids, gates, do_permute, counts, offsets, sorted_idx,
-                                         dest, active);
+#define MOE_SEL(NPL)                                                                                       \
+    route_select_small<NPL><<<1, 256, 0, s>>>(logits, T, E, k, ids, gates, do_permute, counts, offsets, sorted_idx, \
+                                              dest, active)
+    switch (topk_npl(E)) {
+    case 1: MOE_SEL(1); break;
+    case 2: MOE_SEL(2); break;
+    case 4: MOE_SEL(4); break;
+    case 8: MOE_SEL(8); break;
+    default: MOE_SEL(16); break;
+    }
+#undef MOE_SEL
     return check_launch();
 }
 
@@ -620,7 +650,14 @@ int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, cons
                                   nullptr, nullptr, nullptr, s);
     int rc = launch_logits(x, x_dtype, T, d, Wr, bias, E, logits, s);
     if (rc) return rc;
-    route_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, ids, gates);
+    const dim3 grid((T + 3) / 4);
+    switch (topk_npl(E)) {
+    case 1: route_topk<1><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
+    case 2: route_topk<2><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
+    case 4: route_topk<4><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
+    case 8: route_topk<8><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
+    default: route_topk<16><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
+    }
     return check_launch();
 }
 
