@@ -336,7 +336,8 @@ __global__ __launch_bounds__(256) void ffn_q8_down(const int8_t* __restrict__ hq
 // each) by n-tiles (w & 1) and 2 + (w & 1) (gate and up rows of the same 32
 // features, or two halves of the output rows), so SwiGLU needs no exchange.
 // Work items of one tile share blockIdx % 8, i.e. one XCD and its L2, which
-// then serves the tile's activation rows to all of them.  The per-block
+// then serves the tile's activation rows to all of them.  The next chunk is
+// read into registers while the current one is multiplied.  The per-block
 // arithmetic (magic-seeded int32 MFMA, t = sw * P, acc += sa * t, blocks in
 // order) is the same as above, so the results are identical.
 constexpr int kTM = 6;     // m-tiles of 32 tokens per tile (192 rows)
@@ -498,10 +499,13 @@ __global__ __launch_bounds__(256) void ffn_q8_tiled(const int8_t* __restrict__ a
     const int mt0 = 3 * (wave >> 1);
     const int nt0 = MODE == 0 ? (wave & 1) : 2 * (wave & 1);
     const int nt1 = MODE == 0 ? 2 + (wave & 1) : 2 * (wave & 1) + 1;
-    const int16v cmagic = {(int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
-                           (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
-                           (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
-                           (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits};
+    // the magic accumulator seed is made opaque so that it stays in registers
+    // instead of being rebuilt before every MFMA
+    int16v cmagic = {(int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
+                     (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
+                     (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
+                     (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits};
+    asm volatile("" : "+v"(cmagic));
     float16v acc[3][2];
 #pragma unroll
     for (int m = 0; m < 3; ++m)
@@ -510,11 +514,13 @@ __global__ __launch_bounds__(256) void ffn_q8_tiled(const int8_t* __restrict__ a
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
     const int nkc = K / kTKC;
+    load_chunk(0);
     for (int c = 0; c < nkc; ++c) {
         if (c > 0) __syncthreads();  // the previous chunk is no longer read
-        load_chunk(c);
         store_chunk();
         __syncthreads();
+        if (c + 1 < nkc) load_chunk(c + 1);  // the next chunk is in flight during the products
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int kq = 2 * b + (lane >> 5);  // 16-byte chunk holding this lane's 16 k of block b

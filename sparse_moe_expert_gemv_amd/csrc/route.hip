@@ -472,54 +472,108 @@ __global__ __launch_bounds__(256) void route_select_small(const double* __restri
     }
 }
 
-// General T: 64 tokens x 64 experts per workgroup, 4x4 outputs per thread,
-// operands staged in LDS as double.
-constexpr int RT = 64, RE = 64, RK = 16;
+// ------------------------------------------------ large batches: fp64 MFMA ----
+// Workgroup tile: 64 tokens x 128 router rows; wavefront w computes the 32 x 64
+// quadrant ((w / 2) * 32, (w % 2) * 64) as 2 x 4 tiles of v_mfma_f64_16x16x4
+// (lane l holds A row l % 16 and B column l % 16 at k = l / 16; accumulator
+// register r of lane l is row 4 r + l / 16, column l % 16).  k advances in
+// chunks of 32: the next chunk is read into registers while the current one is
+// multiplied, then stored to LDS as double, k-major with padded rows, so that a
+// fragment read is 16 consecutive doubles per k.  Products of fp32/bf16 inputs
+// are exact in double; the sums are double.
+constexpr int LT = 64, LE = 128, LK = 32, LPT = LT + 16, LPE = LE + 16;
+typedef double double4v __attribute__((ext_vector_type(4)));
 template <typename XT>
-__global__ __launch_bounds__(256) void route_logits_tiled(const XT* __restrict__ x, int T, int d,
-                                                          const float* __restrict__ Wr,
-                                                          const float* __restrict__ bias, int E,
-                                                          double* __restrict__ logits) {
-    __shared__ double xs[RK][RT + 1];
-    __shared__ double ws[RK][RE + 1];
-    const int t0 = blockIdx.y * RT, e0 = blockIdx.x * RE;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    double acc[4][4];
+__global__ __launch_bounds__(256) void route_logits_mfma(const XT* __restrict__ x, int T, int d,
+                                                         const float* __restrict__ Wr,
+                                                         const float* __restrict__ bias, int E,
+                                                         double* __restrict__ logits) {
+    __shared__ double xs[LK][LPT];
+    __shared__ double ws[LK][LPE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.y * LT, e0 = blockIdx.x * LE;
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
+    // staging: token row tid / 4 (8 consecutive k at 8 (tid % 4)); router row
+    // tid / 2 (16 consecutive k at 16 (tid % 2)); rows past the end repeat the last
+    const int xr = tid >> 2, xk = (tid & 3) * 8;
+    const int wrow = tid >> 1, wk = (tid & 1) * 16;
+    const XT* xp = x + (size_t)min(t0 + xr, T - 1) * d + xk;
+    const float* wp = Wr + (size_t)min(e0 + wrow, E - 1) * d + wk;
+    constexpr int XU = sizeof(XT) == 4 ? 2 : 1;
+    uint4 xraw[XU];
+    float4 wraw[4];
+    auto load_chunk = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < XU; ++j) xraw[j] = reinterpret_cast<const uint4*>(xp + k0)[j];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    for (int k0 = 0; k0 < d; k0 += RK) {
-        for (int idx = threadIdx.x; idx < RK * RT; idx += 256) {
-            const int kk = idx % RK, r = idx / RK;
-            const int t = t0 + r, e = e0 + r;
-            xs[kk][r] = t < T ? (double)load_xf(x, (size_t)t * d + k0 + kk) : 0.0;
-            ws[kk][r] = e < E ? (double)Wr[(size_t)e * d + k0 + kk] : 0.0;
+        for (int j = 0; j < 4; ++j) wraw[j] = reinterpret_cast<const float4*>(wp + k0)[j];
+    };
+    auto store_chunk = [&]() {
+        double xv[8];
+        if constexpr (sizeof(XT) == 4) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                xv[4 * j] = __uint_as_float(xraw[j].x);
+                xv[4 * j + 1] = __uint_as_float(xraw[j].y);
+                xv[4 * j + 2] = __uint_as_float(xraw[j].z);
+                xv[4 * j + 3] = __uint_as_float(xraw[j].w);
+            }
+        } else {
+            const uint32_t w[4] = {xraw[0].x, xraw[0].y, xraw[0].z, xraw[0].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                xv[2 * q] = __uint_as_float(w[q] << 16);
+                xv[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+            }
         }
-        __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < RK; ++kk) {
-            double a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + ty * 4 + i;
-        if (t >= T) continue;
+        for (int j = 0; j < 8; ++j) xs[xk + j][xr] = xv[j];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int e = e0 + tx * 4 + j;
-            if (e < E) logits[(size_t)t * E + e] = acc[i][j] + (bias ? (double)bias[e] : 0.0);
+            ws[wk + 4 * j][wrow] = wraw[j].x;
+            ws[wk + 4 * j + 1][wrow] = wraw[j].y;
+            ws[wk + 4 * j + 2][wrow] = wraw[j].z;
+            ws[wk + 4 * j + 3][wrow] = wraw[j].w;
         }
+    };
+    double4v acc[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = double4v{0.0, 0.0, 0.0, 0.0};
+    load_chunk(0);
+    for (int k0 = 0; k0 < d; k0 += LK) {
+        __syncthreads();  // the previous chunk's fragments have been read
+        store_chunk();
+        __syncthreads();
+        if (k0 + LK < d) load_chunk(k0 + LK);
+#pragma unroll
+        for (int ks = 0; ks < LK; ks += 4) {
+            const int kr = ks + (lane >> 4);
+            double a[2], b[4];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) a[mt] = xs[kr][wm + 16 * mt + (lane & 15)];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) b[nt] = ws[kr][wn + 16 * nt + (lane & 15)];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int e = e0 + wn + 16 * nt + (lane & 15);
+        if (e >= E) continue;
+        const double be = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = t0 + wm + 16 * mt + 4 * r + (lane >> 4);
+                if (t < T) logits[(size_t)t * E + e] = acc[mt][nt][r] + be;
+            }
     }
 }
 
@@ -614,11 +668,11 @@ static int launch_logits(const void* x, int x_dtype, int T, int d, const float* 
         else
             route_logits_rows<uint16_t><<<grid, 256, lds, s>>>((const uint16_t*)x, T, d, Wr, bias, E, logits);
     } else {
-        dim3 grid((E + RE - 1) / RE, (T + RT - 1) / RT);
+        const dim3 grid((E + LE - 1) / LE, (T + LT - 1) / LT);
         if (x_dtype == MOE_DT_F32)
-            route_logits_tiled<float><<<grid, 256, 0, s>>>((const float*)x, T, d, Wr, bias, E, logits);
+            route_logits_mfma<float><<<grid, 256, 0, s>>>((const float*)x, T, d, Wr, bias, E, logits);
         else
-            route_logits_tiled<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)x, T, d, Wr, bias, E, logits);
+            route_logits_mfma<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)x, T, d, Wr, bias, E, logits);
     }
     return check_launch();
 }
