@@ -403,6 +403,12 @@ template <> struct XChunk<float> {
     }
 };
 
+template <> struct XChunk<_Float16> {
+    uint4v r;
+    __device__ __forceinline__ void load(const _Float16* p) { r = gload(reinterpret_cast<const uint4v*>(p)); }
+    __device__ __forceinline__ half8 cvt() const { return __builtin_bit_cast(half8, r); }
+};
+
 // Buffer resource over [base, base + bytes): loads through it are bounds
 // checked and return zeros outside the range (bytes = 0: nothing is read).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
@@ -717,6 +723,308 @@ static bool launch_down_tok16(const moe_ffn_args* a, const _Float16* h, int slot
 
 size_t float_h_bytes(int T, int f, int k) { return ((size_t)T * k + T) * (size_t)f * sizeof(_Float16); }
 
+// ---- moderate batches (T <= 64): token-dense gate/up, slot-dense down --------
+// Gate/up: every token is a row of the MFMA A operand (four 16-token m-tiles;
+// rows >= T repeat the last token and are discarded).  A workgroup takes
+// (slot, 64 rows of f): wavefront w owns the 16-row strip 4 g + w and streams
+// its quant tiles through registers kPipe chunks ahead, while all four stage
+// the tokens of the current 128-wide k-chunk in LDS as fp16 (double buffered).
+// Each weight is read once and serves every token; the block-scaled weights
+// accumulate in the MFMA as in the small-batch kernel.  The results go to LDS
+// as [token][16 features] and are scattered to the slot's rows from there.
+// Down: the same streaming over f for (slot, 64 output rows), with the slot's
+// h rows (contiguous, at most 64 per pass) as the A operand.
+constexpr int kTok64 = 64;
+constexpr int kKC = 128;     // k per chunk
+constexpr int kPipe64 = 4;   // gate/up chunks in flight ahead of the products (few workgroups: registers are free)
+
+// (q) * s for the 8 int8 weights of one block (two dwords in k order, q stored
+// as q + 128): bytes are paired with the 0x64 magic byte by v_perm_b32
+// (1024 + q + 128 exactly), the offset is removed and the block scale applied
+// with one rounding.
+__device__ __forceinline__ half8 dequant8_scaled(uint32_t v0, uint32_t v1, half2v s2, uint32_t magic) {
+    const half2v m1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const half2v p0 = as_h2(__builtin_amdgcn_perm(magic, v0, 0x04010400u)) + m1152;
+    const half2v p1 = as_h2(__builtin_amdgcn_perm(magic, v0, 0x04030402u)) + m1152;
+    const half2v p2 = as_h2(__builtin_amdgcn_perm(magic, v1, 0x04010400u)) + m1152;
+    const half2v p3 = as_h2(__builtin_amdgcn_perm(magic, v1, 0x04030402u)) + m1152;
+    const half2v q0 = p0 * s2, q1 = p1 * s2, q2 = p2 * s2, q3 = p3 * s2;
+    return half8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+}
+
+// Quant tiles of one strip for one 128-k chunk: TPC packed tiles of one matrix.
+template <int WFMT>
+struct StripChunk {
+    static constexpr int TPC = WFMT == MOE_WFMT_I4B32 ? 1 : 2;
+    uint4v q[TPC];
+    uint2v s[TPC];  // int4: four fp16 block scales; int8: two (.x)
+};
+
+template <int WFMT>
+__device__ __forceinline__ void load_strip_chunk(StripChunk<WFMT>& w, __amdgpu_buffer_rsrc_t r, uint32_t qoff,
+                                                 uint32_t soff, uint32_t tile, int lane) {
+    constexpr int TPC = StripChunk<WFMT>::TPC;
+#pragma unroll
+    for (int j = 0; j < TPC; ++j) {
+        w.q[j] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(r, qoff + (tile + j) * 1024 + lane * 16, 0, 0));
+        if constexpr (WFMT == MOE_WFMT_I4B32)
+            w.s[j] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(r, soff + (tile + j) * 128 + (lane & 15) * 8, 0, 0));
+        else
+            w.s[j] = uint2v{(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, soff + (tile + j) * 64 + (lane & 15) * 4, 0, 0), 0u};
+    }
+}
+
+// scaled fp16 weights of block b (0..3) of a 128-k chunk
+template <int WFMT>
+__device__ __forceinline__ half8 strip_block(const StripChunk<WFMT>& w, int b, uint32_t mlo, uint32_t mhi,
+                                             uint32_t magic) {
+    if constexpr (WFMT == MOE_WFMT_I4B32) {
+        return dequant4_scaled(w.q[0][b], scale_pair(w.s[0], b), mlo, mhi, magic);
+    } else {
+        const int j = b >> 1, bb = b & 1;
+        const uint32_t sw = w.s[j][0];
+        const uint32_t hb = bb ? (sw >> 16) : (sw & 0xFFFFu);
+        return dequant8_scaled(w.q[j][2 * bb], w.q[j][2 * bb + 1], as_h2(hb | (hb << 16)), 0x64646464u);
+    }
+}
+
+// token rows of one 128-k chunk -> LDS (fp16; 16-byte piece c of row r at c ^ (r & 15))
+template <typename XT>
+struct RowChunk {
+    XChunk<XT> v[4];
+    __device__ __forceinline__ void load(const XT* base, int ld, int nrows, int k0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int piece = (int)threadIdx.x + 256 * j, row = piece >> 4, ch = piece & 15;
+            v[j].load(base + (size_t)min(row, nrows - 1) * ld + k0 + 8 * ch);
+        }
+    }
+    __device__ __forceinline__ void store(uint4 (*dst)[kKC / 8]) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int piece = (int)threadIdx.x + 256 * j, row = piece >> 4, ch = piece & 15;
+            dst[row][ch ^ (row & 15)] = __builtin_bit_cast(uint4, v[j].cvt());
+        }
+    }
+};
+
+template <int WFMT, typename XT, int NCH>
+__global__ __launch_bounds__(256) void ffn_gateup_tok64(const XT* __restrict__ x, int T, int d, int f, int k, int E,
+                                                        const void* const* __restrict__ expert_ptrs,
+                                                        const uint8_t* __restrict__ shared_blob,
+                                                        const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ sorted_idx,
+                                                        const int32_t* __restrict__ active, _Float16* __restrict__ h) {
+    constexpr int TPC = StripChunk<WFMT>::TPC;
+    __shared__ uint4 xs[2][kTok64][kKC / 8];
+    __shared__ _Float16 hv_s[4][kTok64][16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_groups = f / 64;
+    const int a = blockIdx.x / n_groups, strip = (blockIdx.x % n_groups) * 4 + wave;
+    RowChunk<XT> xr;
+    xr.load(x, d, T, 0);
+    const int n_active = active[0];
+    const int e_raw = active[1 + min(a, E - 1)];
+    const int e_c = min(max(e_raw, 0), E - 1);
+    const uint8_t* pe = (const uint8_t*)expert_ptrs[e_c];
+    const int ce = counts[e_c], oe = offsets[e_c];
+    const bool routed = a < n_active;
+    const uint8_t* blob = routed ? pe : (a == n_active ? shared_blob : nullptr);
+    if (blob == nullptr) return;  // past the last slot, or no weights behind this expert (uniform per workgroup)
+    const int c = routed ? ce : T, p0 = routed ? oe : T * k;
+    const ExpertLayout L = expert_layout(WFMT, d, f);
+    const __amdgpu_buffer_rsrc_t wr = buf_rsrc(blob, (uint32_t)L.total);
+    const __amdgpu_buffer_rsrc_t ir = buf_rsrc(sorted_idx, routed ? (uint32_t)(T * k * 4) : 0u);
+    // token of each of the slot's first 64 rows (routed) or the row itself (shared)
+    const int slot_of = __builtin_amdgcn_raw_buffer_load_b32(ir, (p0 + min(lane, max(c - 1, 0))) * 4, 0, 0);
+    const uint32_t tile0 = (uint32_t)strip * (uint32_t)(NCH * TPC);
+    StripChunk<WFMT> wg[NCH], wu[NCH];
+#pragma unroll
+    for (int i = 0; i < kPipe64 && i < NCH; ++i) {
+        load_strip_chunk<WFMT>(wg[i], wr, (uint32_t)L.g.qoff, (uint32_t)L.g.soff, tile0 + i * TPC, lane);
+        load_strip_chunk<WFMT>(wu[i], wr, (uint32_t)L.u.qoff, (uint32_t)L.u.soff, tile0 + i * TPC, lane);
+    }
+    xr.store(xs[0]);
+    __syncthreads();
+    uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+    asm volatile("" : "+s"(mlo), "+s"(mhi), "+v"(magic));
+    float4v accg[4], accu[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) accg[mt] = accu[mt] = float4v{0, 0, 0, 0};
+    const int rsel = lane & 15;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        if (i + 1 < NCH) xr.load(x, d, T, (i + 1) * kKC);
+        if (i + kPipe64 < NCH) {
+            load_strip_chunk<WFMT>(wg[i + kPipe64], wr, (uint32_t)L.g.qoff, (uint32_t)L.g.soff, tile0 + (i + kPipe64) * TPC, lane);
+            load_strip_chunk<WFMT>(wu[i + kPipe64], wr, (uint32_t)L.u.qoff, (uint32_t)L.u.soff, tile0 + (i + kPipe64) * TPC, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const half8 Bg = strip_block<WFMT>(wg[i], b, mlo, mhi, magic);
+            const half8 Bu = strip_block<WFMT>(wu[i], b, mlo, mhi, magic);
+            const int ch = 4 * b + (lane >> 4);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int row = 16 * mt + rsel;
+                const half8 A = __builtin_bit_cast(half8, xs[i & 1][row][ch ^ (row & 15)]);
+                accg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bg, accg[mt], 0, 0, 0);
+                accu[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bu, accu[mt], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < NCH) {
+            xr.store(xs[(i + 1) & 1]);
+            __syncthreads();
+        }
+    }
+    // h = silu(g) * u by token, through LDS, then to every row of the slot
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hv_s[wave][16 * mt + 4 * (lane >> 4) + r][lane & 15] = (_Float16)(silu_f(accg[mt][r]) * accu[mt][r]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    const int col = strip * 16 + (lane & 15);
+    const int tok_lane = routed ? slot_of / k : lane;  // token of row `lane` of the slot
+    for (int m0 = 0; m0 < c; m0 += 4) {
+        const int m = m0 + (lane >> 4);
+        int t;
+        if (m < 64) t = __shfl(tok_lane, m);
+        else t = routed ? sorted_idx[p0 + min(m, c - 1)] / k : m;
+        if (m < c) h[(size_t)(p0 + m) * f + col] = hv_s[wave][t][lane & 15];
+    }
+}
+
+template <int WFMT, typename YT, int NCH>
+__global__ __launch_bounds__(256) void ffn_down_tok64(const _Float16* __restrict__ h, int T, int d, int f, int k,
+                                                      int E, const void* const* __restrict__ expert_ptrs,
+                                                      const uint8_t* __restrict__ shared_blob,
+                                                      const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ active, YT* __restrict__ y_perm,
+                                                      float* __restrict__ y_shared) {
+    constexpr int TPC = StripChunk<WFMT>::TPC;
+    __shared__ uint4 hs[2][kTok64][kKC / 8];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_groups = d / 64;
+    const int a = blockIdx.x / n_groups, strip = (blockIdx.x % n_groups) * 4 + wave;
+    const int n_active = active[0];
+    const int e_raw = active[1 + min(a, E - 1)];
+    const int e_c = min(max(e_raw, 0), E - 1);
+    const uint8_t* pe = (const uint8_t*)expert_ptrs[e_c];
+    const int ce = counts[e_c], oe = offsets[e_c];
+    const bool routed = a < n_active;
+    const uint8_t* blob = routed ? pe : (a == n_active ? shared_blob : nullptr);
+    if (blob == nullptr) return;
+    const int c = routed ? ce : T, p0 = routed ? oe : T * k;
+    if (c <= 0) return;
+    const ExpertLayout L = expert_layout(WFMT, d, f);
+    const __amdgpu_buffer_rsrc_t wr = buf_rsrc(blob, (uint32_t)L.total);
+    const uint32_t tile0 = (uint32_t)strip * (uint32_t)(NCH * TPC);
+    uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+    asm volatile("" : "+s"(mlo), "+s"(mhi), "+v"(magic));
+    const int rsel = lane & 15;
+    const int col = strip * 16 + (lane & 15);
+    // passes of 64 slot rows (more than 64 only when a token lists an expert twice)
+    for (int m0 = 0; m0 < c; m0 += kTok64) {
+        const int nr = min(kTok64, c - m0);
+        const _Float16* hb = h + (size_t)(p0 + m0) * f;
+        RowChunk<_Float16> hr;
+        hr.load(hb, f, nr, 0);
+        StripChunk<WFMT> w[NCH];
+#pragma unroll
+        for (int i = 0; i < kPipe && i < NCH; ++i)
+            load_strip_chunk<WFMT>(w[i], wr, (uint32_t)L.dn.qoff, (uint32_t)L.dn.soff, tile0 + i * TPC, lane);
+        if (m0 > 0) __syncthreads();  // the previous pass no longer reads the staging buffers
+        hr.store(hs[0]);
+        __syncthreads();
+        float4v acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = float4v{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            if (i + 1 < NCH) hr.load(hb, f, nr, (i + 1) * kKC);
+            if (i + kPipe < NCH)
+                load_strip_chunk<WFMT>(w[i + kPipe], wr, (uint32_t)L.dn.qoff, (uint32_t)L.dn.soff, tile0 + (i + kPipe) * TPC, lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const half8 Bw = strip_block<WFMT>(w[i], b, mlo, mhi, magic);
+                const int ch = 4 * b + (lane >> 4);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {  // all four m-tiles: rows past the slot repeat its last row
+                    const int row = 16 * mt + rsel;
+                    const half8 A = __builtin_bit_cast(half8, hs[i & 1][row][ch ^ (row & 15)]);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bw, acc[mt], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // one block's A fragments live at a time
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < NCH) {
+                hr.store(hs[(i + 1) & 1]);
+                __syncthreads();
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * mt + 4 * (lane >> 4) + r;
+                if (m >= nr) continue;
+                if (routed) y_perm[(size_t)(p0 + m0 + m) * d + col] = (YT)acc[mt][r];
+                else y_shared[(size_t)(m0 + m) * d + col] = acc[mt][r];
+            }
+    }
+}
+
+// launchers: grid = (slots) x (64-row groups); false when the shape has no instance
+template <int WFMT, typename XT>
+static bool launch_gateup_tok64(const moe_ffn_args* a, _Float16* h, int slots, hipStream_t s) {
+    if (a->d % kKC || a->f % 64) return false;
+    const dim3 grid((unsigned)(slots * (a->f / 64)));
+#define MOE_GU64(NCH)                                                                                              \
+    ffn_gateup_tok64<WFMT, XT, NCH><<<grid, 256, 0, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->E,            \
+                                                         a->expert_ptrs, (const uint8_t*)a->shared_blob, a->counts, \
+                                                         a->offsets, a->sorted_idx, a->active, h)
+    switch (a->d / kKC) {
+    case 1: MOE_GU64(1); return true;
+    case 2: MOE_GU64(2); return true;
+    case 4: MOE_GU64(4); return true;
+    case 8: MOE_GU64(8); return true;
+    case 16: MOE_GU64(16); return true;
+    default: return false;
+    }
+#undef MOE_GU64
+}
+
+template <int WFMT, typename YT>
+static bool launch_down_tok64(const moe_ffn_args* a, const _Float16* h, int slots, hipStream_t s) {
+    if (a->f % kKC || a->d % 64) return false;
+    const dim3 grid((unsigned)(slots * (a->d / 64)));
+#define MOE_DN64(NCH)                                                                                             \
+    ffn_down_tok64<WFMT, YT, NCH><<<grid, 256, 0, s>>>(h, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs,         \
+                                                       (const uint8_t*)a->shared_blob, a->counts, a->offsets,    \
+                                                       a->active, (YT*)a->y_perm, a->y_shared)
+    switch (a->f / kKC) {
+    case 1: MOE_DN64(1); return true;
+    case 2: MOE_DN64(2); return true;
+    case 3: MOE_DN64(3); return true;
+    case 4: MOE_DN64(4); return true;
+    case 6: MOE_DN64(6); return true;
+    case 8: MOE_DN64(8); return true;
+    case 12: MOE_DN64(12); return true;
+    case 16: MOE_DN64(16); return true;
+    default: return false;
+    }
+#undef MOE_DN64
+}
+
 template <int WFMT, typename XT>
 static int run_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     const int max_active = a->E < a->T * a->k ? a->E : a->T * a->k;
@@ -730,7 +1038,8 @@ static int run_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     if (a->phase != 2) {
         // token-dense kernel for small int4 batches; the token tile of d fp16 values per token fits in LDS
         const bool tok16 = WFMT == MOE_WFMT_I4B32 && a->T <= kTokMax && (size_t)a->T * a->d * 2 <= 64 * 1024;
-        if (!(tok16 && launch_gateup_tok16<XT>(a, h, slots, s)))
+        const bool tok64 = !tok16 && a->T <= kTok64;
+        if (!(tok16 && launch_gateup_tok16<XT>(a, h, slots, s)) && !(tok64 && launch_gateup_tok64<WFMT, XT>(a, h, slots, s)))
             ffn_float_gateup<WFMT, XT><<<g1, 256, lds1, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs,
                                                              (const uint8_t*)a->shared_blob, a->counts, a->offsets,
                                                              a->sorted_idx, a->active, h);
@@ -741,13 +1050,15 @@ static int run_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     const size_t lds2 = (size_t)rows_lds * a->f * sizeof(_Float16);
     // every slot has at most T <= 16 rows: one wavefront per 16 output rows
     const bool tok16 = WFMT == MOE_WFMT_I4B32 && a->T <= kTokMax && (size_t)kTokMax * a->f * 2 <= 64 * 1024;
+    const bool tok64 = !tok16 && a->T <= kTok64;
     if (a->y_dtype == MOE_DT_F32) {
-        if (!(tok16 && launch_down_tok16<float>(a, h, slots, s)))
+        if (!(tok16 && launch_down_tok16<float>(a, h, slots, s)) && !(tok64 && launch_down_tok64<WFMT, float>(a, h, slots, s)))
             ffn_float_down<WFMT, float><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
                                                               (const uint8_t*)a->shared_blob, a->counts, a->offsets,
                                                               a->active, (float*)a->y_perm, a->y_shared);
     } else {
-        if (!(tok16 && launch_down_tok16<_Float16>(a, h, slots, s)))
+        if (!(tok16 && launch_down_tok16<_Float16>(a, h, slots, s)) &&
+            !(tok64 && launch_down_tok64<WFMT, _Float16>(a, h, slots, s)))
             ffn_float_down<WFMT, _Float16><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
                                                                  (const uint8_t*)a->shared_blob, a->counts, a->offsets,
                                                                  a->active, (_Float16*)a->y_perm, a->y_shared);

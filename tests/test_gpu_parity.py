@@ -305,3 +305,54 @@ def test_ffn_phases_equal_whole_call(name):
     assert np.array_equal(host(G.y_perm[:T * k]), y0)
     if ys0 is not None:
         assert np.array_equal(host(G.y_shared[:T]), ys0)
+
+
+@pytest.mark.parametrize("name,T", [("decode_t4", 4), ("tiny", 48), ("skew", 40)])
+def test_duplicate_expert_ids_through_permute_ffn_combine(name, T):
+    """Ids handed to moe_permute directly, every token listing expert 3 twice
+    (each time with its own gate): the permutation keeps both slots (stable,
+    bit-exact against the oracle) and the float-mode FFN writes the expert's
+    output to both rows.  Expert 3 then holds 2T rows, more than 64 for T >= 33,
+    which takes the moderate-batch kernels through their multi-pass paths."""
+    L = synth.make_layer(name, T=T)
+    c = L.cfg
+    G = gpu_layer(L, mode=B.MOE_ACT_FLOAT)
+    xt = x_tensor(L)
+    k, E = c.k, c.E
+    rng = np.random.Generator(np.random.PCG64(77))
+    ids = np.empty((T, k), np.int32)
+    others = np.setdiff1d(np.arange(E), [3])
+    for t in range(T):
+        row = np.concatenate([[3, 3], rng.choice(others, size=k - 2, replace=False)]).astype(np.int32)
+        rng.shuffle(row)
+        ids[t] = row
+    gates = rng.random((T, k)).astype(np.float32) + 0.1
+    gates /= gates.sum(axis=1, keepdims=True)
+    n = T * k
+    G.ids[:T].copy_(torch.from_numpy(ids).to(DEV))
+    G.gates[:T].copy_(torch.from_numpy(gates).to(DEV))
+    ws = G._ws_for(T)
+    B.moe_permute(G.ids[:T], E, G.counts, G.offsets, G.sorted_idx[:n], G.dest[:n], G.active, ws)
+    B.moe_expert_ffn(x=xt, T=T, d=c.d, f=c.f, E=E, k=k, wfmt=c.wfmt, act_mode=B.MOE_ACT_FLOAT,
+                     expert_ptrs=G.expert_ptrs, counts=G.counts, offsets=G.offsets, sorted_idx=G.sorted_idx[:n],
+                     active=G.active, y_perm=G.y_perm[:n], ws=ws, shared_blob=G.shared,
+                     y_shared=G.y_shared[:T] if G.shared is not None else None)
+    B.moe_combine(G.y_perm[:n], G.dest[:n], G.gates[:T], G.y_shared[:T] if G.shared is not None else None, None,
+                  G.out[:T])
+    torch.cuda.synchronize()
+    st = routing_state(G, T)
+    counts, offsets, sorted_idx, dest = oracle.permute(ids, E)
+    assert counts[3] == 2 * T
+    assert np.array_equal(st["counts"], counts)
+    assert np.array_equal(st["offsets"], offsets)
+    assert np.array_equal(st["sorted_idx"], sorted_idx)
+    assert np.array_equal(st["dest"], dest)
+    xf = synth.bf16_bits_to_f32(L.x) if c.x_dtype == "bf16" else L.x
+    ref = np.zeros((T, c.d))
+    for e in np.unique(ids):
+        tt, jj = np.nonzero(ids == e)
+        ye = oracle.expert_ffn(xf[tt], L.experts[e], c.wfmt, c.f, oracle.ACT_FLOAT)
+        np.add.at(ref, tt, gates[tt, jj][:, None].astype(np.float64) * ye)  # a token may list e twice
+    if L.shared is not None:
+        ref += oracle.expert_ffn(xf, L.shared, c.wfmt, c.f, oracle.ACT_FLOAT)
+    check_float(host(G.out[:T]), ref, "%s duplicate ids" % name)
