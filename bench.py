@@ -254,6 +254,7 @@ def main():
         roof["kernel"] = "ffn_q8_tiled<0> (moe_expert_ffn phase 1)" if cfg.wfmt == 4 else "ffn_q8_gateup (moe_expert_ffn phase 1)"
     else:
         roof["kernel"] = ("ffn_gateup_tok16 (moe_expert_ffn phase 1)" if cfg.wfmt == 4 and T <= 16
+                          else "ffn_gateup_tok64 (moe_expert_ffn phase 1)" if T <= 64
                           else "ffn_float_gateup (moe_expert_ffn phase 1)")
     roof["kernel_ms"] = round(gu_ms, 5)
     roof["algorithmic_bytes_per_launch"] = int(alg_bytes)

@@ -117,6 +117,9 @@ int launch_route_small(const void* x, int x_dtype, int T, int d, const float* Wr
 size_t float_h_bytes(int T, int f, int k);
 int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
                    int32_t* dest, int32_t* active, int32_t* hist, hipStream_t s);
+// one-workgroup permutation for at most 4096 slots
+int launch_permute_block(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
+                         int32_t* dest, int32_t* active, hipStream_t s);
 int launch_rmsnorm(const float* x, int T, int d, float eps, float* out, hipStream_t s);
 int launch_quant_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float* sx, hipStream_t s);
 int launch_ffn_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s);

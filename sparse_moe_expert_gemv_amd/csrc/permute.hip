@@ -105,6 +105,7 @@ int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int
     const int n = T * k;
     const int nch = (n + kPermChunk - 1) / kPermChunk;
     if (n == 0) return MOE_OK;  // the API treats T == 0 as a no-op before getting here
+    if (n <= 4096) return launch_permute_block(ids, n, E, counts, offsets, sorted_idx, dest, active, s);
     perm_hist<<<nch, 256, E * sizeof(int32_t), s>>>(ids, n, E, hist);
     int rc = check_launch();
     if (rc) return rc;

@@ -444,6 +444,28 @@ __device__ void permute_rank64(const int32_t* s_ids, int n, int E, int32_t* coun
     }
 }
 
+// Permutation of up to kBlockPermMax slots by one workgroup (ids staged in
+// LDS, then the block-level grouping above): one launch instead of three.
+constexpr int kBlockPermMax = 4096;
+__global__ __launch_bounds__(256) void perm_block(const int32_t* __restrict__ ids, int n, int E,
+                                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ sorted_idx, int32_t* __restrict__ dest,
+                                                  int32_t* __restrict__ active) {
+    __shared__ int32_t s_ids[kBlockPermMax];
+    __shared__ int32_t s_cnt[1024];
+    __shared__ int32_t s_part[256], s_flag[256];
+    for (int i = threadIdx.x; i < n; i += 256) s_ids[i] = ids[i];
+    __syncthreads();
+    block_permute(s_ids, n, E, counts, offsets, sorted_idx, dest, active, s_cnt, s_part, s_flag);
+}
+
+int launch_permute_block(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
+                         int32_t* dest, int32_t* active, hipStream_t s) {
+    if (n > kBlockPermMax) return MOE_ERR_UNSUPPORTED;
+    perm_block<<<1, 256, 0, s>>>(ids, n, E, counts, offsets, sorted_idx, dest, active);
+    return check_launch();
+}
+
 // One workgroup: top-k of every token (T <= kSmallSlots / k) and, when asked,
 // the grouping of the routing slots by expert.
 template <int NPL>
@@ -577,6 +599,76 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const XT* __restrict__ 
     }
 }
 
+// ------------------------------------------ moderate batches: split-k fp64 MFMA ----
+// Workgroup = 16 tokens x 16 router rows, sixteen wavefronts splitting k;
+// wavefront s, lane group g = l / 16 owns the contiguous range of d / 64 k at
+// s d / 16 + g d / 64, so that at MFMA step j every lane multiplies its own
+// j-th token value by its own j-th router value (A and B share the k
+// assignment; every product appears once).  Operands come straight from
+// global memory (no reuse across wavefronts); the sixteen partial tiles meet
+// in LDS and are summed in wavefront order, then the bias is added.
+template <typename XT, int KPL>
+__global__ __launch_bounds__(1024) void route_logits_splitk(const XT* __restrict__ x, int T, int d,
+                                                            const float* __restrict__ Wr,
+                                                            const float* __restrict__ bias, int E,
+                                                            double* __restrict__ logits) {
+    __shared__ double part[16][4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.y * 16, e0 = blockIdx.x * 16;
+    const int t = min(t0 + (lane & 15), T - 1), e = min(e0 + (lane & 15), E - 1);
+    const int k0 = wave * (d / 16) + (lane >> 4) * KPL;
+    float xa[KPL], wb[KPL];
+    if constexpr (sizeof(XT) == 4) {
+#pragma unroll
+        for (int j = 0; j < KPL; j += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(x + (size_t)t * d + k0 + j);
+            xa[j] = v.x; xa[j + 1] = v.y; xa[j + 2] = v.z; xa[j + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPL; j += 4) {
+            const uint2 r = *reinterpret_cast<const uint2*>(x + (size_t)t * d + k0 + j);
+            xa[j] = __uint_as_float(r.x << 16); xa[j + 1] = __uint_as_float(r.x & 0xFFFF0000u);
+            xa[j + 2] = __uint_as_float(r.y << 16); xa[j + 3] = __uint_as_float(r.y & 0xFFFF0000u);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; j += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(Wr + (size_t)e * d + k0 + j);
+        wb[j] = v.x; wb[j + 1] = v.y; wb[j + 2] = v.z; wb[j + 3] = v.w;
+    }
+    double4v acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[j], (double)wb[j], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        // output (row 4 r + l / 16, column l % 16) of the tile: r = tid / 64, l = tid % 64
+        const int r = threadIdx.x >> 6, l = threadIdx.x & 63;
+        double sum = 0.0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) sum += part[q][r][l];
+        const int tt = t0 + 4 * r + (l >> 4), ee = e0 + (l & 15);
+        if (tt < T && ee < E) logits[(size_t)tt * E + ee] = sum + (bias ? (double)bias[ee] : 0.0);
+    }
+}
+
+template <typename XT>
+static bool launch_logits_splitk(const XT* x, int T, int d, const float* Wr, const float* bias, int E,
+                                 double* logits, hipStream_t s) {
+    const dim3 grid((E + 15) / 16, (T + 15) / 16);
+    switch (d / 64) {
+    case 2: route_logits_splitk<XT, 2><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
+    case 4: route_logits_splitk<XT, 4><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
+    case 8: route_logits_splitk<XT, 8><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
+    case 16: route_logits_splitk<XT, 16><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
+    case 32: route_logits_splitk<XT, 32><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
+    case 64: route_logits_splitk<XT, 64><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
+    default: return false;
+    }
+}
+
 bool route_small_ok(int T, int d, int k) { return T <= 64 && (size_t)T * k <= kSmallSlots && (size_t)kTG * d * 4 <= 64 * 1024; }
 
 // ------------------------------------------------ wavefront per row (T <= 8) ----
@@ -658,6 +750,12 @@ static int launch_logits(const void* x, int x_dtype, int T, int d, const float* 
         else
             ok = nu <= 2 ? launch_logits_wave<uint16_t, 2>((const uint16_t*)x, T, d, Wr, bias, E, logits, s)
                          : launch_logits_wave<uint16_t, 8>((const uint16_t*)x, T, d, Wr, bias, E, logits, s);
+        if (ok) return check_launch();
+    }
+    if (T <= 256) {
+        const bool ok = x_dtype == MOE_DT_F32
+                            ? launch_logits_splitk<float>((const float*)x, T, d, Wr, bias, E, logits, s)
+                            : launch_logits_splitk<uint16_t>((const uint16_t*)x, T, d, Wr, bias, E, logits, s);
         if (ok) return check_launch();
     }
     if (T <= 256 && (size_t)kTG * d * 4 <= 64 * 1024) {
