@@ -83,6 +83,15 @@ __device__ __forceinline__ V gload(const V* p) {
     return *(const __attribute__((address_space(1))) V*)p;
 }
 
+// Non-temporal load through a global-address-space pointer, for data read once
+// per call (expert weights streamed from HBM): it is not kept in the caches at
+// the expense of data that is reused.
+template <typename V>
+__device__ __forceinline__ V gload_nt(const V* p) {
+    return __builtin_nontemporal_load((const __attribute__((address_space(1))) V*)p);
+}
+constexpr int kBufNT = 2;  // cache-policy operand of a buffer load: non-temporal
+
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // ---- error plumbing -----------------------------------------------------------

@@ -59,8 +59,12 @@ __device__ __forceinline__ float scale_of(const uint2& raw, int b) {
 
 template <int WFMT>
 __device__ __forceinline__ uint2 load_scale_raw(const uint8_t* p) {
-    if constexpr (WFMT == MOE_WFMT_I4B32) return *reinterpret_cast<const uint2*>(p);
-    else return make_uint2(*reinterpret_cast<const uint32_t*>(p), 0u);
+    if constexpr (WFMT == MOE_WFMT_I4B32) {
+        const uint2v v = gload_nt(reinterpret_cast<const uint2v*>(p));
+        return make_uint2(v[0], v[1]);
+    } else {
+        return make_uint2(gload_nt(reinterpret_cast<const uint32_t*>(p)), 0u);
+    }
 }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
@@ -131,10 +135,10 @@ __device__ __forceinline__ void load_chunk(WChunk<NT>& w, const uint8_t* blob, c
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         if (i < nt) {
-            w.q0[i] = q0[(size_t)(t_lo + i) * 64];
+            w.q0[i] = gload_nt(q0 + (size_t)(t_lo + i) * 64);
             w.s0[i] = load_scale_raw<WFMT>(s0 + (size_t)(t_lo + i) * STB);
             if (two) {
-                w.q1[i] = q1[(size_t)(t_lo + i) * 64];
+                w.q1[i] = gload_nt(q1 + (size_t)(t_lo + i) * 64);
                 w.s1[i] = load_scale_raw<WFMT>(s1 + (size_t)(t_lo + i) * STB);
             }
         }
@@ -461,8 +465,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
     const uint32_t ou = (uint32_t)L.u.qoff + tile0 * 1024 + lane * 16;
     const uint32_t osg = (uint32_t)L.g.soff + tile0 * 128 + (lane & 15) * 8;
     const uint32_t osu = (uint32_t)L.u.soff + tile0 * 128 + (lane & 15) * 8;
-    auto ld2 = [&](uint32_t off) { return __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(wr, off, 0, 0)); };
-    auto ld4 = [&](uint32_t off) { return __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0)); };
+    auto ld2 = [&](uint32_t off) { return __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(wr, off, 0, kBufNT)); };
+    auto ld4 = [&](uint32_t off) { return __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, kBufNT)); };
     uint4v qg[NT], qu[NT];
     uint2v sg[NT], su[NT];
 #pragma unroll
@@ -635,8 +639,8 @@ __global__ __launch_bounds__(256) void ffn_down_tok16(const _Float16* __restrict
     uint2v sc[NKT];
 #pragma unroll
     for (int i = 0; i < kPipe && i < NKT; ++i) {
-        sc[i] = gload(ps + i * 16);
-        q[i] = gload(pq + i * 64);
+        sc[i] = gload_nt(ps + i * 16);
+        q[i] = gload_nt(pq + i * 64);
     }
     const int rr0 = lane & 15;
     uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
@@ -649,8 +653,8 @@ __global__ __launch_bounds__(256) void ffn_down_tok16(const _Float16* __restrict
             __syncthreads();  // the previous tile's rows are no longer read
 #pragma unroll
             for (int i = 0; i < kPipe && i < NKT; ++i) {
-                sc[i] = gload(ps + i * 16);
-                q[i] = gload(pq + i * 64);
+                sc[i] = gload_nt(ps + i * 16);
+                q[i] = gload_nt(pq + i * 64);
             }
         }
         // the tile's h rows -> LDS, two 16-byte chunks per thread per round
@@ -677,8 +681,8 @@ __global__ __launch_bounds__(256) void ffn_down_tok16(const _Float16* __restrict
 #pragma unroll
         for (int i = 0; i < NKT; ++i) {
             if (i + kPipe < NKT) {
-                sc[i + kPipe] = gload(ps + (i + kPipe) * 16);
-                q[i + kPipe] = gload(pq + (i + kPipe) * 64);
+                sc[i + kPipe] = gload_nt(ps + (i + kPipe) * 16);
+                q[i + kPipe] = gload_nt(pq + (i + kPipe) * 64);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -766,11 +770,11 @@ __device__ __forceinline__ void load_strip_chunk(StripChunk<WFMT>& w, __amdgpu_b
     constexpr int TPC = StripChunk<WFMT>::TPC;
 #pragma unroll
     for (int j = 0; j < TPC; ++j) {
-        w.q[j] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(r, qoff + (tile + j) * 1024 + lane * 16, 0, 0));
+        w.q[j] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(r, qoff + (tile + j) * 1024 + lane * 16, 0, kBufNT));
         if constexpr (WFMT == MOE_WFMT_I4B32)
-            w.s[j] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(r, soff + (tile + j) * 128 + (lane & 15) * 8, 0, 0));
+            w.s[j] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(r, soff + (tile + j) * 128 + (lane & 15) * 8, 0, kBufNT));
         else
-            w.s[j] = uint2v{(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, soff + (tile + j) * 64 + (lane & 15) * 4, 0, 0), 0u};
+            w.s[j] = uint2v{(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, soff + (tile + j) * 64 + (lane & 15) * 4, 0, kBufNT), 0u};
     }
 }
 

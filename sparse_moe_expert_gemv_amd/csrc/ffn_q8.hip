@@ -452,13 +452,13 @@ __global__ __launch_bounds__(256) void ffn_q8_tiled(const int8_t* __restrict__ a
             const int idx = threadIdx.x + q * 256, st = idx >> 6, ll = idx & 63;
             const MatLayout& M = MODE == 0 ? (st < 4 ? L.g : L.u) : L.dn;
             const int strip = MODE == 0 ? grp * 4 + (st & 3) : grp * 8 + st;
-            rw[q] = gload(reinterpret_cast<const uint4v*>(blob + M.qoff + ((size_t)strip * nkt + c) * 1024) + ll);
+            rw[q] = gload_nt(reinterpret_cast<const uint4v*>(blob + M.qoff + ((size_t)strip * nkt + c) * 1024) + ll);
         }
         if (threadIdx.x < 128) {
             const int st = threadIdx.x >> 4, rr = threadIdx.x & 15;
             const MatLayout& M = MODE == 0 ? (st < 4 ? L.g : L.u) : L.dn;
             const int strip = MODE == 0 ? grp * 4 + (st & 3) : grp * 8 + st;
-            rsw = gload(reinterpret_cast<const uint2v*>(blob + M.soff + ((size_t)strip * nkt + c) * 128 + rr * 8));
+            rsw = gload_nt(reinterpret_cast<const uint2v*>(blob + M.soff + ((size_t)strip * nkt + c) * 128 + rr * 8));
         }
         if (threadIdx.x < kTM * 32)
             rsa = gload(reinterpret_cast<const float4v*>(as_ + (size_t)s_row[threadIdx.x] * nb + c * 4));

@@ -688,7 +688,10 @@ __global__ __launch_bounds__(64) void route_logits_wave(const XT* __restrict__ x
     float4 wv[NU];
     float4 xv[TT][NU];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) wv[u] = w[min(u * 64 + lane, nq - 1)];
+    for (int u = 0; u < NU; ++u) {  // each router row is read once: non-temporal
+        const float4v v = gload_nt(reinterpret_cast<const float4v*>(w) + min(u * 64 + lane, nq - 1));
+        wv[u] = make_float4(v[0], v[1], v[2], v[3]);
+    }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         const int tt = min(t, T - 1);
