@@ -60,7 +60,8 @@ def measured_traffic(workload: str):
     kernel source has not changed since the counters were taken; else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "gateup_%s_hbm_counters.md" % workload)
-    src = os.path.join(ROOT, "sparse_moe_expert_gemv_amd", "csrc", "ffn_float.hip")
+    src = os.path.join(ROOT, "sparse_moe_expert_gemv_amd", "csrc",
+                       "ffn_q8.hip" if workload == "prefill" else "ffn_float.hip")
     if not os.path.exists(path):
         return None
     fields = {}
