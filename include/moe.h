@@ -270,6 +270,25 @@ int moe_cache_lookup(const moe_cache* cache, int layer, int32_t* hit_ids, int* n
 int moe_cache_stage(moe_cache* cache, int layer, int buf, const void* const* host_src, void** dev_table,
                     moe_stream_t stream, moe_event_t done);
 
+/*
+ * Map one layer for reading misses in place ("single RTX 5090 runs a 125B
+ * model", on-demand MoE expert scheduling: only the experts the gating network
+ * picks are computed, so only those need their weights): write the layer's
+ * device pointer table dev_table [E] with hits -> pool slots and misses -> the
+ * device address of their host blob host_src[e] (host array [E] of pointers
+ * into pinned host memory from hipHostMalloc or torch's pin_memory, which is
+ * mapped into the device's address space), on `stream`, then record `done`
+ * (may be NULL).  moe_expert_ffn then reads a missed expert's weights over the
+ * host link, and only when the routing selects it: no copy and no host round
+ * trip between routing and the FFN, so a whole decode stack can be one graph.
+ * The table stays valid until the residency changes (moe_cache_set_resident).
+ * Errors: MOE_ERR_INVALID_ARG (null handle, host_src or dev_table, layer out
+ * of range, a null host pointer for a miss); MOE_ERR_HIP when a host blob is
+ * not mapped for the current device (hipHostGetDevicePointer fails).
+ */
+int moe_cache_map_host(moe_cache* cache, int layer, const void* const* host_src, void** dev_table,
+                       moe_stream_t stream, moe_event_t done);
+
 #ifdef __cplusplus
 }
 #endif

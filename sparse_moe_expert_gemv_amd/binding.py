@@ -29,7 +29,7 @@ EXPORTED = [
     "moe_unpack_experts", "moe_workspace_size", "moe_route", "moe_route_permute", "moe_permute", "moe_quantize_act",
     "moe_expert_ffn", "moe_rmsnorm",
     "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
-    "moe_cache_stage",
+    "moe_cache_stage", "moe_cache_map_host",
 ]
 
 
@@ -84,6 +84,7 @@ def lib():
             "moe_cache_set_resident": ([P, P, I, P, P], I),
             "moe_cache_lookup": ([P, I, P, C.POINTER(I), P, C.POINTER(I)], I),
             "moe_cache_stage": ([P, I, I, P, P, P, P], I),
+            "moe_cache_map_host": ([P, I, P, P, P, P], I),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -251,6 +252,12 @@ class SlotCache:
         _check("moe_cache_stage", lib().moe_cache_stage(self.h, layer, buf, src, _ptr(dev_table), _stream(st), None))
         if done_event is not None:
             done_event.record(st)
+
+    def map_host(self, layer, host_ptrs, dev_table, stream=None):
+        """Point the misses of one layer's table at their pinned host blobs (read in place)."""
+        src = (C.c_void_p * self.E)(*[int(p) for p in host_ptrs])
+        _check("moe_cache_map_host", lib().moe_cache_map_host(self.h, layer, src, _ptr(dev_table), _stream(stream),
+                                                              None))
 
     def close(self):
         if self.h:

@@ -1,9 +1,11 @@
 // Expert slot cache: host bookkeeping of which global expert occupies which
-// slot of a caller-owned HBM pool, and per-layer staging of the misses from
-// pinned host memory on a (side) stream.  "How Strata works" (adaptive expert
-// cache section) loads the most-used ~4,500 experts by a usage ranking into
-// GPU memory; "Strata benchmarks" (prefill optimisation table) streams the
-// next layer's experts over PCIe while the current layer computes.
+// slot of a caller-owned HBM pool, and per-layer pointer tables for the
+// misses: staged from pinned host memory on a (side) stream, or (decode)
+// pointing at the pinned host blobs themselves, read in place by the FFN.
+// "How Strata works" (adaptive expert cache section) loads the most-used
+// ~4,500 experts by a usage ranking into GPU memory; "Strata benchmarks"
+// (prefill optimisation table) streams the next layer's experts over PCIe
+// while the current layer computes.
 #include <vector>
 
 #include "common.hpp"
@@ -133,6 +135,41 @@ int moe_cache_stage(moe_cache* c, int layer, int buf, const void* const* host_sr
             ++i;
         }
     }
+    hipError_t err = hipMemcpyAsync(dev_table, table, sizeof(void*) * (size_t)c->E, hipMemcpyHostToDevice, st);
+    if (err != hipSuccess) return hip_fail(err);
+    err = hipEventRecord(c->table_done[layer], st);
+    if (err != hipSuccess) return hip_fail(err);
+    c->table_pending[layer] = true;
+    if (done) {
+        err = hipEventRecord(reinterpret_cast<hipEvent_t>(done), st);
+        if (err != hipSuccess) return hip_fail(err);
+    }
+    return MOE_OK;
+}
+
+int moe_cache_map_host(moe_cache* c, int layer, const void* const* host_src, void** dev_table, moe_stream_t s,
+                       moe_event_t done) {
+    if (!c || layer < 0 || layer >= c->n_layers || !host_src || !dev_table) return MOE_ERR_INVALID_ARG;
+    for (int e = 0; e < c->E; ++e)
+        if (c->slot_of[(size_t)layer * c->E + e] < 0 && !host_src[e]) return MOE_ERR_INVALID_ARG;
+    if (c->table_pending[layer]) {
+        const hipError_t e = hipEventSynchronize(c->table_done[layer]);
+        if (e != hipSuccess) return hip_fail(e);
+        c->table_pending[layer] = false;
+    }
+    void** table = c->tables + (size_t)layer * c->E;
+    for (int e = 0; e < c->E; ++e) {
+        const int slot = c->slot_of[(size_t)layer * c->E + e];
+        if (slot >= 0) {
+            table[e] = c->pool + (size_t)slot * c->eb;
+        } else {
+            void* dptr = nullptr;
+            const hipError_t err = hipHostGetDevicePointer(&dptr, const_cast<void*>(host_src[e]), 0);
+            if (err != hipSuccess) return hip_fail(err);
+            table[e] = dptr;
+        }
+    }
+    const hipStream_t st = as_stream(s);
     hipError_t err = hipMemcpyAsync(dev_table, table, sizeof(void*) * (size_t)c->E, hipMemcpyHostToDevice, st);
     if (err != hipSuccess) return hip_fail(err);
     err = hipEventRecord(c->table_done[layer], st);

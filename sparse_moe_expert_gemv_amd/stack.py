@@ -11,6 +11,12 @@ layer computes ("Strata benchmarks", prefill optimisation table).  Here:
   two device staging buffers on a side stream (``moe_cache_stage``), which also
   rewrites that layer's device pointer table; layer l + 2 is staged into the
   buffer of layer l as soon as layer l has finished;
+* or (decode, ``miss_mode="host"``) every layer's pointer table sends the
+  misses to the pinned host blobs themselves (``moe_cache_map_host``): the
+  FFN reads a missed expert over the host link only when the routing selects
+  it, so a decode pass needs no staging, no side stream and no host round trip
+  (the pages' "single RTX 5090 runs a 125B model" report: only the experts the
+  gating network picks are computed);
 * the compute stream waits for layer l's staging event, then runs
   rmsnorm -> route -> permute -> quantise -> expert FFN (through the pointer
   table) -> combine with the residual: h_{l+1} = h_l + MoE_l(norm(h_l)).  The
@@ -33,14 +39,20 @@ from .layer import pack_blobs
 
 class ExpertStack:
     def __init__(self, routers, shared_blobs, host_store: torch.Tensor, host_index: np.ndarray, resident_ids,
-                 *, d, f, k, wfmt, act_mode, max_T, staging_slots=None, device="cuda", eps=1e-6):
+                 *, d, f, k, wfmt, act_mode, max_T, staging_slots=None, device="cuda", eps=1e-6,
+                 biases=None, miss_mode="stage"):
         """
         routers      list of L fp32 arrays [E, d]
         shared_blobs [L, bytes] canonical uint8 (numpy) or None
         host_store   pinned host uint8 tensor [n_blobs, bytes] of PACKED expert blobs
         host_index   int array [L, E]: row of host_store holding expert (l, e)
         resident_ids global ids (l * E + e) kept in the slot pool
+        biases       list of L fp32 arrays [E] (router biases) or None
+        miss_mode    "stage": misses copied per layer into staging buffers;
+                     "host": misses read in place from the pinned host store
         """
+        assert miss_mode in ("stage", "host")
+        self.miss_mode = miss_mode
         self.device = torch.device(device)
         self.d, self.f, self.k, self.wfmt, self.act_mode = d, f, k, wfmt, act_mode
         self.eps = eps
@@ -53,6 +65,8 @@ class ExpertStack:
         base = host_store.data_ptr()
         self.host_ptrs = [[base + int(self.host_index[l, e]) * self.eb for e in range(self.E)] for l in range(self.L)]
         self.Wr = [torch.as_tensor(np.ascontiguousarray(w, np.float32)).to(self.device) for w in routers]
+        self.bias = None if biases is None else \
+            [torch.as_tensor(np.ascontiguousarray(b, np.float32)).to(self.device) for b in biases]
         self.shared = None
         if shared_blobs is not None:
             sh = torch.from_numpy(np.ascontiguousarray(shared_blobs, dtype=np.uint8)).to(self.device)
@@ -62,12 +76,17 @@ class ExpertStack:
         self.pool = torch.empty((max(self.n_slots, 1), self.eb), dtype=torch.uint8, device=self.device)
         res_per_layer = np.bincount(np.asarray(resident_ids, dtype=np.int64) // self.E, minlength=self.L)
         need = int(self.E - res_per_layer.min()) if self.n_slots else self.E
+        if miss_mode == "host":
+            need = 0
         self.staging_slots = need if staging_slots is None else staging_slots
         self.staging = torch.empty((2, max(self.staging_slots, 1), self.eb), dtype=torch.uint8, device=self.device)
         self.tables = torch.zeros((self.L, self.E), dtype=torch.int64, device=self.device)
         self.cache = B.SlotCache(self.L, self.E, self.n_slots, self.eb, self.pool, self.staging, 2,
                                  self.staging_slots)
         self.cache.set_resident(resident_ids, [self.host_ptrs[g // self.E][g % self.E] for g in resident_ids])
+        if miss_mode == "host":
+            for l in range(self.L):
+                self.cache.map_host(l, self.host_ptrs[l], self.tables[l])
         torch.cuda.synchronize()
         self.side = torch.cuda.Stream(device=self.device)
         self.staged = [torch.cuda.Event() for _ in range(self.L)]
@@ -108,7 +127,8 @@ class ExpertStack:
         k, E, n = self.k, self.E, h.shape[0] * self.k
         xn = self.xn[:T]
         B.moe_rmsnorm(h, xn, self.eps, stream)
-        B.moe_route_permute(xn, self.Wr[l], None, k, self.ids[:T], self.gates[:T], self.counts, self.offsets,
+        bias = None if self.bias is None else self.bias[l]
+        B.moe_route_permute(xn, self.Wr[l], bias, k, self.ids[:T], self.gates[:T], self.counts, self.offsets,
                             self.sorted_idx[:n], self.dest[:n], self.active, self.ws, stream)
         common = dict(T=T, d=self.d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
                       expert_ptrs=self.tables[l] if table is None else table, counts=self.counts,
@@ -124,11 +144,14 @@ class ExpertStack:
         B.moe_combine(self.y_perm[:n], self.dest[:n], self.gates[:T],
                       None if self.shared is None else self.y_shared[:T], h, out, stream)
 
-    def forward(self, x: torch.Tensor, keep=(), copy_only=False, compute_only_tables=None):
+    def forward(self, x: torch.Tensor, keep=(), copy_only=False, compute_only_tables=None, ids_out=None):
         """Run all layers on x ([T, d] fp32).  Returns (h_L, {l: (h_l, norm(h_l)) for l in keep}).
 
         copy_only: only the staging (timing aid); compute_only_tables: run the
-        compute with these pointer tables [L, E] instead of staging (timing aid).
+        compute with these pointer tables [L, E] instead of staging (timing aid);
+        ids_out: a list that receives a copy of every layer's routed ids [T, k].
+        In "host" miss mode nothing is staged: the tables already point at the
+        pool and at the host blobs.
         """
         T = x.shape[0]
         if T > self.max_T:
@@ -137,6 +160,16 @@ class ExpertStack:
         kept = {}
         h = x
         outs = self.hbuf
+        if self.miss_mode == "host" and compute_only_tables is None:
+            for l in range(self.L):
+                out = outs[l % 2]
+                self.layer(l, h, out)
+                if l in keep:
+                    kept[l] = (h.clone(), self.xn[:T].clone())
+                if ids_out is not None:
+                    ids_out.append(self.ids[:T].clone())
+                h = out
+            return h, kept
         if compute_only_tables is None:
             self.side.wait_stream(comp)
             for l in range(min(2, self.L)):
@@ -149,6 +182,8 @@ class ExpertStack:
                 self.layer(l, h, out, table=None if compute_only_tables is None else compute_only_tables[l])
                 if l in keep:
                     kept[l] = (h.clone(), self.xn[:T].clone())
+                if ids_out is not None:
+                    ids_out.append(self.ids[:T].clone())
                 h = out
             self.done[l].record(comp)
             if compute_only_tables is None and l + 2 < self.L:

@@ -159,6 +159,7 @@ class LayerConfig:
     n_layers: int = 1
     n_resident: int = 0     # slot-pool size for the layer stack
     n_pool_blobs: int = 0   # distinct expert blobs backing the layer stack
+    profile_bias: float = 0.0  # stack routers biased by alpha * ln(profile weight); alpha
     notes: str = ""
 
 
@@ -175,6 +176,16 @@ CONFIGS = {
     # 48-layer stack, 8192-token chunk, 4,500-slot resident pool.
     "stack": LayerConfig("stack", 5, 8192, 2048, 512, 10, 768, WFMT_I4B32, "bf16", True, "q8",
                          n_layers=48, n_resident=4500, n_pool_blobs=1024),
+    # 48-layer decode stack (T=4 verify batch, or T=1) over the same 4,500-slot
+    # pool, with every layer's router biased toward the residency profile so
+    # that about 72% of the selected experts are resident ("How Strata works",
+    # adaptive expert cache section: 72% of expert reads hit GPU memory with
+    # ~4,500 cached experts).  alpha = 0.38 gives that rate for logits of
+    # standard deviation 0.02 * sqrt(2048).
+    "decode_stack": LayerConfig("decode_stack", 6, 4, 2048, 512, 10, 768, WFMT_I4B32, "bf16", True, "float",
+                                n_layers=48, n_resident=4500, n_pool_blobs=1024, profile_bias=0.38),
+    "decode_stack_t1": LayerConfig("decode_stack_t1", 6, 1, 2048, 512, 10, 768, WFMT_I4B32, "bf16", True, "float",
+                                   n_layers=48, n_resident=4500, n_pool_blobs=1024, profile_bias=0.38),
 }
 
 
@@ -261,6 +272,7 @@ class Stack:
     index: np.ndarray        # [L, E] pool row of routed expert (l, e)
     shared_index: np.ndarray  # [L] pool row of layer l's shared expert
     resident: np.ndarray     # global ids (l * E + e) kept resident, best rank first
+    biases: list | None = None  # L arrays [E] fp32 router biases (profile-biased routing) or None
 
     def expert_blob(self, layer: int, e: int) -> np.ndarray:
         return self.pool[self.index[layer, e]]
@@ -287,4 +299,14 @@ def make_stack(seed: int = 0, name: str = "stack", overrides: dict | None = None
     index, shared_index = stack_blob_map(seed, cfg.n_layers, cfg.E, cfg.n_pool_blobs)
     rank = stack_profile(seed, cfg.n_layers, cfg.E)
     resident = np.argsort(rank, kind="stable")[:cfg.n_resident]
-    return Stack(cfg, x, routers, pool, index, shared_index, resident)
+    biases = None
+    if cfg.profile_bias:
+        biases = [profile_router_bias(rank, l, cfg.E, cfg.profile_bias) for l in range(cfg.n_layers)]
+    return Stack(cfg, x, routers, pool, index, shared_index, resident, biases)
+
+
+def profile_router_bias(rank: np.ndarray, layer: int, E: int, alpha: float, s: float = 1.1) -> np.ndarray:
+    """Router bias of one layer from the residency profile: alpha * ln w(rank)
+    with w(r) = (r + 1)^-s, the profile's frequency weight of global id layer*E + e."""
+    r = rank[layer * E:(layer + 1) * E].astype(np.float64)
+    return (-alpha * s * np.log(r + 1.0)).astype(np.float32)

@@ -167,3 +167,120 @@ def test_full_stack_48_layers_sampled():
     hit, miss = G.cache.lookup(0)
     assert len(hit) + len(miss) == c.E
     G.close()
+
+
+# ---------------------------------------------------------------------------
+# Decode stack: profile-biased routers, misses read in place from pinned host
+# memory through the layer's pointer table (moe_cache_map_host).
+# ---------------------------------------------------------------------------
+
+DSMALL = dict(T=4, d=512, E=64, k=4, f=256, n_layers=4, n_resident=100, n_pool_blobs=40)
+
+
+def _decode_stack_gpu(S):
+    c = S.cfg
+    store = build_host_store(S.pool, c.wfmt, c.d, c.f)
+    return ExpertStack(S.routers, S.shared_blobs() if c.has_shared else None, store, S.index, S.resident,
+                       d=c.d, f=c.f, k=c.k, wfmt=c.wfmt, act_mode=B.MOE_ACT_FLOAT, max_T=c.T, biases=S.biases,
+                       miss_mode="host")
+
+
+def _check_decode_layer(S, l, h_in, xn_in):
+    c = S.cfg
+    ref_norm = oracle.rmsnorm(h_in, 1e-6)
+    assert np.max(np.abs(xn_in - ref_norm)) <= 1e-6 * (1 + np.max(np.abs(ref_norm)))
+    return oracle.moe_layer(xn_in, S.routers[l], S.biases[l], S.layer_experts(l),
+                            S.shared_blobs()[l] if c.has_shared else None, c.wfmt, c.f, c.k,
+                            act_mode=oracle.ACT_FLOAT, residual=h_in)
+
+
+def _resident_mask(S):
+    c = S.cfg
+    m = np.zeros(c.n_layers * c.E, dtype=bool)
+    m[np.asarray(S.resident, dtype=np.int64)] = True
+    return m.reshape(c.n_layers, c.E)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_small_decode_stack_host_misses_teacher_forced(T):
+    """Every layer teacher-forced against the oracle (ids and permutation bit-exact,
+    outputs within the float tolerance); across the layers the routing selects
+    both resident experts and misses, so both kinds of table entry are read."""
+    S = synth.make_stack(name="decode_stack", overrides=DSMALL, T=T)
+    c = S.cfg
+    G = _decode_stack_gpu(S)
+    x = _x0(S)
+    ids_l = []
+    hL, kept = G.forward(x, keep=range(c.n_layers), ids_out=ids_l)
+    torch.cuda.synchronize()
+    hs = [kept[l][0].cpu().numpy() for l in range(c.n_layers)] + [hL.cpu().numpy()]
+    res = _resident_mask(S)
+    n_hit = n_miss = 0
+    for l in range(c.n_layers):
+        o = _check_decode_layer(S, l, hs[l], kept[l][1].cpu().numpy())
+        ids = ids_l[l].cpu().numpy()
+        assert np.array_equal(ids, o["ids"]), "layer %d ids" % l
+        ok, rel, mx = R.within_tolerance(hs[l + 1], o["out"])
+        assert ok, "layer %d: rel %.3e max %.3e" % (l, rel, mx)
+        used = np.unique(ids)
+        n_hit += int(res[l][used].sum())
+        n_miss += int((~res[l][used]).sum())
+    assert n_hit > 0 and n_miss > 0, (n_hit, n_miss)
+    G.close()
+
+
+def test_small_decode_stack_host_reads_match_device_copy_bitexact():
+    """A layer computed through the host-mapped table equals, bit for bit, the
+    same layer computed from a plain device copy of its experts."""
+    S = synth.make_stack(name="decode_stack", overrides=DSMALL)
+    c = S.cfg
+    G = _decode_stack_gpu(S)
+    x = _x0(S)
+    res = _resident_mask(S)
+    for l in range(c.n_layers):
+        plain = pack_blobs(torch.from_numpy(S.layer_experts(l)).to(DEV), c.wfmt, c.d, c.f)
+        out_a = torch.empty_like(x)
+        out_b = torch.empty_like(x)
+        G.layer(l, x, out_a)
+        ids = G.ids[:c.T].cpu().numpy()
+        G.layer(l, x, out_b, table=pointer_table(plain))
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), "layer %d" % l
+        assert np.array_equal(G.ids[:c.T].cpu().numpy(), ids)
+    # the tables hold host addresses for exactly the non-resident experts
+    tables = G.tables.cpu().numpy()
+    pool_lo = G.pool.data_ptr()
+    pool_hi = pool_lo + G.pool.numel()
+    in_pool = (tables >= pool_lo) & (tables < pool_hi)
+    assert np.array_equal(in_pool, res)
+    G.close()
+
+
+def test_full_decode_stack_48_layers():
+    """The 48-layer decode stack at T=4 over the 4,500-slot pool, misses read
+    from the 24,576-expert pinned host store: first, middle and last layer
+    teacher-forced against the oracle; the hit rate near the intended 72%."""
+    S = synth.make_stack(name="decode_stack")
+    c = S.cfg
+    assert c.n_layers * c.E == 24576 and len(S.resident) == 4500 and c.T == 4
+    G = _decode_stack_gpu(S)
+    x = _x0(S)
+    check = [0, 23, 47]
+    ids_l = []
+    hL, kept = G.forward(x, keep=check, ids_out=ids_l)
+    torch.cuda.synchronize()
+    for l in check:
+        h_in = kept[l][0].cpu().numpy()
+        o = _check_decode_layer(S, l, h_in, kept[l][1].cpu().numpy())
+        assert np.array_equal(ids_l[l].cpu().numpy(), o["ids"]), "layer %d ids" % l
+        out = torch.empty_like(x)
+        G.layer(l, kept[l][0], out)
+        torch.cuda.synchronize()
+        ok, rel, mx = R.within_tolerance(out.cpu().numpy(), o["out"])
+        assert ok, "layer %d: rel %.3e max %.3e" % (l, rel, mx)
+        if l == c.n_layers - 1:
+            assert np.array_equal(out.cpu().numpy(), hL.cpu().numpy())
+    res = _resident_mask(S)
+    sel = np.concatenate([res[l][ids_l[l].cpu().numpy().ravel()] for l in range(c.n_layers)])
+    assert 0.55 < sel.mean() < 0.9, sel.mean()
+    G.close()

@@ -102,3 +102,24 @@ def test_cache_argument_validation():
         B.MOE_ERR_INVALID_ARG
     assert L.moe_cache_destroy(None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_cache_lookup(None, 0, None, None, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_cache_map_host(None, 0, C.c_void_p(1), C.c_void_p(1), None, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_decode_stack_inputs_follow_the_profile():
+    """The decode stack's router biases are alpha * ln w(rank) of the residency
+    profile: within a layer, a better-ranked expert has a larger bias, and the
+    resident set is the profile's top ranks."""
+    import numpy as np
+    import synth
+    S = synth.make_stack(name="decode_stack", overrides=dict(d=256, E=64, f=128, n_layers=3, n_resident=40,
+                                                              n_pool_blobs=8))
+    c = S.cfg
+    rank = synth.stack_profile(0, c.n_layers, c.E)
+    assert sorted(S.resident.tolist()) == sorted(np.argsort(rank)[:40].tolist())
+    for l in range(c.n_layers):
+        r = rank[l * c.E:(l + 1) * c.E]
+        b = S.biases[l]
+        assert b.dtype == np.float32 and b.shape == (c.E,)
+        order = np.argsort(r)
+        assert np.all(np.diff(b[order]) < 0)
+        assert abs(float(b[order[0]]) - (-0.38 * 1.1 * np.log(r[order[0]] + 1.0))) < 1e-5
