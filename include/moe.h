@@ -289,6 +289,54 @@ int moe_cache_stage(moe_cache* cache, int layer, int buf, const void* const* hos
 int moe_cache_map_host(moe_cache* cache, int layer, const void* const* host_src, void** dev_table,
                        moe_stream_t stream, moe_event_t done);
 
+/* ---------------------------------------------------------------------------
+ * Adaptive residency ("How Strata works", adaptive expert cache section: the
+ * cache keeps learning which experts the session uses most and adjusts its
+ * contents).  Usage is counted on the device from the per-layer expert counts
+ * of moe_permute / moe_route_permute; the caller ages the counts into scores
+ * on the host; moe_cache_plan picks which resident experts to swap for which
+ * missing ones; moe_cache_replace carries the swaps out on a stream.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * usage[e] += counts[e] for e < E (device int32 arrays; counts as written by
+ * moe_permute for one layer).  Stream-ordered; wraps modulo 2^32 like any
+ * int32 counter.  Errors: MOE_ERR_INVALID_ARG (null pointer, E < 1).
+ */
+int moe_usage_accumulate(int32_t* usage, const int32_t* counts, int E, moe_stream_t stream);
+
+/*
+ * Replacement plan (host only, no HIP call): over n_total global ids with
+ * resident[g] in {0, 1} and non-negative scores score[g], pair the missing ids
+ * by descending score (ties: lower id first) with the resident ids by
+ * ascending score (ties: lower id first) and keep pair i while
+ * score[admit] > (1 + margin) * score[evict], at most max_swaps pairs.
+ * Writes evict_ids[i], admit_ids[i] (room for max_swaps each) and *n_swaps.
+ * Errors: MOE_ERR_INVALID_ARG (null pointer, n_total < 1, max_swaps < 0,
+ * margin < 0 or not finite, a resident flag other than 0/1, a negative or
+ * non-finite score).
+ */
+int moe_cache_plan(int n_total, const uint8_t* resident, const float* score, int max_swaps, float margin,
+                   int32_t* evict_ids, int32_t* admit_ids, int* n_swaps);
+
+/*
+ * Carry out n swaps on `stream`: admitted expert admit_ids[i] takes the pool
+ * slot of evict_ids[i] (a resident id; admit ids not resident; all 2n ids
+ * distinct), its blob is copied there from host_src[admit] (host array
+ * [n_layers * E] of pinned host pointers, indexed by global id), and the
+ * device pointer tables dev_tables ([n_layers][E] device array of pointers)
+ * of every layer that moe_cache_map_host or moe_cache_stage has written are
+ * rewritten: the admitted expert -> its slot, the evicted one -> the device
+ * address of its host blob (read in place).  Work already enqueued on
+ * `stream` sees the old contents; work enqueued after sees the new ones, so
+ * the call belongs on the stream that runs the layers.
+ * Errors: MOE_ERR_INVALID_ARG (as above, or a null host pointer for an
+ * involved id); MOE_ERR_HIP (a host blob not mapped for the device, a copy
+ * that cannot be enqueued).
+ */
+int moe_cache_replace(moe_cache* cache, int n, const int32_t* evict_ids, const int32_t* admit_ids,
+                      const void* const* host_src, void** dev_tables, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ EXPORTED = [
     "moe_unpack_experts", "moe_workspace_size", "moe_route", "moe_route_permute", "moe_permute", "moe_quantize_act",
     "moe_expert_ffn", "moe_rmsnorm",
     "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
-    "moe_cache_stage", "moe_cache_map_host",
+    "moe_cache_stage", "moe_cache_map_host", "moe_usage_accumulate", "moe_cache_plan", "moe_cache_replace",
 ]
 
 
@@ -85,6 +85,9 @@ def lib():
             "moe_cache_lookup": ([P, I, P, C.POINTER(I), P, C.POINTER(I)], I),
             "moe_cache_stage": ([P, I, I, P, P, P, P], I),
             "moe_cache_map_host": ([P, I, P, P, P, P], I),
+            "moe_usage_accumulate": ([P, P, I, P], I),
+            "moe_cache_plan": ([I, P, P, I, C.c_float, P, P, C.POINTER(I)], I),
+            "moe_cache_replace": ([P, I, P, P, P, P, P], I),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -259,6 +262,16 @@ class SlotCache:
         _check("moe_cache_map_host", lib().moe_cache_map_host(self.h, layer, src, _ptr(dev_table), _stream(stream),
                                                               None))
 
+    def replace(self, evict_ids, admit_ids, host_ptrs_all, dev_tables, stream=None):
+        """Swap resident evict_ids[i] for admit_ids[i] (global ids) on `stream`;
+        host_ptrs_all is indexed by global id; dev_tables is the [L, E] pointer tables."""
+        n = len(evict_ids)
+        ev = (C.c_int32 * max(n, 1))(*[int(g) for g in evict_ids])
+        ad = (C.c_int32 * max(n, 1))(*[int(g) for g in admit_ids])
+        src = (C.c_void_p * len(host_ptrs_all))(*[int(p) for p in host_ptrs_all])
+        _check("moe_cache_replace", lib().moe_cache_replace(self.h, n, ev, ad, src, _ptr(dev_tables),
+                                                            _stream(stream)))
+
     def close(self):
         if self.h:
             lib().moe_cache_destroy(self.h)
@@ -269,3 +282,25 @@ class SlotCache:
             self.close()
         except Exception:  # noqa: BLE001
             pass
+
+
+def moe_usage_accumulate(usage, counts, stream=None):
+    """usage[e] += counts[e] on the device (int32 tensors of E entries)."""
+    import torch
+    assert usage.dtype == torch.int32 and counts.dtype == torch.int32 and usage.numel() == counts.numel()
+    _check("moe_usage_accumulate", lib().moe_usage_accumulate(_ptr(usage), _ptr(counts), usage.numel(),
+                                                              _stream(stream)))
+
+
+def moe_cache_plan(resident, score, max_swaps, margin=0.0):
+    """Host replacement plan: returns (evict_ids, admit_ids) as int32 numpy arrays."""
+    import numpy as np
+    res = np.ascontiguousarray(resident, dtype=np.uint8)
+    sc = np.ascontiguousarray(score, dtype=np.float32)
+    assert res.shape == sc.shape and res.ndim == 1
+    ev = np.zeros(max(max_swaps, 1), dtype=np.int32)
+    ad = np.zeros(max(max_swaps, 1), dtype=np.int32)
+    n = C.c_int()
+    _check("moe_cache_plan", lib().moe_cache_plan(res.size, res.ctypes.data, sc.ctypes.data, max_swaps,
+                                                  float(margin), ev.ctypes.data, ad.ctypes.data, C.byref(n)))
+    return ev[:n.value].copy(), ad[:n.value].copy()

@@ -6,6 +6,9 @@
 // ~4,500 experts by a usage ranking into GPU memory; "Strata benchmarks"
 // (prefill optimisation table) streams the next layer's experts over PCIe
 // while the current layer computes.
+#include <algorithm>
+#include <cmath>
+#include <numeric>
 #include <vector>
 
 #include "common.hpp"
@@ -19,9 +22,17 @@ struct moe_cache {
     void** tables;                       // pinned host [n_layers][E] pointer tables
     std::vector<hipEvent_t> table_done;  // per layer: last upload of its table
     std::vector<bool> table_pending;
+    std::vector<bool> table_written;     // the pinned table of the layer holds a full mapping
 };
 
 using namespace moe;
+
+// per-expert selection counter of one layer (wrapping int32)
+__global__ __launch_bounds__(256) static void usage_accumulate(int32_t* __restrict__ usage,
+                                                              const int32_t* __restrict__ counts, int E) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e < E) usage[e] = (int32_t)((uint32_t)usage[e] + (uint32_t)counts[e]);
+}
 
 static int hip_fail(hipError_t e) {
     set_last_hip_error(e);
@@ -47,6 +58,7 @@ int moe_cache_create(moe_cache** cache, int n_layers, int E, int n_slots, size_t
     if (e != hipSuccess) { delete c; return hip_fail(e); }
     c->table_done.assign(n_layers, nullptr);
     c->table_pending.assign(n_layers, false);
+    c->table_written.assign(n_layers, false);
     for (int l = 0; l < n_layers; ++l) {
         e = hipEventCreateWithFlags(&c->table_done[l], hipEventDisableTiming);
         if (e != hipSuccess) { moe_cache_destroy(c); return hip_fail(e); }
@@ -140,6 +152,7 @@ int moe_cache_stage(moe_cache* c, int layer, int buf, const void* const* host_sr
     err = hipEventRecord(c->table_done[layer], st);
     if (err != hipSuccess) return hip_fail(err);
     c->table_pending[layer] = true;
+    c->table_written[layer] = true;
     if (done) {
         err = hipEventRecord(reinterpret_cast<hipEvent_t>(done), st);
         if (err != hipSuccess) return hip_fail(err);
@@ -175,9 +188,97 @@ int moe_cache_map_host(moe_cache* c, int layer, const void* const* host_src, voi
     err = hipEventRecord(c->table_done[layer], st);
     if (err != hipSuccess) return hip_fail(err);
     c->table_pending[layer] = true;
+    c->table_written[layer] = true;
     if (done) {
         err = hipEventRecord(reinterpret_cast<hipEvent_t>(done), st);
         if (err != hipSuccess) return hip_fail(err);
+    }
+    return MOE_OK;
+}
+
+int moe_usage_accumulate(int32_t* usage, const int32_t* counts, int E, moe_stream_t s) {
+    if (!usage || !counts || E < 1) return MOE_ERR_INVALID_ARG;
+    usage_accumulate<<<(E + 255) / 256, 256, 0, as_stream(s)>>>(usage, counts, E);
+    return check_launch();
+}
+
+int moe_cache_plan(int n_total, const uint8_t* resident, const float* score, int max_swaps, float margin,
+                   int32_t* evict_ids, int32_t* admit_ids, int* n_swaps) {
+    if (n_total < 1 || !resident || !score || max_swaps < 0 || !n_swaps || !(margin >= 0.0f) ||
+        !std::isfinite(margin) || (max_swaps > 0 && (!evict_ids || !admit_ids)))
+        return MOE_ERR_INVALID_ARG;
+    std::vector<int32_t> in, out;
+    for (int g = 0; g < n_total; ++g) {
+        if (resident[g] > 1 || !(score[g] >= 0.0f) || !std::isfinite(score[g])) return MOE_ERR_INVALID_ARG;
+        (resident[g] ? in : out).push_back(g);
+    }
+    const int m = std::min<int>(max_swaps, (int)std::min(in.size(), out.size()));
+    // the m weakest residents (score ascending, lower id first) and the m
+    // strongest missing ids (score descending, lower id first)
+    auto weaker = [&](int32_t a, int32_t b) { return score[a] < score[b] || (score[a] == score[b] && a < b); };
+    auto stronger = [&](int32_t a, int32_t b) { return score[a] > score[b] || (score[a] == score[b] && a < b); };
+    std::partial_sort(in.begin(), in.begin() + m, in.end(), weaker);
+    std::partial_sort(out.begin(), out.begin() + m, out.end(), stronger);
+    int n = 0;
+    while (n < m && score[out[n]] > (1.0f + margin) * score[in[n]]) {
+        evict_ids[n] = in[n];
+        admit_ids[n] = out[n];
+        ++n;
+    }
+    *n_swaps = n;
+    return MOE_OK;
+}
+
+int moe_cache_replace(moe_cache* c, int n, const int32_t* evict_ids, const int32_t* admit_ids,
+                      const void* const* host_src, void** dev_tables, moe_stream_t s) {
+    if (!c || n < 0) return MOE_ERR_INVALID_ARG;
+    if (n == 0) return MOE_OK;
+    if (!evict_ids || !admit_ids || !host_src || !dev_tables) return MOE_ERR_INVALID_ARG;
+    const long total = (long)c->n_layers * c->E;
+    std::vector<char> seen(total, 0);
+    for (int i = 0; i < n; ++i) {
+        const int32_t v = evict_ids[i], a = admit_ids[i];
+        if (v < 0 || v >= total || a < 0 || a >= total || seen[v] || seen[a] || v == a) return MOE_ERR_INVALID_ARG;
+        seen[v] = seen[a] = 1;
+        if (c->slot_of[v] < 0 || c->slot_of[a] >= 0 || !host_src[v] || !host_src[a]) return MOE_ERR_INVALID_ARG;
+    }
+    // device addresses of the evicted experts' host blobs, before anything changes
+    std::vector<void*> vdev(n);
+    for (int i = 0; i < n; ++i) {
+        const hipError_t e = hipHostGetDevicePointer(&vdev[i], const_cast<void*>(host_src[evict_ids[i]]), 0);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    std::vector<char> touched(c->n_layers, 0);
+    for (int i = 0; i < n; ++i) {
+        touched[evict_ids[i] / c->E] = 1;
+        touched[admit_ids[i] / c->E] = 1;
+    }
+    for (int l = 0; l < c->n_layers; ++l)
+        if (touched[l] && c->table_pending[l]) {
+            const hipError_t e = hipEventSynchronize(c->table_done[l]);
+            if (e != hipSuccess) return hip_fail(e);
+            c->table_pending[l] = false;
+        }
+    const hipStream_t st = as_stream(s);
+    for (int i = 0; i < n; ++i) {
+        const int32_t v = evict_ids[i], a = admit_ids[i];
+        const int slot = c->slot_of[v];
+        char* dst = c->pool + (size_t)slot * c->eb;
+        const hipError_t e = hipMemcpyAsync(dst, host_src[a], c->eb, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) return hip_fail(e);
+        c->slot_of[v] = -1;
+        c->slot_of[a] = slot;
+        c->tables[v] = vdev[i];
+        c->tables[a] = dst;
+    }
+    for (int l = 0; l < c->n_layers; ++l) {
+        if (!touched[l] || !c->table_written[l]) continue;
+        hipError_t e = hipMemcpyAsync(dev_tables + (size_t)l * c->E, c->tables + (size_t)l * c->E,
+                                      sizeof(void*) * (size_t)c->E, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) return hip_fail(e);
+        e = hipEventRecord(c->table_done[l], st);
+        if (e != hipSuccess) return hip_fail(e);
+        c->table_pending[l] = true;
     }
     return MOE_OK;
 }

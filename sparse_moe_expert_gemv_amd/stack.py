@@ -17,6 +17,9 @@ layer computes ("Strata benchmarks", prefill optimisation table).  Here:
   it, so a decode pass needs no staging, no side stream and no host round trip
   (the pages' "single RTX 5090 runs a 125B model" report: only the experts the
   gating network picks are computed);
+* the residency can adapt (``AdaptiveResidency``): per-layer selection
+  counters on the device, aged into scores on the host, and swaps of the
+  weakest resident experts for the strongest missing ones;
 * the compute stream waits for layer l's staging event, then runs
   rmsnorm -> route -> permute -> quantise -> expert FFN (through the pointer
   table) -> combine with the residual: h_{l+1} = h_l + MoE_l(norm(h_l)).  The
@@ -88,6 +91,7 @@ class ExpertStack:
             for l in range(self.L):
                 self.cache.map_host(l, self.host_ptrs[l], self.tables[l])
         torch.cuda.synchronize()
+        self.usage = None  # [L, E] int32 selection counters once enable_usage() is called
         self.side = torch.cuda.Stream(device=self.device)
         self.staged = [torch.cuda.Event() for _ in range(self.L)]
         self.done = [torch.cuda.Event() for _ in range(self.L)]
@@ -113,6 +117,11 @@ class ExpertStack:
         self.xn = torch.empty((T, d), dtype=torch.float32, device=dev)
         self.ws = torch.empty(B.moe_workspace_size(T, d, f, E, k, self.act_mode), dtype=torch.uint8, device=dev)
 
+    def enable_usage(self):
+        """Count, per layer and expert, how often the routing selects it (device int32)."""
+        self.usage = torch.zeros((self.L, self.E), dtype=torch.int32, device=self.device)
+        return self.usage
+
     def misses(self, layer):
         return self.cache.lookup(layer)[1]
 
@@ -130,6 +139,8 @@ class ExpertStack:
         bias = None if self.bias is None else self.bias[l]
         B.moe_route_permute(xn, self.Wr[l], bias, k, self.ids[:T], self.gates[:T], self.counts, self.offsets,
                             self.sorted_idx[:n], self.dest[:n], self.active, self.ws, stream)
+        if self.usage is not None:
+            B.moe_usage_accumulate(self.usage[l], self.counts, stream)
         common = dict(T=T, d=self.d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
                       expert_ptrs=self.tables[l] if table is None else table, counts=self.counts,
                       offsets=self.offsets, sorted_idx=self.sorted_idx[:n], active=self.active,
@@ -193,6 +204,49 @@ class ExpertStack:
 
     def close(self):
         self.cache.close()
+
+
+class AdaptiveResidency:
+    """Host side of the adaptive expert cache ("How Strata works", adaptive
+    expert cache section: the cache keeps learning the session's hot experts).
+
+    Every update reads the device selection counters, ages them into scores
+    (score = decay * score + selections since the last update, in fp32), asks
+    moe_cache_plan for up to max_swaps (evict, admit) pairs and carries them
+    out with moe_cache_replace on the compute stream.  Work enqueued before an
+    update reads the old pool contents, work enqueued after it the new ones.
+    """
+
+    def __init__(self, stack: ExpertStack, decay=0.5, max_swaps=128, margin=0.0):
+        self.S = stack
+        self.decay, self.max_swaps, self.margin = np.float32(decay), int(max_swaps), float(margin)
+        n = stack.L * stack.E
+        self.usage = stack.usage if stack.usage is not None else stack.enable_usage()
+        self.prev = np.zeros(n, dtype=np.int64)
+        self.score = np.zeros(n, dtype=np.float32)
+        self.resident = np.zeros(n, dtype=np.uint8)
+        for l in range(stack.L):
+            for e in stack.cache.lookup(l)[0]:
+                self.resident[l * stack.E + e] = 1
+        self.host_all = [p for row in stack.host_ptrs for p in row]
+        self.swaps = 0
+        self.policy_s = 0.0  # host time in scoring, planning and enqueueing (after the counters arrive)
+
+    def update(self, stream=None):
+        """One policy step; returns the number of swaps enqueued."""
+        now = self.usage.reshape(-1).cpu().numpy().astype(np.int64)
+        t0 = time.perf_counter()
+        delta = (now - self.prev) & 0xFFFFFFFF  # counters wrap modulo 2^32
+        self.prev = now
+        self.score = self.score * self.decay + delta.astype(np.float32)
+        ev, ad = B.moe_cache_plan(self.resident, self.score, self.max_swaps, self.margin)
+        if len(ev):
+            self.S.cache.replace(ev, ad, self.host_all, self.S.tables, stream)
+            self.resident[ev] = 0
+            self.resident[ad] = 1
+            self.swaps += len(ev)
+        self.policy_s += time.perf_counter() - t0
+        return len(ev)
 
 
 def build_host_store(pool_canonical: np.ndarray, wfmt: int, d: int, f: int, device="cuda") -> torch.Tensor:

@@ -284,3 +284,59 @@ def test_full_decode_stack_48_layers():
     sel = np.concatenate([res[l][ids_l[l].cpu().numpy().ravel()] for l in range(c.n_layers)])
     assert 0.55 < sel.mean() < 0.9, sel.mean()
     G.close()
+
+
+def test_small_decode_stack_adaptive_residency():
+    """The session routes by another profile than the one the pool was filled
+    from.  Usage counters match the routing exactly; periodic swaps keep the
+    cache's bookkeeping, the pointer tables and the pool contents consistent
+    (every layer bit-identical to a plain device copy of its experts), and the
+    adapted pool serves clearly more selections than the static one."""
+    from sparse_moe_expert_gemv_amd.stack import AdaptiveResidency
+    S = synth.make_stack(name="decode_stack", overrides=DSMALL)
+    c = S.cfg
+    G = _decode_stack_gpu(S)
+    rank_b = synth.stack_profile(1, c.n_layers, c.E)
+    for l in range(c.n_layers):
+        G.bias[l].copy_(torch.from_numpy(synth.profile_router_bias(rank_b, l, c.E, c.profile_bias)))
+    A = AdaptiveResidency(G, decay=0.5, max_swaps=16)
+    res0 = A.resident.copy()
+    static_hits, adaptive_hits = [], []
+    for step in range(24):
+        x = torch.from_numpy(synth.bf16_bits_to_f32(synth.gen_x(0, c, layer=0, draw=step))).to(DEV)
+        before = G.usage.cpu().numpy().copy()
+        ids_l = []
+        G.forward(x, ids_out=ids_l)
+        torch.cuda.synchronize()
+        after = G.usage.cpu().numpy()
+        cur = A.resident.copy()
+        for l in range(c.n_layers):
+            ids = ids_l[l].cpu().numpy().ravel()
+            assert np.array_equal(after[l] - before[l], np.bincount(ids, minlength=c.E)), (step, l)
+            static_hits.append(res0[ids + l * c.E])
+            adaptive_hits.append(cur[ids + l * c.E])
+        if step % 2 == 1:
+            A.update()
+    torch.cuda.synchronize()
+    assert A.swaps > 0
+    for l in range(c.n_layers):
+        hit, _ = G.cache.lookup(l)
+        assert hit == [e for e in range(c.E) if A.resident[l * c.E + e]]
+    tail = c.n_layers * 8
+    s_rate = np.concatenate(static_hits[-tail:]).mean()
+    a_rate = np.concatenate(adaptive_hits[-tail:]).mean()
+    assert a_rate > s_rate + 0.1, (a_rate, s_rate)
+    x = _x0(S)
+    for l in range(c.n_layers):
+        plain = pack_blobs(torch.from_numpy(S.layer_experts(l)).to(DEV), c.wfmt, c.d, c.f)
+        out_a = torch.empty_like(x)
+        out_b = torch.empty_like(x)
+        G.layer(l, x, out_a)
+        G.layer(l, x, out_b, table=pointer_table(plain))
+        torch.cuda.synchronize()
+        assert torch.equal(out_a, out_b), "layer %d" % l
+    tables = G.tables.cpu().numpy()
+    pool_lo = G.pool.data_ptr()
+    in_pool = (tables >= pool_lo) & (tables < pool_lo + G.pool.numel())
+    assert np.array_equal(in_pool.ravel(), A.resident.astype(bool))
+    G.close()
