@@ -33,8 +33,10 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# per-file extra flags: the int8 FFN keeps MFMA results in VGPRs (its epilogue reads every element)
-FILE_FLAGS = {"ffn_q8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# per-file extra flags: MFMA results stay in VGPRs, since the epilogues read every element
+# (the int8 FFN after each block, the decode gate/up after each block's seeded sum)
+FILE_FLAGS = {"ffn_q8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "ffn_float.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -343,11 +343,12 @@ __global__ __launch_bounds__(256) void ffn_float_down(const _Float16* __restrict
 // S wavefronts (2 or 4) split its reduction (NT tiles each) and
 // software-pipeline their quant tiles two ahead, so that loads of later tiles
 // overlap the products of earlier ones.  S = 4 when few experts are active,
-// so that enough loads are in flight.  Each block of 8 weights becomes (q - 8) * s in
-// fp16 with one rounding: the low nibbles of a byte through the 0x6400 magic
-// (1024 + q), the high nibbles in place (1024 + 16 q) rescaled by an exact
-// fma, then one multiply by the block scale; the MFMA then accumulates the
-// scaled products of all blocks in fp32.
+// so that enough loads are in flight.  The quants enter the MFMA raw (one
+// v_and_or_b32 per pair: 1024 + q, or 1024 + 16 q for the high nibbles, whose
+// token values are staged divided by 16); a third MFMA of the same A with a
+// constant B seeds each block's sum so that the offsets cancel exactly, and
+// the exact block sum x . (q - 8) is scaled by the row's block scale in fp32
+// (one v_fma_mix per output and block).
 
 // (q - 8) * s for the 8 nibbles of one int4 dword ([k0 k2 k4 k6 k1 k3 k5 k7])
 __device__ __forceinline__ half8 dequant4_scaled(uint32_t v, half2v s2, uint32_t mlo, uint32_t mhi,
@@ -364,11 +365,36 @@ __device__ __forceinline__ half8 dequant4_scaled(uint32_t v, half2v s2, uint32_t
     return half8{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
 }
 
+// fp16 scale of block b (of 4) of an int4 tile row, as fp32
+__device__ __forceinline__ float scale_f32(const uint2v& raw, int b) {
+    const uint32_t w = b < 2 ? raw[0] : raw[1];
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)((b & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
+
 // fp16 scale of block b (of 4) of an int4 tile row, broadcast to both halves
 __device__ __forceinline__ half2v scale_pair(const uint2v& raw, int b) {
     const uint32_t w = b < 2 ? raw[0] : raw[1];
     const uint32_t hb = (b & 1) ? (w >> 16) : (w & 0xFFFFu);
     return as_h2(hb | (hb << 16));
+}
+
+// int4 quants as raw fp16 words, without offset or scale: 1024 + q for the
+// low nibbles (k0 k1, k4 k5 of the dword) and 1024 + 16 q for the high ones
+// (k2 k3, k6 k7); one v_and_or_b32 per pair
+__device__ __forceinline__ half8 raw4(uint32_t v, uint32_t mlo, uint32_t mhi, uint32_t magic) {
+    const uint32_t v8 = v >> 8;
+    return __builtin_bit_cast(half8, uint4v{(v & mlo) | magic, (v & mhi) | magic, (v8 & mlo) | magic, (v8 & mhi) | magic});
+}
+
+// Seed of the raw block products: with the token values at the high-nibble
+// positions (k2 k3 k6 k7 of every 8) staged divided by 16, a block's raw MFMA
+// sum is sum x (1024 + q) over the low positions plus sum (x / 16)(1024 + 16 q)
+// over the high ones; the products of the same A with this constant B,
+// -1032 and -1152 per position, remove exactly the offsets (1024 + 8 and
+// 16 (64 + 8)), leaving sum x (q - 8).  All values are exact in fp16.
+__device__ __forceinline__ half8 offset_seed_b() {
+    const _Float16 lo = (_Float16)-1032.0f, hi = (_Float16)-1152.0f;
+    return half8{lo, lo, hi, hi, lo, lo, hi, hi};
 }
 
 constexpr int kTokMax = 16;   // tokens of the token-dense kernels
@@ -377,6 +403,12 @@ constexpr int kPipe = 2;      // quant tiles in flight ahead of the products
 // Raw 16-byte token chunks, converted to fp16 only when stored to LDS, so that
 // the loads can be issued before anything else without waiting on them.
 template <typename XT> struct XChunk;
+// a token chunk with elements 2, 3, 6, 7 divided by 16 (exact in fp16)
+__device__ __forceinline__ half8 pre16(half8 v) {
+    const half2v r = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2v a = half2v{v[2], v[3]} * r, b = half2v{v[6], v[7]} * r;
+    return half8{v[0], v[1], a.x, a.y, v[4], v[5], b.x, b.y};
+}
 template <> struct XChunk<uint16_t> {
     uint4v r;
     __device__ __forceinline__ void load(const uint16_t* p) { r = gload(reinterpret_cast<const uint4v*>(p)); }
@@ -389,6 +421,7 @@ template <> struct XChunk<uint16_t> {
         }
         return v;
     }
+    __device__ __forceinline__ half8 cvt_pre16() const { return pre16(cvt()); }
 };
 template <> struct XChunk<float> {
     uint4v a, b;
@@ -405,12 +438,14 @@ template <> struct XChunk<float> {
         }
         return v;
     }
+    __device__ __forceinline__ half8 cvt_pre16() const { return pre16(cvt()); }
 };
 
 template <> struct XChunk<_Float16> {
     uint4v r;
     __device__ __forceinline__ void load(const _Float16* p) { r = gload(reinterpret_cast<const uint4v*>(p)); }
     __device__ __forceinline__ half8 cvt() const { return __builtin_bit_cast(half8, r); }
+    __device__ __forceinline__ half8 cvt_pre16() const { return pre16(cvt()); }
 };
 
 // Buffer resource over [base, base + bytes): loads through it are bounds
@@ -434,7 +469,8 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
                                                         const int32_t* __restrict__ sorted_idx,
                                                         const int32_t* __restrict__ active, _Float16* __restrict__ h) {
     extern __shared__ __align__(16) uint4 xs4[];  // [T][d / 8] fp16, chunk c of row r at (c ^ r); later [4][2][4][64] f32
-    const int XC = d / 8;
+    const int XC = d / 8;           // a power of two (checked by the launcher)
+    const int lxc = __builtin_ctz(XC);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int part = wave % S;
@@ -476,13 +512,13 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
         qg[i] = ld4(og + i * 1024);
         qu[i] = ld4(ou + i * 1024);
     }
-    // tokens -> LDS as fp16
+    // tokens -> LDS as fp16, the high-nibble positions divided by 16
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int idx = (int)threadIdx.x + j * 256;
         if (idx < nx) {
-            const int r = idx / XC, cc = idx % XC;
-            xs4[r * XC + (cc ^ r)] = __builtin_bit_cast(uint4, xr[j].cvt());
+            const int r = idx >> lxc, cc = idx & (XC - 1);
+            xs4[r * XC + (cc ^ r)] = __builtin_bit_cast(uint4, xr[j].cvt_pre16());
         }
     }
     for (int base = 1024; base < nx; base += 1024) {
@@ -493,13 +529,15 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
         for (int j = 0; j < 4; ++j) {
             const int idx = base + (int)threadIdx.x + j * 256;
             if (idx < nx) {
-                const int r = idx / XC, cc = idx % XC;
-                xs4[r * XC + (cc ^ r)] = __builtin_bit_cast(uint4, xq[j].cvt());
+                const int r = idx >> lxc, cc = idx & (XC - 1);
+                xs4[r * XC + (cc ^ r)] = __builtin_bit_cast(uint4, xq[j].cvt_pre16());
             }
         }
     }
     __syncthreads();
     float4v accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+    const half8 Bc = offset_seed_b();
+    const float4v zero4 = {0, 0, 0, 0};
     {
         const int rr = min(lane & 15, T - 1);
         // bit masks and magic in registers so that each extraction is one v_and_or_b32
@@ -517,12 +555,19 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const half8 Bg = dequant4_scaled(qg[i][b], scale_pair(sg[i], b), mlo, mhi, magic);
-                const half8 Bu = dequant4_scaled(qu[i][b], scale_pair(su[i], b), mlo, mhi, magic);
                 const int kk = ((part * NT + i) * 4 + b) * 32 + 8 * (lane >> 4);
                 const half8 A = __builtin_bit_cast(half8, xs4[rr * XC + ((kk >> 3) ^ rr)]);
-                accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bg, accg, 0, 0, 0);
-                accu = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bu, accu, 0, 0, 0);
+                // exact block sums x . (q - 8): raw quants seeded with A . Bc,
+                // then scaled by the row's block scale in fp32
+                const float4v dc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bc, zero4, 0, 0, 0);
+                const float4v dg = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, raw4(qg[i][b], mlo, mhi, magic), dc, 0, 0, 0);
+                const float4v du = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, raw4(qu[i][b], mlo, mhi, magic), dc, 0, 0, 0);
+                const float sgb = scale_f32(sg[i], b), sub = scale_f32(su[i], b);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    accg[r] = fmaf(dg[r], sgb, accg[r]);
+                    accu[r] = fmaf(du[r], sub, accu[r]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1041,7 +1086,8 @@ static int run_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     const size_t lds1 = std::max<size_t>((size_t)rows_lds * a->d * sizeof(_Float16), 4 * 2 * 4 * 64 * sizeof(float));
     if (a->phase != 2) {
         // token-dense kernel for small int4 batches; the token tile of d fp16 values per token fits in LDS
-        const bool tok16 = WFMT == MOE_WFMT_I4B32 && a->T <= kTokMax && (size_t)a->T * a->d * 2 <= 64 * 1024;
+        const bool tok16 = WFMT == MOE_WFMT_I4B32 && a->T <= kTokMax && (size_t)a->T * a->d * 2 <= 64 * 1024 &&
+                           (a->d & (a->d - 1)) == 0;
         const bool tok64 = !tok16 && a->T <= kTok64;
         if (!(tok16 && launch_gateup_tok16<XT>(a, h, slots, s)) && !(tok64 && launch_gateup_tok64<WFMT, XT>(a, h, slots, s)))
             ffn_float_gateup<WFMT, XT><<<g1, 256, lds1, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs,
