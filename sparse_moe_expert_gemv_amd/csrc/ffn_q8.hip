@@ -9,7 +9,9 @@
 // prefill optimisation table); here the int4 weights become int8 while they
 // are staged in LDS, once per workgroup and k-chunk.
 //
-// Block sums are exact integers |P| < 2^22.  The MFMA accumulator is seeded
+// Block sums are exact integers |P| < 2^22 (the tiled int4 kernels stage the
+// quants as 16 q and the scales as s / 16; 16 |P| <= 16 * 32 * 127 * 8 is
+// still below 2^22).  The MFMA accumulator is seeded
 // with the bit pattern of 1.5 * 2^23, so the int32 result read as fp32 is
 // exactly 1.5 * 2^23 + P.  With the weight row's block scale sw constant per
 // lane, t = fma(D, sw, -1.5 * 2^23 * sw) = sw * P (one rounding; the constant
@@ -386,14 +388,16 @@ __global__ __launch_bounds__(1024) void q8_tile_plan(const int32_t* __restrict__
     }
 }
 
-// 16 bytes of a packed int4 lane word (one 32-block per dword) -> signed int8, k order
-__device__ __forceinline__ void int4_word_to_i8(uint32_t v, uint32_t& w0, uint32_t& w1) {
-    const uint32_t lo = v & 0x0F0F0F0Fu;         // bytes: k0 k4 k1 k5
-    const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;  // bytes: k2 k6 k3 k7
-    w0 = (lo & 0xFFu) | ((lo >> 8) & 0xFF00u) | ((hi & 0xFFu) << 16) | ((hi << 8) & 0xFF000000u);
-    w1 = ((lo >> 8) & 0xFFu) | ((lo >> 16) & 0xFF00u) | ((hi << 8) & 0xFF0000u) | (hi & 0xFF000000u);
-    w0 = (w0 + 0x78787878u) ^ 0x80808080u;
-    w1 = (w1 + 0x78787878u) ^ 0x80808080u;
+// One packed int4 word (offset binary u = q + 8, nibbles k0 k2 k4 k6 k1 k3 k5
+// k7) -> eight int8 bytes in k order holding 16 q: u ^ 8 is the 4-bit two's
+// complement of q, so with it in the high half of a byte the byte read as int8
+// is exactly 16 q.  Five operations; the factor 16 is taken out of the weight
+// block scale (exact in fp32).
+__device__ __forceinline__ void int4_word_to_i8x16(uint32_t v, uint32_t& w0, uint32_t& w1) {
+    const uint32_t hi = (v ^ 0x88888888u) & 0xF0F0F0F0u;         // bytes: k2 k6 k3 k7
+    const uint32_t lo = ((v << 4) ^ 0x88888888u) & 0xF0F0F0F0u;  // bytes: k0 k4 k1 k5
+    w0 = __builtin_amdgcn_perm(hi, lo, 0x06040200u);              // k0 k1 k2 k3
+    w1 = __builtin_amdgcn_perm(hi, lo, 0x07050301u);              // k4 k5 k6 k7
 }
 
 // MODE 0: gate/up, A = x (int8 per 32-block), output h requantised; MODE 1: down, A = h, output y
@@ -476,20 +480,21 @@ __global__ __launch_bounds__(256) void ffn_q8_tiled(const int8_t* __restrict__ a
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 uint32_t w0, w1;
-                int4_word_to_i8(rw[q][b], w0, w1);
+                int4_word_to_i8x16(rw[q][b], w0, w1);
                 const int ch = 2 * b + (kq >> 1);
                 uint2* dst = reinterpret_cast<uint2*>(&S.w[row][ch ^ (row & 7)]) + (kq & 1);
                 *dst = make_uint2(w0, w1);
             }
         }
         if (threadIdx.x < 128) {
-            // fp16 scales by integer extraction (a bit cast of a vector element to a half pair is avoided)
+            // fp16 scales by integer extraction (a bit cast of a vector element to a half pair is avoided),
+            // divided by 16 for the staged quants 16 q
             const int row = threadIdx.x;
             const uint32_t w01 = rsw[0], w23 = rsw[1];
-            S.sw[0][row] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w01 & 0xFFFFu));
-            S.sw[1][row] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w01 >> 16));
-            S.sw[2][row] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w23 & 0xFFFFu));
-            S.sw[3][row] = (float)__builtin_bit_cast(_Float16, (unsigned short)(w23 >> 16));
+            S.sw[0][row] = 0.0625f * (float)__builtin_bit_cast(_Float16, (unsigned short)(w01 & 0xFFFFu));
+            S.sw[1][row] = 0.0625f * (float)__builtin_bit_cast(_Float16, (unsigned short)(w01 >> 16));
+            S.sw[2][row] = 0.0625f * (float)__builtin_bit_cast(_Float16, (unsigned short)(w23 & 0xFFFFu));
+            S.sw[3][row] = 0.0625f * (float)__builtin_bit_cast(_Float16, (unsigned short)(w23 >> 16));
         }
         if (threadIdx.x < kTM * 32) {
 #pragma unroll
