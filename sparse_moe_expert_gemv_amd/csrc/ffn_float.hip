@@ -785,7 +785,7 @@ size_t float_h_bytes(int T, int f, int k) { return ((size_t)T * k + T) * (size_t
 // h rows (contiguous, at most 64 per pass) as the A operand.
 constexpr int kTok64 = 64;
 constexpr int kKC = 128;     // k per chunk
-constexpr int kPipe64 = 4;   // gate/up chunks in flight ahead of the products (few workgroups: registers are free)
+constexpr int kPipe64 = 2;   // gate/up chunks in flight ahead of the products (three wavefronts per SIMD fit)
 
 // (q) * s for the 8 int8 weights of one block (two dwords in k order, q stored
 // as q + 128): bytes are paired with the 0x64 magic byte by v_perm_b32
@@ -858,7 +858,7 @@ struct RowChunk {
 };
 
 template <int WFMT, typename XT, int NCH>
-__global__ __launch_bounds__(256) void ffn_gateup_tok64(const XT* __restrict__ x, int T, int d, int f, int k, int E,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void ffn_gateup_tok64(const XT* __restrict__ x, int T, int d, int f, int k, int E,
                                                         const void* const* __restrict__ expert_ptrs,
                                                         const uint8_t* __restrict__ shared_blob,
                                                         const int32_t* __restrict__ counts,

@@ -356,3 +356,26 @@ def test_duplicate_expert_ids_through_permute_ffn_combine(name, T):
     if L.shared is not None:
         ref += oracle.expert_ffn(xf, L.shared, c.wfmt, c.f, oracle.ACT_FLOAT)
     check_float(host(G.out[:T]), ref, "%s duplicate ids" % name)
+
+
+@pytest.mark.parametrize("d", [132, 136, 2048])
+def test_combine_fp16_rows_equal_fp32_rows(d):
+    """moe_combine on fp16 expert rows (eight outputs per thread when d % 8 == 0,
+    four otherwise) equals, bit for bit, moe_combine on the same rows widened
+    to fp32: the same products summed in the same order."""
+    rng = np.random.default_rng(d)
+    T, k = 37, 5
+    n = T * k
+    y16 = torch.from_numpy(rng.standard_normal((n, d)).astype(np.float16)).cuda()
+    y32 = y16.float()
+    dest = torch.from_numpy(rng.permutation(n).astype(np.int32)).cuda()
+    gates = torch.from_numpy(rng.random((T, k)).astype(np.float32)).cuda()
+    ysh = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).cuda()
+    res = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).cuda()
+    for sh, r in ((None, None), (ysh, res)):
+        a = torch.empty((T, d), dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        B.moe_combine(y16, dest, gates, sh, r, a)
+        B.moe_combine(y32, dest, gates, sh, r, b)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
