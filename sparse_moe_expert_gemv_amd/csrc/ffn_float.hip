@@ -207,7 +207,6 @@ __global__ __launch_bounds__(256) void ffn_float_gateup(const XT* __restrict__ x
                                                         const int32_t* __restrict__ sorted_idx,
                                                         const int32_t* __restrict__ active, _Float16* __restrict__ h) {
     constexpr int KPT = WFMT == MOE_WFMT_I4B32 ? 128 : 64;
-    constexpr int NB = KPT / 32;
     constexpr int kMaxT = kChunkK / KPT;
     // LDS: 16 activation rows of d fp16, 16-byte chunk c of row r stored at
     // chunk (c ^ r) so the 16 rows read by one MFMA operand hit distinct banks;
@@ -219,7 +218,6 @@ __global__ __launch_bounds__(256) void ffn_float_gateup(const XT* __restrict__ x
     const int n_strips = f / 16;
     const int nkt = d / KPT;
     const int kt_lo = (wave * nkt) / 4, kt_hi = ((wave + 1) * nkt) / 4;
-    const int nt0 = min(kMaxT, kt_hi - kt_lo);
     const int n_active = active[0];
     const int n_items = (n_active + (shared_blob ? 1 : 0)) * n_strips;
     const ExpertLayout L = expert_layout(WFMT, d, f);
@@ -288,7 +286,6 @@ __global__ __launch_bounds__(256) void ffn_float_down(const _Float16* __restrict
                                                       const int32_t* __restrict__ active, YT* __restrict__ y_perm,
                                                       float* __restrict__ y_shared) {
     constexpr int KPT = WFMT == MOE_WFMT_I4B32 ? 128 : 64;
-    constexpr int NB = KPT / 32;
     constexpr int kMaxT = kChunkK / KPT;
     extern __shared__ __align__(16) uint4 hs4[];  // [16][f / 8], chunk c of row r at (c ^ r)
     const int HC = f / 8;
@@ -298,7 +295,6 @@ __global__ __launch_bounds__(256) void ffn_float_down(const _Float16* __restrict
     const int n_items = (n_active + (shared_blob ? 1 : 0)) * n_groups;
     const ExpertLayout L = expert_layout(WFMT, d, f);
     const int nkt = L.dn.nkt;
-    const int nt0 = min(kMaxT, nkt);
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int grp = item % n_groups;
         const SlotInfo S = slot_info(item / n_groups, n_active, active, expert_ptrs, shared_blob, counts, offsets,

@@ -29,7 +29,6 @@ template <>
 __device__ __forceinline__ float load_xf<uint16_t>(const uint16_t* x, size_t i) { return bf16_bits_to_float(x[i]); }
 
 // ---------------------------------------------------------------- top-k ----
-constexpr int kMaxPerLane = 16;  // E <= 1024
 
 // Iterative wave argmax: k rounds of (lane best, wave best).  Exact; used when
 // the threshold filter below leaves more than 64 candidates.
