@@ -3,20 +3,26 @@
 // Matrix-core formulation of the bandwidth-bound expert GEMV: a wavefront owns
 // a strip of 16 weight rows and multiplies it with up to 16 tokens per
 // v_mfma_f32_16x16x32_f16 (A = 16 tokens x 32 k, B = 32 k x 16 weight rows,
-// one instruction per 32-wide quantisation block).  Weights are dequantised in
-// registers to exact fp16 integers (int4: 0x6400|u is 1024+u, minus 1032;
-// int8: 0x6400|(q+128) minus 1152); activations are rounded to fp16 once,
-// when a workgroup stages them in LDS; each block's exact-integer-weighted
-// product is scaled by the block's fp16 scale in fp32 (acc += s_b * D_b).
+// one instruction per 32-wide quantisation block).  Weights become exact fp16
+// integers in registers (int4: 0x6400|u is 1024+u; int8: 0x6400|(q+128) is
+// 1024+q+128); activations are rounded to fp16 once, when a workgroup stages
+// them in LDS.  Three kernel families, chosen per call by run_float:
 //
-// gate/up: work item = (expert, 16 rows of f); the four wavefronts of a
-// workgroup split the reduction, each issuing all of its weight loads before
-// any math, and meet in LDS (fixed order, deterministic) to form
-// h = silu(g) * u in fp16.  down: work item = (expert, 64 output rows); each
-// wavefront holds the whole reduction length of its 16 rows in registers.
-// Activations / h rows of the current 16-token tile are staged once per
-// workgroup in LDS with 16-byte loads (d <= 2048 keeps 16 rows within 64 KiB).
-// Items are grid-strided over device-side counts: no host synchronisation.
+//  * T <= 16, int4 (decode): ffn_gateup_tok16 / ffn_down_tok16.  Every token
+//    is a row of A, so a work item (slot, 16-row strip) needs no gather.
+//    Gate/up feeds the raw quants to the MFMA and cancels their offsets with
+//    a seed MFMA, then scales each exact block sum in fp32; down builds
+//    (q - 8) * s in fp16 before its MFMA.
+//  * T <= 64 (moderate batches, either weight format): ffn_gateup_tok64 /
+//    ffn_down_tok64, the same token-dense idea with four 16-token m-tiles.
+//  * otherwise: ffn_float_gateup / ffn_float_down, which gather each slot's
+//    rows 16 at a time; the four wavefronts of a gate/up workgroup split the
+//    reduction and meet in LDS (fixed order, deterministic); the down kernel
+//    keeps a strip's whole reduction in registers.  Both scale each block's
+//    exact-integer-weighted product in fp32 (acc += s_b * D_b).
+//
+// Items are derived from device-side counts and the active-expert list: no
+// host synchronisation.
 #include "common.hpp"
 
 namespace moe {

@@ -5,13 +5,16 @@
 // RTX 5090 runs a 125B model": a light gating network picks the top-K
 // experts per token; the others do not compute).
 //
-// Small and moderate batches: every wavefront computes one router row against
-// a group of up to 8 tokens staged in LDS; for small batches a single
-// workgroup then selects the top-k of every token and, when asked, also groups
-// the routing slots by expert (the moe_permute outputs), so decode routing is
-// two launches.  A device-wide last-workgroup election would need an
-// agent-scope release per workgroup, which on this multi-die part writes back
-// the L2 each time; the kernel boundary is cheaper.
+// Logits by batch size: T <= 8, one wavefront per router row against all
+// tokens (route_logits_wave); 8 < T <= 256, 16 x 16 tiles on fp64 MFMA with
+// the reduction split over sixteen wavefronts (route_logits_splitk); larger
+// T, 64 x 128 tiles on fp64 MFMA (route_logits_mfma); route_logits_rows covers
+// widths the split-k kernel is not instantiated for.  For up to 64 tokens and
+// 512 slots a single workgroup then selects the top-k of every token and,
+// when asked, also groups the routing slots by expert (the moe_permute
+// outputs), so decode routing is two launches.  A device-wide last-workgroup
+// election would need an agent-scope release per workgroup, which on this
+// multi-die part writes back the L2 each time; the kernel boundary is cheaper.
 #include <float.h>
 
 #include <algorithm>
