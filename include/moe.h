@@ -197,12 +197,18 @@ typedef struct moe_ffn_args {
 
 /*
  * Grouped SwiGLU expert FFN over the rows grouped by moe_permute, plus the
- * shared expert over all T tokens.  Block-32 weights are dequantised in
- * registers.  MOE_ACT_FLOAT: fp32 accumulation (fp16 matrix-core products of
- * exact weight integers and fp16-rounded activations, per-block scales applied
- * in fp32).  MOE_ACT_Q8: int8 x int8 matrix cores with exact per-block
- * integer sums; the SwiGLU intermediate is requantised to int8 per 32 features
- * before the down projection.
+ * shared expert over all T tokens ("How Strata works", three-tier division:
+ * 10 of 24,576 small experts per token plus a resident shared expert).
+ * Block-32 weights are dequantised in registers.  MOE_ACT_FLOAT: fp16
+ * matrix-core products with fp32 accumulation; activations and the SwiGLU
+ * intermediate h are rounded to fp16 once.  The weight block scale is applied
+ * in fp32 to each exact block sum by the int4 gate/up kernel for T <= 16 and
+ * by the general kernels (T > 64); the other small-batch kernels fold it into
+ * the weights, rounding each (q - 8) * s to fp16 once (relative error at most
+ * 2^-11 per weight).  MOE_ACT_Q8: int8 x int8 matrix cores with exact
+ * per-block integer sums, both block scales applied in fp32; the SwiGLU
+ * intermediate is requantised to int8 per 32 features before the down
+ * projection.
  */
 int moe_expert_ffn(const moe_ffn_args* args, moe_stream_t stream);
 
