@@ -169,6 +169,30 @@ def test_ragged_token_counts_and_float_mode_large_batch():
     check_float(out, o["out"], "T=77 float")
 
 
+@pytest.mark.parametrize("T", [8, 9, 16, 17, 64, 65, 256, 257, 409, 410])
+def test_dispatch_boundaries_decode_layer(T):
+    """The decode-shaped layer (int4 + shared, float mode) at token counts on
+    both sides of every kernel switch: router logits (T <= 8 one wavefront per
+    row, <= 256 split-k fp64 MFMA, then tiled fp64 MFMA), single-workgroup
+    selection (T <= 64, T*k <= 512), one-workgroup permutation (T*k <= 4096),
+    and the FFN families (T <= 16 token-dense int4, <= 64 token-dense, then
+    gathered rows).  Routing bit-exact, outputs within tolerance."""
+    L = synth.make_layer("decode_t4", T=T)
+    G, out, st, o = run_layer(L)
+    check_routing(st, o, L.cfg.E)
+    check_float(out, o["out"], "decode layer T=%d" % T)
+
+
+@pytest.mark.parametrize("T", [5, 300])
+def test_q8_mode_small_and_mid_batches(T):
+    """int8-activation mode on the decode-shaped layer with few tokens per
+    expert: tiles of one or two rows, and the shared expert's tile of all T."""
+    L = synth.make_layer("decode_t4", T=T, overrides={"act_mode": "q8"})
+    G, out, st, o = run_layer(L)
+    check_routing(st, o, L.cfg.E)
+    check_float(out, o["out"], "q8 T=%d" % T)
+
+
 def test_one_expert_takes_every_token_q8():
     """Router bias forces one expert into every token's top-k (count = T = 300
     > one 128-token tile) in int8 mode; ties elsewhere still resolve to the
