@@ -345,7 +345,9 @@ __global__ __launch_bounds__(256) void ffn_float_down(const _Float16* __restrict
 // S wavefronts (2 or 4) split its reduction (NT tiles each) and
 // software-pipeline their quant tiles two ahead, so that loads of later tiles
 // overlap the products of earlier ones.  S = 4 when few experts are active,
-// so that enough loads are in flight.  The quants enter the MFMA raw (one
+// so that enough loads are in flight (one item per 256-thread workgroup);
+// with S = 2 a 512-thread workgroup takes four items, so the token tile is
+// converted and staged once per four items.  The quants enter the MFMA raw (one
 // v_and_or_b32 per pair: 1024 + q, or 1024 + 16 q for the high nibbles, whose
 // token values are staged divided by 16); a third MFMA of the same A with a
 // constant B seeds each block's sum so that the offsets cancel exactly, and
@@ -462,8 +464,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 // through buffer resources of size 0 when there is nothing to read, so that
 // the code stays straight-line and every wait is exact; only then the tokens
 // go to LDS.
-template <int NT, int S, typename XT>
-__global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x, int T, int d, int f, int k, int E,
+template <int NT, int S, typename XT, int NTH = 256>
+__global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x, int T, int d, int f, int k, int E,
                                                         const void* const* __restrict__ expert_ptrs,
                                                         const uint8_t* __restrict__ shared_blob,
                                                         const int32_t* __restrict__ counts,
@@ -477,12 +479,12 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int part = wave % S;
     const int n_strips = f / 16;
-    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * (4 / S) + wave / S);
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * (NTH / 64 / S) + wave / S);
     const int a = item / n_strips, strip = item % n_strips;
     const int nx = T * XC;
     XChunk<XT> xr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xr[j].load(x + (size_t)min((int)threadIdx.x + j * 256, nx - 1) * 8);
+    for (int j = 0; j < 4; ++j) xr[j].load(x + (size_t)min((int)threadIdx.x + j * NTH, nx - 1) * 8);
     const int n_active = active[0];
     const int e_raw = active[1 + min(a, E - 1)];
     const int e_c = min(max(e_raw, 0), E - 1);
@@ -517,19 +519,19 @@ __global__ __launch_bounds__(256) void ffn_gateup_tok16(const XT* __restrict__ x
     // tokens -> LDS as fp16, the high-nibble positions divided by 16
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int idx = (int)threadIdx.x + j * 256;
+        const int idx = (int)threadIdx.x + j * NTH;
         if (idx < nx) {
             const int r = idx >> lxc, cc = idx & (XC - 1);
             xs4[r * XC + (cc ^ r)] = __builtin_bit_cast(uint4, xr[j].cvt_pre16());
         }
     }
-    for (int base = 1024; base < nx; base += 1024) {
+    for (int base = 4 * NTH; base < nx; base += 4 * NTH) {
         XChunk<XT> xq[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xq[j].load(x + (size_t)min(base + (int)threadIdx.x + j * 256, nx - 1) * 8);
+        for (int j = 0; j < 4; ++j) xq[j].load(x + (size_t)min(base + (int)threadIdx.x + j * NTH, nx - 1) * 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int idx = base + (int)threadIdx.x + j * 256;
+            const int idx = base + (int)threadIdx.x + j * NTH;
             if (idx < nx) {
                 const int r = idx >> lxc, cc = idx & (XC - 1);
                 xs4[r * XC + (cc ^ r)] = __builtin_bit_cast(uint4, xq[j].cvt_pre16());
@@ -618,10 +620,10 @@ static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, h
     const int items = slots * (a->f / 16);
     // few items (a single token routes to k + 1 slots): four wavefronts per item
     const bool four = items < 1024 && nkt % 4 == 0;
-    const dim3 grid(four ? items : (items + 1) / 2);
-    const size_t lds = std::max<size_t>((size_t)a->T * a->d * sizeof(_Float16), 4 * 2 * 4 * 64 * sizeof(float));
+    const dim3 grid(four ? items : (items + 3) / 4);
+    const size_t lds = std::max<size_t>((size_t)a->T * a->d * sizeof(_Float16), 8 * 2 * 4 * 64 * sizeof(float));
 #define MOE_GU16(NT, S)                                                                                         \
-    ffn_gateup_tok16<NT, S, XT><<<grid, 256, lds, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs, \
+    ffn_gateup_tok16<NT, S, XT, S == 2 ? 512 : 256><<<grid, S == 2 ? 512 : 256, lds, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs, \
                                                        (const uint8_t*)a->shared_blob, a->counts, a->offsets,    \
                                                        a->sorted_idx, a->active, h)
     if (four) {
@@ -777,9 +779,11 @@ size_t float_h_bytes(int T, int f, int k) { return ((size_t)T * k + T) * (size_t
 // ---- moderate batches (T <= 64): token-dense gate/up, slot-dense down --------
 // Gate/up: every token is a row of the MFMA A operand (four 16-token m-tiles;
 // rows >= T repeat the last token and are discarded).  A workgroup takes
-// (slot, 64 rows of f): wavefront w owns the 16-row strip 4 g + w and streams
-// its quant tiles through registers kPipe chunks ahead, while all four stage
-// the tokens of the current 128-wide k-chunk in LDS as fp16 (double buffered).
+// (slot, 16 NW rows of f): wavefront w of NW owns the 16-row strip NW g + w
+// and streams its quant tiles through registers kPipe chunks ahead, while all
+// NW stage the tokens of the current 128-wide k-chunk in LDS as fp16 (double
+// buffered).  NW = 8 on large grids, so each token chunk is converted once per
+// 128 rows of f; NW = 4 on small ones.
 // Each weight is read once and serves every token; the block-scaled weights
 // accumulate in the MFMA as in the small-batch kernel.  The results go to LDS
 // as [token][16 features] and are scattered to the slot's rows from there.
@@ -840,27 +844,28 @@ __device__ __forceinline__ half8 strip_block(const StripChunk<WFMT>& w, int b, u
 }
 
 // token rows of one 128-k chunk -> LDS (fp16; 16-byte piece c of row r at c ^ (r & 15))
-template <typename XT>
+template <typename XT, int NTH = 256>
 struct RowChunk {
-    XChunk<XT> v[4];
+    static constexpr int NP = 1024 / NTH;
+    XChunk<XT> v[NP];
     __device__ __forceinline__ void load(const XT* base, int ld, int nrows, int k0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int piece = (int)threadIdx.x + 256 * j, row = piece >> 4, ch = piece & 15;
+        for (int j = 0; j < NP; ++j) {
+            const int piece = (int)threadIdx.x + NTH * j, row = piece >> 4, ch = piece & 15;
             v[j].load(base + (size_t)min(row, nrows - 1) * ld + k0 + 8 * ch);
         }
     }
     __device__ __forceinline__ void store(uint4 (*dst)[kKC / 8]) const {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int piece = (int)threadIdx.x + 256 * j, row = piece >> 4, ch = piece & 15;
+        for (int j = 0; j < NP; ++j) {
+            const int piece = (int)threadIdx.x + NTH * j, row = piece >> 4, ch = piece & 15;
             dst[row][ch ^ (row & 15)] = __builtin_bit_cast(uint4, v[j].cvt());
         }
     }
 };
 
-template <int WFMT, typename XT, int NCH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void ffn_gateup_tok64(const XT* __restrict__ x, int T, int d, int f, int k, int E,
+template <int WFMT, typename XT, int NCH, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3))) void ffn_gateup_tok64(const XT* __restrict__ x, int T, int d, int f, int k, int E,
                                                         const void* const* __restrict__ expert_ptrs,
                                                         const uint8_t* __restrict__ shared_blob,
                                                         const int32_t* __restrict__ counts,
@@ -869,12 +874,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
                                                         const int32_t* __restrict__ active, _Float16* __restrict__ h) {
     constexpr int TPC = StripChunk<WFMT>::TPC;
     __shared__ uint4 xs[2][kTok64][kKC / 8];
-    __shared__ _Float16 hv_s[4][kTok64][16];
+    __shared__ _Float16 hv_s[NW][kTok64][16];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n_groups = f / 64;
-    const int a = blockIdx.x / n_groups, strip = (blockIdx.x % n_groups) * 4 + wave;
-    RowChunk<XT> xr;
+    const int n_groups = f / (16 * NW);
+    const int a = blockIdx.x / n_groups, strip = (blockIdx.x % n_groups) * NW + wave;
+    RowChunk<XT, 64 * NW> xr;
     xr.load(x, d, T, 0);
     const int n_active = active[0];
     const int e_raw = active[1 + min(a, E - 1)];
@@ -1034,15 +1039,23 @@ __global__ __launch_bounds__(256) void ffn_down_tok64(const _Float16* __restrict
     }
 }
 
-// launchers: grid = (slots) x (64-row groups); false when the shape has no instance
+// launchers: grid = (slots) x (row groups); false when the shape has no instance
 template <int WFMT, typename XT>
 static bool launch_gateup_tok64(const moe_ffn_args* a, _Float16* h, int slots, hipStream_t s) {
     if (a->d % kKC || a->f % 64) return false;
-    const dim3 grid((unsigned)(slots * (a->f / 64)));
-#define MOE_GU64(NCH)                                                                                              \
-    ffn_gateup_tok64<WFMT, XT, NCH><<<grid, 256, 0, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->E,            \
-                                                         a->expert_ptrs, (const uint8_t*)a->shared_blob, a->counts, \
-                                                         a->offsets, a->sorted_idx, a->active, h)
+    // eight wavefronts (128 rows of f) per workgroup halve the token conversion
+    // work when the grid is large; small grids keep four for parallelism
+    const bool wide = a->f % 128 == 0 && (long)slots * (a->f / 64) >= 256;
+    const dim3 grid((unsigned)(slots * (a->f / (wide ? 128 : 64))));
+#define MOE_GU64(NCH)                                                                                                   \
+    if (wide)                                                                                                           \
+        ffn_gateup_tok64<WFMT, XT, NCH, 8><<<grid, 512, 0, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->E,          \
+                                                                a->expert_ptrs, (const uint8_t*)a->shared_blob,        \
+                                                                a->counts, a->offsets, a->sorted_idx, a->active, h);   \
+    else                                                                                                                \
+        ffn_gateup_tok64<WFMT, XT, NCH, 4><<<grid, 256, 0, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->E,          \
+                                                                a->expert_ptrs, (const uint8_t*)a->shared_blob,        \
+                                                                a->counts, a->offsets, a->sorted_idx, a->active, h)
     switch (a->d / kKC) {
     case 1: MOE_GU64(1); return true;
     case 2: MOE_GU64(2); return true;
