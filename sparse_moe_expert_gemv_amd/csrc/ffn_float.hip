@@ -646,11 +646,12 @@ static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, h
 
 // Down projection for small batches (int4): work item = (slot, 16 output
 // rows), one wavefront per item over the whole reduction, four items of one
-// slot per workgroup sharing the slot's h rows staged in LDS (16 rows at a
+// slot per workgroup (eight when few slots are active) sharing the slot's h
+// rows staged in LDS (16 rows at a
 // time); the first kPipe quant tiles are requested before the h rows, the
 // rest pipelined.
-template <int NKT, typename YT>
-__global__ __launch_bounds__(256) void ffn_down_tok16(const _Float16* __restrict__ h, int T, int d, int f, int k,
+template <int NKT, typename YT, int NW>
+__global__ __launch_bounds__(64 * NW) void ffn_down_tok16(const _Float16* __restrict__ h, int T, int d, int f, int k,
                                                       const void* const* __restrict__ expert_ptrs,
                                                       const uint8_t* __restrict__ shared_blob,
                                                       const int32_t* __restrict__ counts,
@@ -660,8 +661,8 @@ __global__ __launch_bounds__(256) void ffn_down_tok16(const _Float16* __restrict
     extern __shared__ __align__(16) uint4 hs4[];  // [16][f / 8], chunk c of row r at (c ^ r)
     const int HC = f / 8;
     const int lane = threadIdx.x & 63;
-    const int n_strips = d / 16;  // a multiple of 4: the four items of a workgroup share one slot
-    const int item0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 4);
+    const int n_strips = d / 16;  // a multiple of NW: the NW items of a workgroup share one slot
+    const int item0 = __builtin_amdgcn_readfirstlane(blockIdx.x * NW);
     const int strip = (item0 % n_strips) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int a = item0 / n_strips;
     const int n_active = active[0];
@@ -708,16 +709,16 @@ __global__ __launch_bounds__(256) void ffn_down_tok16(const _Float16* __restrict
         }
         // the tile's h rows -> LDS, two 16-byte chunks per thread per round
         const int nh = nr * HC;
-        for (int base = 0; base < nh; base += 512) {
+        for (int base = 0; base < nh; base += 128 * NW) {
             uint4v v[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int idx = min(base + (int)threadIdx.x + j * 256, nh - 1);
+                const int idx = min(base + (int)threadIdx.x + j * 64 * NW, nh - 1);
                 v[j] = gload(reinterpret_cast<const uint4v*>(h + (size_t)(p0 + m0 + idx / HC) * f) + idx % HC);
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int idx = base + (int)threadIdx.x + j * 256;
+                const int idx = base + (int)threadIdx.x + j * 64 * NW;
                 if (idx < nh) {
                     const int r = idx / HC, cc = idx % HC;
                     hs4[r * HC + (cc ^ r)] = __builtin_bit_cast(uint4, v[j]);
@@ -756,12 +757,19 @@ __global__ __launch_bounds__(256) void ffn_down_tok16(const _Float16* __restrict
 template <typename YT>
 static bool launch_down_tok16(const moe_ffn_args* a, const _Float16* h, int slots, hipStream_t s) {
     if (a->d % 64) return false;
-    const dim3 grid(slots * (a->d / 64));
+    // few slots (a single token): eight items per workgroup share the staged h rows
+    const bool wide = a->d % 128 == 0 && (long)slots * (a->d / 64) < 1024;
+    const dim3 grid(slots * (a->d / (wide ? 128 : 64)));
     const size_t lds = (size_t)kTokMax * a->f * sizeof(_Float16);
-#define MOE_DN16(NKT)                                                                                            \
-    ffn_down_tok16<NKT, YT><<<grid, 256, lds, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,                    \
-                                                   (const uint8_t*)a->shared_blob, a->counts, a->offsets, a->active, \
-                                                   (YT*)a->y_perm, a->y_shared)
+#define MOE_DN16(NKT)                                                                                               \
+    if (wide)                                                                                                       \
+        ffn_down_tok16<NKT, YT, 8><<<grid, 512, lds, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,                \
+                                                          (const uint8_t*)a->shared_blob, a->counts, a->offsets,    \
+                                                          a->active, (YT*)a->y_perm, a->y_shared);                  \
+    else                                                                                                            \
+        ffn_down_tok16<NKT, YT, 4><<<grid, 256, lds, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,                \
+                                                          (const uint8_t*)a->shared_blob, a->counts, a->offsets,    \
+                                                          a->active, (YT*)a->y_perm, a->y_shared)
     switch (a->f / 128) {
     case 2: MOE_DN16(2); return true;
     case 4: MOE_DN16(4); return true;
