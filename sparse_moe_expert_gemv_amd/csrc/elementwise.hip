@@ -81,49 +81,50 @@ __device__ __forceinline__ void fma4(float g, const float4& v, float4& acc) {
     acc.z = fmaf(g, v.z, acc.z); acc.w = fmaf(g, v.w, acc.w);
 }
 
-// One thread per (token, V outputs): V = 4, or 8 for fp16 rows (16-byte loads).
+// One workgroup per token (its gates and row indices are uniform, read with
+// scalar loads); each thread sums V consecutive outputs (V = 4, or 8 for fp16
+// rows: 16-byte loads), looping when d / V exceeds the workgroup.
 template <typename YT, int V>
 __global__ __launch_bounds__(256) void combine(const YT* __restrict__ y, const int32_t* __restrict__ dest,
                                                const float* __restrict__ gates, const float* __restrict__ ysh,
                                                const float* residual, int T, int k, int d, float* out) {
     constexpr int NQ = V / 4;
-    const int q = d / V;
-    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (long)T * q) return;
-    const int t = (int)(gid / q), o = (int)(gid % q) * V;
-    float4 acc[NQ];
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-        acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (residual) acc[u] = *reinterpret_cast<const float4*>(residual + (size_t)t * d + o + 4 * u);
-        if (ysh) {
-            const float4 v = *reinterpret_cast<const float4*>(ysh + (size_t)t * d + o + 4 * u);
-            acc[u].x += v.x; acc[u].y += v.y; acc[u].z += v.z; acc[u].w += v.w;
-        }
-    }
     constexpr int U = 16;
-    for (int j0 = 0; j0 < k; j0 += U) {
-        float g[U];
-        float4 v[U][NQ];
+    const int t = blockIdx.x;
+    for (int o = (int)threadIdx.x * V; o < d; o += 256 * V) {
+        float4 acc[NQ];
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-            if (j0 + j < k) {
-                g[j] = gates[(size_t)t * k + j0 + j];
-                const size_t off = (size_t)dest[(size_t)t * k + j0 + j] * d + o;
-                if constexpr (V == 4) v[j][0] = load_y4(y, off);
-                else load_y8(reinterpret_cast<const _Float16*>(y), off, v[j][0], v[j][NQ - 1]);
+        for (int u = 0; u < NQ; ++u) {
+            acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (residual) acc[u] = *reinterpret_cast<const float4*>(residual + (size_t)t * d + o + 4 * u);
+            if (ysh) {
+                const float4 v = *reinterpret_cast<const float4*>(ysh + (size_t)t * d + o + 4 * u);
+                acc[u].x += v.x; acc[u].y += v.y; acc[u].z += v.z; acc[u].w += v.w;
+            }
+        }
+        for (int j0 = 0; j0 < k; j0 += U) {
+            float g[U];
+            float4 v[U][NQ];
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                if (j0 + j < k) {
+                    g[j] = gates[(size_t)t * k + j0 + j];
+                    const size_t off = (size_t)dest[(size_t)t * k + j0 + j] * d + o;
+                    if constexpr (V == 4) v[j][0] = load_y4(y, off);
+                    else load_y8(reinterpret_cast<const _Float16*>(y), off, v[j][0], v[j][NQ - 1]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                if (j0 + j < k) {
+#pragma unroll
+                    for (int u = 0; u < NQ; ++u) fma4(g[j], v[j][u], acc[u]);
+                }
             }
         }
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-            if (j0 + j < k) {
-#pragma unroll
-                for (int u = 0; u < NQ; ++u) fma4(g[j], v[j][u], acc[u]);
-            }
-        }
+        for (int u = 0; u < NQ; ++u) *reinterpret_cast<float4*>(out + (size_t)t * d + o + 4 * u) = acc[u];
     }
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) *reinterpret_cast<float4*>(out + (size_t)t * d + o + 4 * u) = acc[u];
 }
 
 // out[t] = x[t] / sqrt(mean(x[t]^2) + eps): one wavefront per row, sums of
@@ -160,9 +161,8 @@ int launch_rmsnorm(const float* x, int T, int d, float eps, float* out, hipStrea
 int launch_combine(const void* y_perm, int y_dtype, const int32_t* dest, const float* gates, const float* y_shared,
                    const float* residual, int T, int k, int d, float* out, hipStream_t s) {
     const int V = (y_dtype == MOE_DT_F16 && d % 8 == 0) ? 8 : 4;
-    const long n = (long)T * (d / V);
-    if (n == 0) return MOE_OK;
-    const int grid = (int)((n + 255) / 256);
+    if (T == 0) return MOE_OK;
+    const int grid = T;
     if (y_dtype == MOE_DT_F32)
         combine<float, 4><<<grid, 256, 0, s>>>((const float*)y_perm, dest, gates, y_shared, residual, T, k, d, out);
     else if (V == 8)
