@@ -673,25 +673,29 @@ static bool launch_logits_splitk(const XT* x, int T, int d, const float* Wr, con
 
 bool route_small_ok(int T, int d, int k) { return T <= 64 && (size_t)T * k <= kSmallSlots && (size_t)kTG * d * 4 <= 64 * 1024; }
 
-// ------------------------------------------------ wavefront per row (T <= 8) ----
-// Decode batches: grid = E wavefronts, each computes one router row against all
-// T <= 8 tokens.  The lane's router values (float4 q = u * 64 + lane) and the
-// matching token values are loaded straight from global memory, all before any
-// arithmetic; no LDS and no barrier, so every wavefront runs on its own.
-template <typename XT, int TT, int NU>
-__global__ __launch_bounds__(64) void route_logits_wave(const XT* __restrict__ x, int T, int d,
-                                                        const float* __restrict__ Wr,
-                                                        const float* __restrict__ bias, int E,
-                                                        double* __restrict__ logits) {
-    const int lane = threadIdx.x;
+// ------------------------------------------------ workgroup per row (T <= 8) ----
+// Decode batches: grid = E workgroups, each computes one router row against
+// all T <= 8 tokens.  The row is split over NW wavefronts (NU float4 per lane
+// each); a lane's router values and the matching token values are loaded
+// straight from global memory, all before any arithmetic.  Each wavefront
+// reduces its share in double; the NW partial sums are added in wavefront
+// order (deterministic) after one barrier.
+template <typename XT, int TT, int NU, int NW>
+__global__ __launch_bounds__(64 * NW) void route_logits_wave(const XT* __restrict__ x, int T, int d,
+                                                             const float* __restrict__ Wr,
+                                                             const float* __restrict__ bias, int E,
+                                                             double* __restrict__ logits) {
+    __shared__ double part[NW][TT];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int e = blockIdx.x;
     const int nq = d / 4;
+    const int q0 = wave * NU * 64;  // this wavefront's share of the row, in float4
     const float4* w = reinterpret_cast<const float4*>(Wr + (size_t)e * d);
     float4 wv[NU];
     float4 xv[TT][NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {  // each router row is read once: non-temporal
-        const float4v v = gload_nt(reinterpret_cast<const float4v*>(w) + min(u * 64 + lane, nq - 1));
+        const float4v v = gload_nt(reinterpret_cast<const float4v*>(w) + min(q0 + u * 64 + lane, nq - 1));
         wv[u] = make_float4(v[0], v[1], v[2], v[3]);
     }
 #pragma unroll
@@ -699,7 +703,7 @@ __global__ __launch_bounds__(64) void route_logits_wave(const XT* __restrict__ x
         const int tt = min(t, T - 1);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int q = min(u * 64 + lane, nq - 1);
+            const int q = min(q0 + u * 64 + lane, nq - 1);
             if constexpr (sizeof(XT) == 4) {
                 xv[t][u] = reinterpret_cast<const float4*>(x + (size_t)tt * d)[q];
             } else {
@@ -714,7 +718,7 @@ __global__ __launch_bounds__(64) void route_logits_wave(const XT* __restrict__ x
     for (int t = 0; t < TT; ++t) acc[t] = 0.0;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        if (u * 64 + lane >= nq) continue;
+        if (q0 + u * 64 + lane >= nq) continue;
         const double w0 = wv[u].x, w1 = wv[u].y, w2 = wv[u].z, w3 = wv[u].w;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
@@ -724,21 +728,28 @@ __global__ __launch_bounds__(64) void route_logits_wave(const XT* __restrict__ x
             acc[t] = fma((double)xv[t][u].w, w3, acc[t]);
         }
     }
-    const double b = bias ? (double)bias[e] : 0.0;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         const double sm = wave_sum_xor_d(acc[t]);
-        if (lane == 0 && t < T) logits[(size_t)t * E + e] = sm + b;
+        if (lane == 0) part[wave][t] = sm;
+    }
+    if constexpr (NW > 1) __syncthreads();
+    if (threadIdx.x < TT && (int)threadIdx.x < T) {
+        const int t = threadIdx.x;
+        double sm = part[0][t];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) sm += part[q][t];  // wavefront order: deterministic
+        logits[(size_t)t * E + e] = sm + (bias ? (double)bias[e] : 0.0);
     }
 }
 
-template <typename XT, int NU>
+template <typename XT, int NU, int NW>
 static bool launch_logits_wave(const XT* x, int T, int d, const float* Wr, const float* bias, int E, double* logits,
                                hipStream_t s) {
-    if (T <= 1) route_logits_wave<XT, 1, NU><<<E, 64, 0, s>>>(x, T, d, Wr, bias, E, logits);
-    else if (T <= 2) route_logits_wave<XT, 2, NU><<<E, 64, 0, s>>>(x, T, d, Wr, bias, E, logits);
-    else if (T <= 4) route_logits_wave<XT, 4, NU><<<E, 64, 0, s>>>(x, T, d, Wr, bias, E, logits);
-    else if (T <= 8) route_logits_wave<XT, 8, NU><<<E, 64, 0, s>>>(x, T, d, Wr, bias, E, logits);
+    if (T <= 1) route_logits_wave<XT, 1, NU, NW><<<E, 64 * NW, 0, s>>>(x, T, d, Wr, bias, E, logits);
+    else if (T <= 2) route_logits_wave<XT, 2, NU, NW><<<E, 64 * NW, 0, s>>>(x, T, d, Wr, bias, E, logits);
+    else if (T <= 4) route_logits_wave<XT, 4, NU, NW><<<E, 64 * NW, 0, s>>>(x, T, d, Wr, bias, E, logits);
+    else if (T <= 8) route_logits_wave<XT, 8, NU, NW><<<E, 64 * NW, 0, s>>>(x, T, d, Wr, bias, E, logits);
     else return false;
     return true;
 }
@@ -746,15 +757,15 @@ static bool launch_logits_wave(const XT* x, int T, int d, const float* Wr, const
 static int launch_logits(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E,
                          double* logits, hipStream_t s) {
     if (T <= 8 && d <= 2048) {
-        // one wavefront per router row; NU float4 per lane cover d
+        // one workgroup per router row: one wavefront for d <= 512, else four, 2 float4 per lane
         const int nu = (d / 4 + 63) / 64;
         bool ok;
         if (x_dtype == MOE_DT_F32)
-            ok = nu <= 2 ? launch_logits_wave<float, 2>((const float*)x, T, d, Wr, bias, E, logits, s)
-                         : launch_logits_wave<float, 8>((const float*)x, T, d, Wr, bias, E, logits, s);
+            ok = nu <= 2 ? launch_logits_wave<float, 2, 1>((const float*)x, T, d, Wr, bias, E, logits, s)
+                         : launch_logits_wave<float, 2, 4>((const float*)x, T, d, Wr, bias, E, logits, s);
         else
-            ok = nu <= 2 ? launch_logits_wave<uint16_t, 2>((const uint16_t*)x, T, d, Wr, bias, E, logits, s)
-                         : launch_logits_wave<uint16_t, 8>((const uint16_t*)x, T, d, Wr, bias, E, logits, s);
+            ok = nu <= 2 ? launch_logits_wave<uint16_t, 2, 1>((const uint16_t*)x, T, d, Wr, bias, E, logits, s)
+                         : launch_logits_wave<uint16_t, 2, 4>((const uint16_t*)x, T, d, Wr, bias, E, logits, s);
         if (ok) return check_launch();
     }
     if (T <= 256) {
