@@ -254,7 +254,7 @@ def main():
     if mode == B.MOE_ACT_Q8:
         achieved = alg_ops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None}
+                "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": measured_traffic(name)}
     else:
         achieved = alg_bytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
