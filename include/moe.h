@@ -209,6 +209,13 @@ typedef struct moe_ffn_args {
  * per-block integer sums, both block scales applied in fp32; the SwiGLU
  * intermediate is requantised to int8 per 32 features before the down
  * projection.
+ * Errors: MOE_ERR_INVALID_ARG (null pointers, shapes not multiples of the
+ * quantisation block, a workspace smaller than moe_workspace_size);
+ * MOE_ERR_UNSUPPORTED for float-mode shapes no kernel covers: more than 64
+ * tokens with d or f above 2048 (16 rows of either, in fp16, must fit the
+ * 64 KiB of LDS the general kernels use), or, for T <= 64, a width the
+ * token-dense kernels have no instance for (d / 128 or f / 128 outside their
+ * sets) together with that same limit.
  */
 int moe_expert_ffn(const moe_ffn_args* args, moe_stream_t stream);
 

@@ -1070,6 +1070,7 @@ static bool launch_gateup_tok64(const moe_ffn_args* a, _Float16* h, int slots, h
     case 4: MOE_GU64(4); return true;
     case 8: MOE_GU64(8); return true;
     case 16: MOE_GU64(16); return true;
+    case 32: MOE_GU64(32); return true;
     default: return false;
     }
 #undef MOE_GU64
@@ -1107,15 +1108,21 @@ static int run_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     const int g1 = (int)std::min<long>((long)slots * (a->f / 16), (long)n_cu * 64);
     const size_t lds1 = std::max<size_t>((size_t)rows_lds * a->d * sizeof(_Float16), 4 * 2 * 4 * 64 * sizeof(float));
+    // the general kernels (T > 64) stage 16 rows of d (gate/up) or f (down) fp16 values in LDS
+    if (a->T > kTok64 && (size_t)rows_lds * std::max(a->d, a->f) * 2 > 64 * 1024) return MOE_ERR_UNSUPPORTED;
     if (a->phase != 2) {
         // token-dense kernel for small int4 batches; the token tile of d fp16 values per token fits in LDS
         const bool tok16 = WFMT == MOE_WFMT_I4B32 && a->T <= kTokMax && (size_t)a->T * a->d * 2 <= 64 * 1024 &&
                            (a->d & (a->d - 1)) == 0;
         const bool tok64 = !tok16 && a->T <= kTok64;
-        if (!(tok16 && launch_gateup_tok16<XT>(a, h, slots, s)) && !(tok64 && launch_gateup_tok64<WFMT, XT>(a, h, slots, s)))
+        if (!(tok16 && launch_gateup_tok16<XT>(a, h, slots, s)) &&
+            !(tok64 && launch_gateup_tok64<WFMT, XT>(a, h, slots, s))) {
+            // the general kernel stages 16 activation rows of d (fp16) in LDS
+            if ((size_t)rows_lds * a->d * 2 > 64 * 1024) return MOE_ERR_UNSUPPORTED;
             ffn_float_gateup<WFMT, XT><<<g1, 256, lds1, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->expert_ptrs,
                                                              (const uint8_t*)a->shared_blob, a->counts, a->offsets,
                                                              a->sorted_idx, a->active, h);
+        }
         const int rc = check_launch();
         if (rc || a->phase == 1) return rc;
     }
@@ -1125,24 +1132,26 @@ static int run_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     const bool tok16 = WFMT == MOE_WFMT_I4B32 && a->T <= kTokMax && (size_t)kTokMax * a->f * 2 <= 64 * 1024;
     const bool tok64 = !tok16 && a->T <= kTok64;
     if (a->y_dtype == MOE_DT_F32) {
-        if (!(tok16 && launch_down_tok16<float>(a, h, slots, s)) && !(tok64 && launch_down_tok64<WFMT, float>(a, h, slots, s)))
+        if (!(tok16 && launch_down_tok16<float>(a, h, slots, s)) && !(tok64 && launch_down_tok64<WFMT, float>(a, h, slots, s))) {
+            if (lds2 > 64 * 1024) return MOE_ERR_UNSUPPORTED;
             ffn_float_down<WFMT, float><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
                                                               (const uint8_t*)a->shared_blob, a->counts, a->offsets,
                                                               a->active, (float*)a->y_perm, a->y_shared);
+        }
     } else {
         if (!(tok16 && launch_down_tok16<_Float16>(a, h, slots, s)) &&
-            !(tok64 && launch_down_tok64<WFMT, _Float16>(a, h, slots, s)))
+            !(tok64 && launch_down_tok64<WFMT, _Float16>(a, h, slots, s))) {
+            if (lds2 > 64 * 1024) return MOE_ERR_UNSUPPORTED;
             ffn_float_down<WFMT, _Float16><<<g2, 256, lds2, s>>>(h, a->T, a->d, a->f, a->k, a->expert_ptrs,
                                                                  (const uint8_t*)a->shared_blob, a->counts, a->offsets,
                                                                  a->active, (_Float16*)a->y_perm, a->y_shared);
+        }
     }
     return check_launch();
 }
 
 int launch_ffn_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
-    // LDS holds 16 activation rows of d (fp16) in gate/up; registers hold all f in down
-    if ((size_t)std::min(16, a->T) * a->d * 2 > 64 * 1024 || a->f / 8 < 16 || a->d / 8 < 16)
-        return MOE_ERR_UNSUPPORTED;
+    if (a->f / 8 < 16 || a->d / 8 < 16) return MOE_ERR_UNSUPPORTED;
     if (a->wfmt == MOE_WFMT_I4B32)
         return a->x_dtype == MOE_DT_F32 ? run_float<MOE_WFMT_I4B32, float>(a, w, s)
                                         : run_float<MOE_WFMT_I4B32, uint16_t>(a, w, s);

@@ -193,6 +193,28 @@ def test_q8_mode_small_and_mid_batches(T):
     check_float(out, o["out"], "q8 T=%d" % T)
 
 
+@pytest.mark.parametrize("T", [4, 40])
+def test_wide_model_dimension(T):
+    """d = 4096 (twice the decode layer's width), f = 512, 64 experts, top-8:
+    the token-dense kernels with 32 k-tiles per row, the router's split-k and
+    four-wavefront row kernels at another width."""
+    L = synth.make_layer("decode_t4", T=T, overrides={"d": 4096, "f": 512, "E": 64, "k": 8})
+    G, out, st, o = run_layer(L)
+    check_routing(st, o, L.cfg.E)
+    check_float(out, o["out"], "d=4096 T=%d" % T)
+
+
+@pytest.mark.parametrize("T,mode", [(3, "float"), (30, "float"), (30, "q8")])
+def test_many_experts_large_k(T, mode):
+    """E = 1024 experts (sixteen logits per lane in the top-k) with k = 32 (past
+    the sixteen group maxima of the threshold search, so the lane-maximum path
+    runs) on a narrow layer, both activation modes."""
+    L = synth.make_layer("tiny", T=T, overrides={"E": 1024, "k": 32, "act_mode": mode})
+    G, out, st, o = run_layer(L)
+    check_routing(st, o, L.cfg.E)
+    check_float(out, o["out"], "E=1024 k=32 T=%d %s" % (T, mode))
+
+
 def test_one_expert_takes_every_token_q8():
     """Router bias forces one expert into every token's top-k (count = T = 300
     > one 128-token tile) in int8 mode; ties elsewhere still resolve to the
