@@ -121,7 +121,7 @@ int moe_route(const void* x, int x_dtype, int T, int d, const float* Wr, const f
               int32_t* ids, float* gates, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
- * moe_route followed by moe_permute.  For small batches (T <= 64 and
+ * moe_route followed by moe_permute.  For small batches (T <= 16 and
  * T*k <= 512: decode, MTP verify) this is two launches: the router logits,
  * then one workgroup that selects the top-k of every token and groups the
  * slots; larger batches run the two calls' kernels in sequence.  Outputs and

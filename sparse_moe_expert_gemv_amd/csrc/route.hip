@@ -9,7 +9,7 @@
 // tokens (route_logits_wave); 8 < T <= 256, 16 x 16 tiles on fp64 MFMA with
 // the reduction split over sixteen wavefronts (route_logits_splitk); larger
 // T, 64 x 128 tiles on fp64 MFMA (route_logits_mfma); route_logits_rows covers
-// widths the split-k kernel is not instantiated for.  For up to 64 tokens and
+// widths the split-k kernel is not instantiated for.  For up to 16 tokens and
 // 512 slots a single workgroup then selects the top-k of every token and,
 // when asked, also groups the routing slots by expert (the moe_permute
 // outputs), so decode routing is two launches.  A device-wide last-workgroup
@@ -224,80 +224,102 @@ __global__ __launch_bounds__(256) void route_topk(const double* __restrict__ log
 // 256-thread workgroup.  Same outputs as the multi-workgroup path.
 constexpr int kSmallSlots = 512;
 
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele with lane shifts).
+__device__ __forceinline__ int wave_prefix_incl(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// The four wavefronts each own a contiguous range of the slots (a multiple of
+// 64): per-range expert histograms, one scan of the totals over the experts,
+// per-range base positions, then every wavefront places its own slots in
+// ascending order (ballot ranking within 64-slot chunks), so the grouping is
+// stable and the four ranges are placed concurrently.
 __device__ void block_permute(const int32_t* s_ids, int n, int E, int32_t* counts, int32_t* offsets,
-                              int32_t* sorted_idx, int32_t* dest, int32_t* active, int32_t* s_cnt, int32_t* s_part,
-                              int32_t* s_flag) {
-    const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += 256) s_cnt[e] = 0;
+                              int32_t* sorted_idx, int32_t* dest, int32_t* active, int32_t (*s_wc)[1024],
+                              int32_t* s_part, int32_t* s_flag) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rng = ((n + 255) / 256) * 64;  // slots per wavefront range
+    const int f_lo = min(n, wave * rng), f_hi = min(n, f_lo + rng);
+    for (int i = tid; i < 4 * 1024; i += 256) (&s_wc[0][0])[i] = 0;
     __syncthreads();
-    for (int f = tid; f < n; f += 256) {
+    for (int f = f_lo + lane; f < f_hi; f += 64) {
         const int id = s_ids[f];
-        if ((unsigned)id < (unsigned)E) atomicAdd(&s_cnt[id], 1);
+        if ((unsigned)id < (unsigned)E) atomicAdd(&s_wc[wave][id], 1);
     }
     __syncthreads();
-    // exclusive scan of counts (and of active flags): 4 experts per thread, then 256 partials
+    // totals of 4 experts per thread, exclusive scan over the experts (wavefront
+    // scans, then the totals of the preceding wavefronts)
     int c4[4], p = 0, fl = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = tid * 4 + i;
-        c4[i] = e < E ? s_cnt[e] : 0;
+        c4[i] = e < E ? s_wc[0][e] + s_wc[1][e] + s_wc[2][e] + s_wc[3][e] : 0;
         p += c4[i];
         fl += c4[i] > 0;
     }
-    s_part[tid] = p;
-    s_flag[tid] = fl;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const int a = tid >= off ? s_part[tid - off] : 0;
-        const int b = tid >= off ? s_flag[tid - off] : 0;
-        __syncthreads();
-        s_part[tid] += a;
-        s_flag[tid] += b;
-        __syncthreads();
+    const int pi = wave_prefix_incl(p), fi = wave_prefix_incl(fl);
+    if (lane == 63) {
+        s_part[wave] = pi;
+        s_flag[wave] = fi;
     }
-    int run = s_part[tid] - p, frun = s_flag[tid] - fl;
+    __syncthreads();
+    int run = pi - p, frun = fi - fl;
+    for (int w = 0; w < wave; ++w) {
+        run += s_part[w];
+        frun += s_flag[w];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = tid * 4 + i;
         if (e < E) {
             counts[e] = c4[i];
             offsets[e] = run;
-            s_cnt[e] = run;  // becomes the running position of expert e
             if (c4[i] > 0) active[1 + frun++] = e;
+            // base position of expert e in each range: the slots of e in earlier ranges come first
+            int b = run;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int cw = s_wc[w][e];
+                s_wc[w][e] = b;
+                b += cw;
+            }
             run += c4[i];
         }
     }
     if (tid == 255) {
-        offsets[E] = s_part[255];
-        active[0] = s_flag[255];
+        offsets[E] = run;
+        active[0] = frun;
     }
     __syncthreads();
-    // stable scatter by wavefront 0, slots in ascending order
-    if (tid < 64) {
-        const int lane = tid;
-        int nbits = 0;
-        while ((1 << nbits) < E) ++nbits;
-        const unsigned long long lt = (1ull << lane) - 1ull;
-        for (int f0 = 0; f0 < n; f0 += 64) {
-            const int f = f0 + lane;
-            const int raw = f < n ? s_ids[f] : -1;
-            const bool valid = (unsigned)raw < (unsigned)E;
-            const int id = valid ? raw : 0;
-            unsigned long long peers = __ballot(valid);
-            for (int b = 0; b < nbits; ++b) {
-                const unsigned long long on = __ballot(valid && ((id >> b) & 1));
-                peers &= ((id >> b) & 1) ? on : ~on;
-            }
-            const int rank = __popcll(peers & lt);
-            const int cnt = __popcll(peers);
-            const int pos = valid ? s_cnt[id] + rank : 0;
-            __builtin_amdgcn_wave_barrier();
-            if (valid && rank == 0) s_cnt[id] += cnt;
-            __builtin_amdgcn_wave_barrier();
-            if (valid) {
-                sorted_idx[pos] = f;
-                dest[f] = pos;
-            }
+    // stable scatter: wavefront w places the slots of its range in ascending order
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    for (int f0 = f_lo; f0 < f_hi; f0 += 64) {
+        const int f = f0 + lane;
+        const int raw = f < f_hi ? s_ids[f] : -1;
+        const bool valid = (unsigned)raw < (unsigned)E;
+        const int id = valid ? raw : 0;
+        unsigned long long peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const unsigned long long on = __ballot(valid && ((id >> b) & 1));
+            peers &= ((id >> b) & 1) ? on : ~on;
+        }
+        const int rank = __popcll(peers & lt);
+        const int cnt = __popcll(peers);
+        const int pos = valid ? s_wc[wave][id] + rank : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid && rank == 0) s_wc[wave][id] += cnt;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            sorted_idx[pos] = f;
+            dest[f] = pos;
         }
     }
 }
@@ -454,11 +476,11 @@ __global__ __launch_bounds__(256) void perm_block(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ sorted_idx, int32_t* __restrict__ dest,
                                                   int32_t* __restrict__ active) {
     __shared__ int32_t s_ids[kBlockPermMax];
-    __shared__ int32_t s_cnt[1024];
-    __shared__ int32_t s_part[256], s_flag[256];
+    __shared__ int32_t s_wc[4][1024];
+    __shared__ int32_t s_part[4], s_flag[4];
     for (int i = threadIdx.x; i < n; i += 256) s_ids[i] = ids[i];
     __syncthreads();
-    block_permute(s_ids, n, E, counts, offsets, sorted_idx, dest, active, s_cnt, s_part, s_flag);
+    block_permute(s_ids, n, E, counts, offsets, sorted_idx, dest, active, s_wc, s_part, s_flag);
 }
 
 int launch_permute_block(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
@@ -479,8 +501,8 @@ __global__ __launch_bounds__(256) void route_select_small(const double* __restri
                                                           int32_t* __restrict__ dest, int32_t* __restrict__ active) {
     __shared__ RankScratch sc[4];
     __shared__ int32_t s_ids[kSmallSlots];
-    __shared__ int32_t s_cnt[1024];
-    __shared__ int32_t s_part[256], s_flag[256];
+    __shared__ int32_t s_wc[4][1024];
+    __shared__ int32_t s_part[4], s_flag[4];
     __shared__ __align__(16) uint32_t s_keys[64];
     __shared__ __align__(16) uint32_t s_sorted[128];
     const int wave = threadIdx.x >> 6;
@@ -492,7 +514,7 @@ __global__ __launch_bounds__(256) void route_select_small(const double* __restri
         if (T * k <= 64)
             permute_rank64(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_keys, s_sorted);
         else
-            block_permute(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_cnt, s_part, s_flag);
+            block_permute(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_wc, s_part, s_flag);
     }
 }
 
@@ -671,7 +693,9 @@ static bool launch_logits_splitk(const XT* x, int T, int d, const float* Wr, con
     }
 }
 
-bool route_small_ok(int T, int d, int k) { return T <= 64 && (size_t)T * k <= kSmallSlots && (size_t)kTG * d * 4 <= 64 * 1024; }
+// the single-workgroup selection serialises T / 4 tokens per wavefront: beyond
+// 16 tokens the separate top-k (one wavefront per token) and permutation win
+bool route_small_ok(int T, int d, int k) { return T <= 16 && (size_t)T * k <= kSmallSlots && (size_t)kTG * d * 4 <= 64 * 1024; }
 
 // ------------------------------------------------ workgroup per row (T <= 8) ----
 // Decode batches: grid = E workgroups, each computes one router row against
