@@ -30,7 +30,11 @@ void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* bas
     };
     const size_t rows = (size_t)T * k + (size_t)T;
     const size_t nch = ((size_t)T * k + kPermChunk - 1) / kPermChunk;
-    w->logits = reinterpret_cast<double*>(take(sizeof(double) * (size_t)T * E));
+    // room for the split-k planes of any batch up to T (a workspace sized for
+    // T also serves every smaller batch): P T' <= kMaxLogitPlanes T' with P = 1
+    // beyond 256 tokens
+    const size_t logit_rows = (size_t)T + (size_t)(kMaxLogitPlanes - 1) * std::min(T, 256);
+    w->logits = reinterpret_cast<double*>(take(sizeof(double) * logit_rows * E));
     w->route_bytes = off;
     w->hist = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * std::max<size_t>(nch, 1) * E));
     w->permute_bytes = off;

@@ -104,7 +104,7 @@ inline hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream
 // Regions are laid out in this order so that route and permute only need a
 // prefix of the workspace.
 struct Workspace {
-    double* logits;     // [T, E]                         route
+    double* logits;     // [P, T, E] (P k planes)         route
     int32_t* hist;      // [ceil(T*k / kPermChunk), E]    permute
     int32_t* tiles;     // q8 tile list (int2) + count    ffn
     void* h;            // SwiGLU intermediate [T*k + T, f]: fp16 (float mode) or int8 (q8)
@@ -117,6 +117,10 @@ void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* bas
 
 // ---- launchers (defined in the .hip files) -----------------------------------
 int launch_pack(const void* src, void* dst, int n, int wfmt, int d, int f, bool unpack, hipStream_t s);
+// number of [T, E] planes of partial router logits the routing writes (k split
+// over workgroups for moderate batches; 1 otherwise)
+int logit_planes(int T, int d, int E);
+constexpr int kMaxLogitPlanes = 4;
 int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
                  int32_t* ids, float* gates, double* logits, hipStream_t s);
 bool route_small_ok(int T, int d, int k);

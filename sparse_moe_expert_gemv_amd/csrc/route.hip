@@ -102,11 +102,16 @@ struct RankScratch {
 // More than 64 candidates (heavy ties) fall back to k rounds of wave argmax.
 template <int NPL>
 __device__ void topk_rank(const double* __restrict__ z, int E, int k, int32_t* __restrict__ ids,
-                          float* __restrict__ gates, int32_t* s_ids, RankScratch& S) {
+                          float* __restrict__ gates, int32_t* s_ids, RankScratch& S, int planes = 1,
+                          size_t plane_stride = 0) {
     const int lane = threadIdx.x & 63;
     double v[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) v[i] = z[min(lane + 64 * i, E - 1)];
+    // split-k logits: the partial sums of the k planes are added in plane order
+    for (int p = 1; p < planes; ++p)
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) v[i] += z[p * plane_stride + min(lane + 64 * i, E - 1)];
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
         if (lane + 64 * i >= E) v[i] = -DBL_MAX;
@@ -211,12 +216,13 @@ inline int topk_npl(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : 
 
 template <int NPL>
 __global__ __launch_bounds__(256) void route_topk(const double* __restrict__ logits, int T, int E, int k,
-                                                  int32_t* __restrict__ ids, float* __restrict__ gates) {
+                                                  int32_t* __restrict__ ids, float* __restrict__ gates, int planes) {
     __shared__ RankScratch sc[4];
     const int wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
-    topk_rank<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, nullptr, sc[wave]);
+    topk_rank<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, nullptr, sc[wave],
+                   planes, (size_t)T * E);
 }
 
 // ------------------------------------------------- block-level permutation ----
@@ -498,7 +504,8 @@ __global__ __launch_bounds__(256) void route_select_small(const double* __restri
                                                           int do_permute, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_idx,
-                                                          int32_t* __restrict__ dest, int32_t* __restrict__ active) {
+                                                          int32_t* __restrict__ dest, int32_t* __restrict__ active,
+                                                          int planes) {
     __shared__ RankScratch sc[4];
     __shared__ int32_t s_ids[kSmallSlots];
     __shared__ int32_t s_wc[4][1024];
@@ -508,7 +515,7 @@ __global__ __launch_bounds__(256) void route_select_small(const double* __restri
     const int wave = threadIdx.x >> 6;
     for (int t = wave; t < T; t += 4)
         topk_rank<NPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k, s_ids + t * k,
-                       sc[wave]);
+                       sc[wave], planes, (size_t)T * E);
     block_lds_sync();
     if (do_permute) {
         if (T * k <= 64)
@@ -624,13 +631,17 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const XT* __restrict__ 
 }
 
 // ------------------------------------------ moderate batches: split-k fp64 MFMA ----
-// Workgroup = 16 tokens x 16 router rows, sixteen wavefronts splitting k;
-// wavefront s, lane group g = l / 16 owns the contiguous range of d / 64 k at
-// s d / 16 + g d / 64, so that at MFMA step j every lane multiplies its own
-// j-th token value by its own j-th router value (A and B share the k
+// Workgroup = 16 tokens x 16 router rows x one of P = gridDim.z planes of k
+// (d / P consecutive k each), sixteen wavefronts splitting the plane's k:
+// wavefront s, lane group g = l / 16 owns the KPL = d / (64 P) consecutive k at
+// plane * d / P + (4 s + g) KPL, so that at MFMA step j every lane multiplies
+// its own j-th token value by its own j-th router value (A and B share the k
 // assignment; every product appears once).  Operands come straight from
 // global memory (no reuse across wavefronts); the sixteen partial tiles meet
-// in LDS and are summed in wavefront order, then the bias is added.
+// in LDS and are summed in wavefront order.  Plane p writes its partial sums
+// to logits + p T E, plane 0 with the bias added; the top-k reads the planes
+// back and adds them in plane order.  P > 1 only spreads small tiles grids
+// over more compute units.
 template <typename XT, int KPL>
 __global__ __launch_bounds__(1024) void route_logits_splitk(const XT* __restrict__ x, int T, int d,
                                                             const float* __restrict__ Wr,
@@ -640,7 +651,7 @@ __global__ __launch_bounds__(1024) void route_logits_splitk(const XT* __restrict
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t0 = blockIdx.y * 16, e0 = blockIdx.x * 16;
     const int t = min(t0 + (lane & 15), T - 1), e = min(e0 + (lane & 15), E - 1);
-    const int k0 = wave * (d / 16) + (lane >> 4) * KPL;
+    const int k0 = blockIdx.z * 64 * KPL + (4 * wave + (lane >> 4)) * KPL;
     float xa[KPL], wb[KPL];
     if constexpr (sizeof(XT) == 4) {
 #pragma unroll
@@ -674,16 +685,29 @@ __global__ __launch_bounds__(1024) void route_logits_splitk(const XT* __restrict
 #pragma unroll
         for (int q = 0; q < 16; ++q) sum += part[q][r][l];
         const int tt = t0 + 4 * r + (l >> 4), ee = e0 + (l & 15);
-        if (tt < T && ee < E) logits[(size_t)tt * E + ee] = sum + (bias ? (double)bias[ee] : 0.0);
+        if (tt < T && ee < E)
+            logits[(size_t)blockIdx.z * T * E + (size_t)tt * E + ee] =
+                sum + (bias && blockIdx.z == 0 ? (double)bias[ee] : 0.0);
     }
+}
+
+// k planes of the split-k kernel: enough workgroups for every compute unit,
+// at least 4 k per lane; 0 where the kernel does not apply (KPL = d / (64 P)
+// must be a power of two from 4 to 64)
+static int splitk_planes(int T, int d, int E) {
+    const int kpl = d / 64;
+    if (d % 64 || kpl < 4 || kpl > 64 || (kpl & (kpl - 1))) return 0;
+    const long tiles = (long)((E + 15) / 16) * ((T + 15) / 16);
+    int P = 1;
+    while (P < kMaxLogitPlanes && tiles * P < 256 && kpl / (2 * P) >= 4) P *= 2;
+    return P;
 }
 
 template <typename XT>
 static bool launch_logits_splitk(const XT* x, int T, int d, const float* Wr, const float* bias, int E,
-                                 double* logits, hipStream_t s) {
-    const dim3 grid((E + 15) / 16, (T + 15) / 16);
-    switch (d / 64) {
-    case 2: route_logits_splitk<XT, 2><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
+                                 double* logits, int P, hipStream_t s) {
+    const dim3 grid((E + 15) / 16, (T + 15) / 16, P);
+    switch (d / (64 * P)) {
     case 4: route_logits_splitk<XT, 4><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
     case 8: route_logits_splitk<XT, 8><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
     case 16: route_logits_splitk<XT, 16><<<grid, 1024, 0, s>>>(x, T, d, Wr, bias, E, logits); return true;
@@ -778,6 +802,12 @@ static bool launch_logits_wave(const XT* x, int T, int d, const float* Wr, const
     return true;
 }
 
+int logit_planes(int T, int d, int E) {
+    if (T <= 0 || (T <= 8 && d <= 2048) || T > 256) return 1;
+    const int P = splitk_planes(T, d, E);
+    return P > 0 ? P : 1;
+}
+
 static int launch_logits(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E,
                          double* logits, hipStream_t s) {
     if (T <= 8 && d <= 2048) {
@@ -792,10 +822,11 @@ static int launch_logits(const void* x, int x_dtype, int T, int d, const float* 
                          : launch_logits_wave<uint16_t, 2, 4>((const uint16_t*)x, T, d, Wr, bias, E, logits, s);
         if (ok) return check_launch();
     }
-    if (T <= 256) {
+    if (T <= 256 && splitk_planes(T, d, E) > 0) {
+        const int P = splitk_planes(T, d, E);
         const bool ok = x_dtype == MOE_DT_F32
-                            ? launch_logits_splitk<float>((const float*)x, T, d, Wr, bias, E, logits, s)
-                            : launch_logits_splitk<uint16_t>((const uint16_t*)x, T, d, Wr, bias, E, logits, s);
+                            ? launch_logits_splitk<float>((const float*)x, T, d, Wr, bias, E, logits, P, s)
+                            : launch_logits_splitk<uint16_t>((const uint16_t*)x, T, d, Wr, bias, E, logits, P, s);
         if (ok) return check_launch();
     }
     if (T <= 256 && (size_t)kTG * d * 4 <= 64 * 1024) {
@@ -820,9 +851,10 @@ int launch_route_small(const void* x, int x_dtype, int T, int d, const float* Wr
                        int32_t* offsets, int32_t* sorted_idx, int32_t* dest, int32_t* active, hipStream_t s) {
     int rc = launch_logits(x, x_dtype, T, d, Wr, bias, E, logits, s);
     if (rc) return rc;
+    const int planes = logit_planes(T, d, E);
 #define MOE_SEL(NPL)                                                                                       \
     route_select_small<NPL><<<1, 256, 0, s>>>(logits, T, E, k, ids, gates, do_permute, counts, offsets, sorted_idx, \
-                                              dest, active)
+                                              dest, active, planes)
     switch (topk_npl(E)) {
     case 1: MOE_SEL(1); break;
     case 2: MOE_SEL(2); break;
@@ -842,13 +874,14 @@ int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, cons
                                   nullptr, nullptr, nullptr, s);
     int rc = launch_logits(x, x_dtype, T, d, Wr, bias, E, logits, s);
     if (rc) return rc;
+    const int planes = logit_planes(T, d, E);
     const dim3 grid((T + 3) / 4);
     switch (topk_npl(E)) {
-    case 1: route_topk<1><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
-    case 2: route_topk<2><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
-    case 4: route_topk<4><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
-    case 8: route_topk<8><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
-    default: route_topk<16><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates); break;
+    case 1: route_topk<1><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates, planes); break;
+    case 2: route_topk<2><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates, planes); break;
+    case 4: route_topk<4><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates, planes); break;
+    case 8: route_topk<8><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates, planes); break;
+    default: route_topk<16><<<grid, 256, 0, s>>>(logits, T, E, k, ids, gates, planes); break;
     }
     return check_launch();
 }

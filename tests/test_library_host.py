@@ -54,6 +54,15 @@ def test_workspace_size_grows_with_tokens_and_rejects_bad_shapes():
         B.moe_workspace_size(4, 2048, 768, 2048, 10, B.MOE_ACT_FLOAT)  # E > 1024
 
 
+def test_workspace_for_a_batch_serves_every_smaller_batch():
+    # callers size one workspace for their largest batch (the layer objects and
+    # the decode stack do); the split-k router planes must not break that
+    for d, f, E, k in ((2048, 768, 512, 10), (4096, 1024, 1024, 32), (256, 128, 64, 4)):
+        for mode in (B.MOE_ACT_FLOAT, B.MOE_ACT_Q8):
+            sizes = [B.moe_workspace_size(T, d, f, E, k, mode) for T in range(1, 601)]
+            assert all(a <= b for a, b in zip(sizes, sizes[1:])), (d, f, E, k, mode)
+
+
 def test_invalid_arguments_rejected_before_any_hip_call():
     L = B.lib()
     null = None
