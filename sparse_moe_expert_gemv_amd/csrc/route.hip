@@ -101,7 +101,7 @@ struct RankScratch {
 //     lane r then holds the entry of rank r.
 // More than 64 candidates (heavy ties) fall back to k rounds of wave argmax.
 template <int NPL>
-__device__ void topk_rank(const double* __restrict__ z, int E, int k, int32_t* __restrict__ ids,
+__device__ __forceinline__ void topk_rank(const double* __restrict__ z, int E, int k, int32_t* __restrict__ ids,
                           float* __restrict__ gates, int32_t* s_ids, RankScratch& S, int planes = 1,
                           size_t plane_stride = 0) {
     const int lane = threadIdx.x & 63;
@@ -802,11 +802,12 @@ static bool launch_logits_wave(const XT* x, int T, int d, const float* Wr, const
     return true;
 }
 
-int logit_planes(int T, int d, int E) {
-    if (T <= 0 || (T <= 8 && d <= 2048) || T > 256) return 1;
-    const int P = splitk_planes(T, d, E);
-    return P > 0 ? P : 1;
+// the logits of T tokens take the split-k kernel
+static bool logits_splitk(int T, int d, int E) {
+    return T > 0 && !(T <= 8 && d <= 2048) && T <= 256 && splitk_planes(T, d, E) > 0;
 }
+
+int logit_planes(int T, int d, int E) { return logits_splitk(T, d, E) ? splitk_planes(T, d, E) : 1; }
 
 static int launch_logits(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E,
                          double* logits, hipStream_t s) {
@@ -822,7 +823,7 @@ static int launch_logits(const void* x, int x_dtype, int T, int d, const float* 
                          : launch_logits_wave<uint16_t, 2, 4>((const uint16_t*)x, T, d, Wr, bias, E, logits, s);
         if (ok) return check_launch();
     }
-    if (T <= 256 && splitk_planes(T, d, E) > 0) {
+    if (logits_splitk(T, d, E)) {
         const int P = splitk_planes(T, d, E);
         const bool ok = x_dtype == MOE_DT_F32
                             ? launch_logits_splitk<float>((const float*)x, T, d, Wr, bias, E, logits, P, s)

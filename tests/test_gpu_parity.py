@@ -302,14 +302,18 @@ def test_graph_replays_match_eager(name):
         del junk
 
 
-def test_route_permute_fused_equals_separate_calls():
-    """moe_route_permute (selection and grouping in one workgroup for small T)
-    equals moe_route followed by moe_permute."""
-    L = _layer("decode_t4")
+@pytest.mark.parametrize("name,T", [("decode_t4", 4), ("decode_t4", 16), ("tiny", 32), ("skew", 17),
+                                    ("skew", 64), ("skew", 256)])
+def test_route_permute_fused_equals_separate_calls(name, T):
+    """moe_route_permute (selection and grouping in one workgroup for T <= 16)
+    equals moe_route followed by moe_permute, also when the workspace starts
+    with arbitrary bytes (no state may carry over in it)."""
+    L = synth.make_layer(name, T=T)
     G = gpu_layer(L)
     xt = x_tensor(L)
     T, k, E = L.cfg.T, L.cfg.k, L.cfg.E
     ws = G._ws_for(T)
+    ws.fill_(0x5A)
     B.moe_route_permute(xt, G.Wr, G.bias, k, G.ids[:T], G.gates[:T], G.counts, G.offsets, G.sorted_idx[:T * k],
                         G.dest[:T * k], G.active, ws)
     torch.cuda.synchronize()
