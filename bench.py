@@ -1,8 +1,10 @@
 """Benchmark of the sparse-MoE FFN layer hot path on one MI355X.
 
-One step = one pass of the whole layer (moe_route -> moe_permute ->
-[moe_quantize_act] -> moe_expert_ffn -> moe_combine) over one batch of seeded
-synthetic input already resident in HBM.  Default workload: the decode layer
+One step = one pass of the whole layer (moe_route_permute (routing and
+grouping) -> [moe_quantize_act] -> moe_expert_ffn_combine (expert FFN and the
+gate-weighted combine; for decode batches with int4 weights the down projection
+and the combine are one kernel)) over one batch of seeded synthetic input
+already resident in HBM.  Default workload: the decode layer
 (d=2048, 512 int4 experts + shared, top-10, f=768) at T=4 tokens, the MTP
 verify batch; ``--workload`` selects another layer (decode_t1, prefill, skew,
 tiny) or a 48-layer stack over the 4,500-slot expert pool (``stack``: the
@@ -22,8 +24,8 @@ projection, ``moe_expert_ffn`` phase 1, rotating over the weight copies, also
 replayed from graphs) between two HIP events on its launch stream, whose mean
 launch time gives the roofline figure.
 
-Prints one JSON line (rank 0).  ``--gpus`` above 1 is not supported: this
-build runs on one GPU.
+Prints one JSON line (rank 0).  ``--gpus`` above 1 is not supported: the
+benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -104,7 +106,7 @@ def gateup_algorithmic(cfg, n_active: int, T: int):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus %d" % a.gpus)
+        print("bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus %d" % a.gpus)
         sys.exit(2)
     import torch
 
@@ -175,15 +177,23 @@ def main():
         else:
             B.moe_expert_ffn(x=x, **common)
 
-    def run_combine(G, x):
+    def run_ffn_combine(G, x):
+        # expert FFN and the weighted combine (one kernel for the down projection
+        # and the sum where the library has it)
         n = T * cfg.k
-        B.moe_combine(G.y_perm[:n], G.dest[:n], G.gates[:T], G.y_shared[:T] if G.shared is not None else None,
-                      None, G.out[:T])
+        common = dict(T=T, d=cfg.d, f=cfg.f, E=cfg.E, k=cfg.k, wfmt=cfg.wfmt, act_mode=mode,
+                      expert_ptrs=G.expert_ptrs, counts=G.counts, offsets=G.offsets, sorted_idx=G.sorted_idx[:n],
+                      active=G.active, y_perm=G.y_perm[:n], ws=G._ws_for(T), shared_blob=G.shared,
+                      y_shared=G.y_shared[:T] if G.shared is not None else None, ids=G.ids[:T], dest=G.dest[:n],
+                      gates=G.gates[:T], out=G.out[:T])
+        if mode == B.MOE_ACT_Q8:
+            B.moe_expert_ffn_combine(xq=G.xq[:T], sx=G.sx[:T], **common)
+        else:
+            B.moe_expert_ffn_combine(x=x, **common)
 
     def run_step(G, x):
         run_route(G, x)
-        run_ffn(G, x)
-        run_combine(G, x)
+        run_ffn_combine(G, x)
 
     # warm up eagerly on every copy
     for i in range(max(warmup, rotate)):

@@ -49,7 +49,7 @@ typedef void* moe_event_t;  /* hipEvent_t  */
 /* status codes */
 #define MOE_OK 0
 #define MOE_ERR_INVALID_ARG 1    /* null pointer, bad shape, k > E, unsupported dtype value */
-#define MOE_ERR_UNSUPPORTED 2    /* valid request this build does not implement */
+#define MOE_ERR_UNSUPPORTED 2    /* valid request no kernel of the library covers */
 #define MOE_ERR_HIP 3            /* a HIP runtime call failed; see moe_last_hip_error */
 #define MOE_ERR_NO_MEMORY 4      /* workspace too small, or host bookkeeping allocation failed */
 #define MOE_ERR_CACHE_CAPACITY 5 /* slot pool or staging buffer too small for the request */
@@ -218,6 +218,27 @@ typedef struct moe_ffn_args {
  * sets) together with that same limit.
  */
 int moe_expert_ffn(const moe_ffn_args* args, moe_stream_t stream);
+
+/*
+ * Expert FFN and combine in one call: out[t] = residual[t] + shared(x_t) +
+ * sum_{j<k} gates[t,j] * FFN_{ids[t,j]}(x_t), the whole layer output after the
+ * routing ("How Strata works", three-tier division: routed small experts plus
+ * the resident shared expert; the weighted sum is the mixture's output).
+ *   args: as for moe_expert_ffn, phase must be 0 (args->y_perm and
+ *         args->y_shared must still be valid buffers: the shapes without a
+ *         fused kernel go through them);
+ *   ids [T, k] (from moe_route), dest [T*k] (from moe_permute), gates [T, k],
+ *   residual [T, d] fp32 or NULL, out [T, d] fp32 (may alias residual).
+ * For float mode, int4 weights, T <= 8 and f / 128 in {2, 4, 6, 8} the down
+ * projection and the weighted sum run in one kernel: every workgroup owns one
+ * token's 16 output rows, the expert outputs stay in fp32 and are summed in a
+ * fixed order (deterministic; neither y_perm nor y_shared is written).  Other
+ * shapes run moe_expert_ffn then moe_combine.  Ids outside [0, E) contribute
+ * nothing.  Errors: those of moe_expert_ffn; MOE_ERR_INVALID_ARG for a phase
+ * other than 0 or a null ids, dest, gates or out.
+ */
+int moe_expert_ffn_combine(const moe_ffn_args* args, const int32_t* ids, const int32_t* dest, const float* gates,
+                           const float* residual, float* out, moe_stream_t stream);
 
 /*
  * Combine: out[t] = residual[t] + y_shared[t] + sum_{j<k} gates[t,j] * y_perm[dest[t*k+j]],

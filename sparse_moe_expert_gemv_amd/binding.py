@@ -27,7 +27,7 @@ MOE_ACT_FLOAT, MOE_ACT_Q8 = 0, 1
 EXPORTED = [
     "moe_version", "moe_last_hip_error", "moe_status_string", "moe_expert_bytes", "moe_pack_experts",
     "moe_unpack_experts", "moe_workspace_size", "moe_route", "moe_route_permute", "moe_permute", "moe_quantize_act",
-    "moe_expert_ffn", "moe_rmsnorm",
+    "moe_expert_ffn", "moe_expert_ffn_combine", "moe_rmsnorm",
     "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
     "moe_cache_stage", "moe_cache_map_host", "moe_usage_accumulate", "moe_cache_plan", "moe_cache_replace",
 ]
@@ -78,6 +78,7 @@ def lib():
             "moe_quantize_act": ([P, I, I, I, P, P, P], I),
             "moe_rmsnorm": ([P, I, I, C.c_float, P, P], I),
             "moe_expert_ffn": ([C.POINTER(FfnArgs), P], I),
+            "moe_expert_ffn_combine": ([C.POINTER(FfnArgs), P, P, P, P, P, P], I),
             "moe_combine": ([P, I, P, P, P, P, I, I, I, P, P], I),
             "moe_cache_create": ([C.POINTER(P), I, I, I, S, P, P, I, I], I),
             "moe_cache_destroy": ([P], I),
@@ -190,8 +191,8 @@ def moe_quantize_act(x, xq, sx, stream=None):
                                                       _stream(stream)))
 
 
-def moe_expert_ffn(*, T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offsets, sorted_idx, active, y_perm,
-                   ws, x=None, xq=None, sx=None, shared_blob=None, y_shared=None, stream=None, phase=0):
+def _ffn_args(T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offsets, sorted_idx, active, y_perm, ws, x, xq,
+              sx, shared_blob, y_shared, phase):
     a = FfnArgs()
     a.T, a.d, a.f, a.E, a.k = T, d, f, E, k
     a.wfmt, a.act_mode = wfmt, act_mode
@@ -207,7 +208,23 @@ def moe_expert_ffn(*, T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offset
     a.y_shared = None if y_shared is None else y_shared.data_ptr()
     a.ws, a.ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
     a.phase = phase
+    return a
+
+
+def moe_expert_ffn(*, T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offsets, sorted_idx, active, y_perm,
+                   ws, x=None, xq=None, sx=None, shared_blob=None, y_shared=None, stream=None, phase=0):
+    a = _ffn_args(T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offsets, sorted_idx, active, y_perm, ws, x, xq,
+                  sx, shared_blob, y_shared, phase)
     _check("moe_expert_ffn", lib().moe_expert_ffn(C.byref(a), _stream(stream)))
+
+
+def moe_expert_ffn_combine(*, T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offsets, sorted_idx, active, y_perm,
+                           ws, ids, dest, gates, out, residual=None, x=None, xq=None, sx=None, shared_blob=None,
+                           y_shared=None, stream=None):
+    a = _ffn_args(T, d, f, E, k, wfmt, act_mode, expert_ptrs, counts, offsets, sorted_idx, active, y_perm, ws, x, xq,
+                  sx, shared_blob, y_shared, 0)
+    _check("moe_expert_ffn_combine", lib().moe_expert_ffn_combine(C.byref(a), _ptr(ids), _ptr(dest), _ptr(gates),
+                                                                  _ptr(residual), _ptr(out), _stream(stream)))
 
 
 def moe_combine(y_perm, dest, gates, y_shared, residual, out, stream=None):

@@ -181,6 +181,25 @@ int moe_expert_ffn(const moe_ffn_args* a, moe_stream_t s) {
     return a->act_mode == MOE_ACT_FLOAT ? launch_ffn_float(a, w, as_stream(s)) : launch_ffn_q8(a, w, as_stream(s));
 }
 
+int moe_expert_ffn_combine(const moe_ffn_args* a, const int32_t* ids, const int32_t* dest, const float* gates,
+                           const float* residual, float* out, moe_stream_t s) {
+    if (!a || a->phase != 0) return MOE_ERR_INVALID_ARG;
+    if (a->T > 0 && (!ids || !dest || !gates || !out)) return MOE_ERR_INVALID_ARG;
+    if (!down_combine_ok(a)) {
+        const int rc = moe_expert_ffn(a, s);
+        if (rc || a->T == 0) return rc;
+        return moe_combine(a->y_perm, a->y_dtype, dest, gates, a->shared_blob ? a->y_shared : nullptr, residual,
+                           a->T, a->k, a->d, out, s);
+    }
+    moe_ffn_args g = *a;
+    g.phase = 1;  // gate/up + SwiGLU into the workspace; validates every argument
+    const int rc = moe_expert_ffn(&g, s);
+    if (rc || a->T == 0) return rc;
+    Workspace w;
+    workspace_layout(a->T, a->d, a->f, a->E, a->k, a->act_mode, (char*)a->ws, &w);
+    return launch_down_combine(a, w, ids, dest, gates, residual, out, as_stream(s));
+}
+
 int moe_combine(const void* y_perm, int y_dtype, const int32_t* dest, const float* gates, const float* y_shared,
                 const float* residual, int T, int k, int d, float* out, moe_stream_t s) {
     if (T < 0 || k < 1 || d <= 0 || d % 4 || (y_dtype != MOE_DT_F32 && y_dtype != MOE_DT_F16))

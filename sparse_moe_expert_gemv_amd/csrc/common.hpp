@@ -135,6 +135,12 @@ int launch_permute_block(const int32_t* ids, int n, int E, int32_t* counts, int3
                          int32_t* dest, int32_t* active, hipStream_t s);
 int launch_rmsnorm(const float* x, int T, int d, float eps, float* out, hipStream_t s);
 int launch_quant_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float* sx, hipStream_t s);
+// down projection + weighted combine in one kernel (float mode, int4, few
+// tokens): out = residual + shared + sum_j g_j y_j without y_perm
+constexpr int kDownCombineMax = 8;
+bool down_combine_ok(const moe_ffn_args* a);
+int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t* ids, const int32_t* dest,
+                        const float* gates, const float* residual, float* out, hipStream_t s);
 int launch_ffn_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s);
 int launch_ffn_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s);
 size_t q8_tile_capacity(int T, int k, int E);  // int2 entries of the q8 tile list

@@ -402,6 +402,8 @@ __device__ __forceinline__ half8 offset_seed_b() {
 }
 
 constexpr int kTokMax = 16;   // tokens of the token-dense kernels
+constexpr int kDcWaves = 4;     // wavefronts of ffn_down_combine (slots split over them)
+constexpr int kDcWavesFew = 8;  // the same for one or two tokens
 constexpr int kPipe = 2;      // quant tiles in flight ahead of the products
 
 // Raw 16-byte token chunks, converted to fp16 only when stored to LDS, so that
@@ -780,6 +782,155 @@ static bool launch_down_tok16(const moe_ffn_args* a, const _Float16* h, int slot
     default: return false;
     }
 #undef MOE_DN16
+}
+
+// ---- few tokens, int4: down projection and weighted combine in one kernel ----
+// Workgroup = (token t, 16 output rows); its NW wavefronts split the token's
+// k routed slots and the shared expert (slot j goes to wavefront j % NW).
+// The slots' expert pointers, gates and h rows are staged once per workgroup
+// (h rows in LDS, chunk c of slot j at j * f / 8 + c).  A wavefront streams
+// the 16-row down strip of each of its slots (all f / 128 quant tiles at
+// once), issuing the next slot's tiles before the products of the current
+// one (a second slot ahead measured slower); the A operand repeats the slot's
+// h row in all 16 MFMA rows, so every accumulator row holds the same 16
+// outputs.  Each wavefront adds gate * y in
+// its slot order; the NW partial vectors meet in LDS and are added in
+// wavefront order after the residual (deterministic).  The expert outputs
+// stay in fp32: no y_perm rows are written or read back.
+constexpr int kDcMaxSlots = 65;  // k <= 64 routed slots + the shared expert
+constexpr int kDcChunks = 8;     // h chunks staged per thread: nj f / 8 <= kDcChunks * 64 * NW
+template <int NKT, int NW>
+__global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __restrict__ h, int T, int d, int f,
+                                                            int k, int E, const void* const* __restrict__ expert_ptrs,
+                                                            const uint8_t* __restrict__ shared_blob,
+                                                            const int32_t* __restrict__ ids,
+                                                            const int32_t* __restrict__ dest,
+                                                            const float* __restrict__ gates, const float* residual,
+                                                            float* out) {
+    extern __shared__ __align__(16) uint4 hrow[];  // [nj][f / 8]
+    __shared__ const uint8_t* s_blob[kDcMaxSlots];  // nullptr: the slot is ignored
+    __shared__ int32_t s_p[kDcMaxSlots];
+    __shared__ float s_g[kDcMaxSlots];
+    __shared__ float part[NW][16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_strips = d / 16;
+    const int t = blockIdx.x / n_strips, strip = blockIdx.x % n_strips;
+    const int nj = k + (shared_blob ? 1 : 0);
+    const int HC = f / 8;
+    for (int j = threadIdx.x; j < nj; j += 64 * NW) {
+        if (j < k) {
+            const int e = ids[(size_t)t * k + j];
+            const bool ok = (unsigned)e < (unsigned)E;  // ids outside [0, E) are ignored, as in the grouping
+            s_blob[j] = ok ? (const uint8_t*)expert_ptrs[e] : nullptr;
+            s_p[j] = ok ? dest[(size_t)t * k + j] : 0;
+            s_g[j] = gates[(size_t)t * k + j];
+        } else {
+            s_blob[j] = shared_blob;
+            s_p[j] = T * k + t;
+            s_g[j] = 1.f;
+        }
+    }
+    __syncthreads();
+    const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
+    const size_t qoff = L.dn.qoff + (size_t)strip * NKT * 1024 + lane * 16;
+    const size_t soff = L.dn.soff + (size_t)strip * NKT * 128 + (lane & 15) * 8;
+    uint4v q[NKT], qn[NKT];
+    uint2v sc[NKT], scn[NKT];
+    auto issue = [&](int j, uint4v (&qq)[NKT], uint2v (&ss)[NKT]) {
+        const uint8_t* blob = s_blob[j];
+        if (blob == nullptr) return;
+        const uint4v* pq = reinterpret_cast<const uint4v*>(blob + qoff);
+        const uint2v* ps = reinterpret_cast<const uint2v*>(blob + soff);
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) {
+            ss[i] = gload_nt(ps + i * 16);
+            qq[i] = gload_nt(pq + i * 64);
+        }
+    };
+    // the slots' h rows (at most kDcChunks 16-byte chunks per thread) and the
+    // first slot's quant tiles are all in flight before any LDS store
+    const int nh = nj * HC;
+    uint4v v[kDcChunks];
+#pragma unroll
+    for (int u = 0; u < kDcChunks; ++u) {  // past the end: the last chunk again (not stored)
+        const int idx = min((int)threadIdx.x + u * 64 * NW, nh - 1);
+        const int j = idx / HC;
+        v[u] = gload(reinterpret_cast<const uint4v*>(h + (size_t)s_p[j] * f) + (idx - j * HC));
+    }
+    if (wave < nj) issue(wave, q, sc);
+#pragma unroll
+    for (int u = 0; u < kDcChunks; ++u) {
+        const int idx = (int)threadIdx.x + u * 64 * NW;
+        if (idx < nh) hrow[idx] = __builtin_bit_cast(uint4, v[u]);
+    }
+    __syncthreads();
+    uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
+    asm volatile("" : "+s"(mlo), "+s"(mhi), "+v"(magic));
+    float tot = 0.f;
+    for (int j = wave; j < nj; j += NW) {
+        if (j + NW < nj) issue(j + NW, qn, scn);
+        __builtin_amdgcn_sched_barrier(0);  // the next slot's tiles are in flight before these products
+        if (s_blob[j] != nullptr) {
+            const uint4* hr = hrow + j * HC + (lane >> 4);
+            float4v acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < NKT; ++i)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const half8 B = dequant4_scaled(q[i][b], scale_pair(sc[i], b), mlo, mhi, magic);
+                    const half8 A = __builtin_bit_cast(half8, hr[(i * 4 + b) * 4]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
+                }
+            tot = fmaf(s_g[j], acc[0], tot);  // lane l < 16: output row strip * 16 + l
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NKT; ++i) {
+            q[i] = qn[i];
+            sc[i] = scn[i];
+        }
+    }
+    if (lane < 16) part[wave][lane] = tot;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const size_t o = (size_t)t * d + strip * 16 + threadIdx.x;
+        float sum = residual ? residual[o] : 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += part[w][threadIdx.x];
+        out[o] = sum;
+    }
+}
+
+bool down_combine_ok(const moe_ffn_args* a) {
+    const int nkt = a->f / 128;
+    const int nj = a->k + (a->shared_blob ? 1 : 0);
+    const int nw = a->T <= 2 ? kDcWavesFew : kDcWaves;
+    return a->act_mode == MOE_ACT_FLOAT && a->wfmt == MOE_WFMT_I4B32 && a->T <= kDownCombineMax && a->d % 16 == 0 &&
+           (nkt == 2 || nkt == 4 || nkt == 6 || nkt == 8) && (long)nj * (a->f / 8) <= (long)kDcChunks * 64 * nw;
+}
+
+int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t* ids, const int32_t* dest,
+                        const float* gates, const float* residual, float* out, hipStream_t s) {
+    if (!down_combine_ok(a)) return MOE_ERR_UNSUPPORTED;
+    const _Float16* h = reinterpret_cast<const _Float16*>(w.h);
+    const dim3 grid(a->T * (a->d / 16));
+    const uint8_t* sb = (const uint8_t*)a->shared_blob;
+    const size_t lds = (size_t)(a->k + (sb ? 1 : 0)) * a->f * sizeof(_Float16);
+#define MOE_DC(NKT, NW)                                                                                          \
+    ffn_down_combine<NKT, NW><<<grid, 64 * NW, lds, s>>>(h, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs, sb, ids, \
+                                                        dest, gates, residual, out)
+#define MOE_DC_NW(NKT)                          \
+    if (a->T <= 2) MOE_DC(NKT, kDcWavesFew);    \
+    else MOE_DC(NKT, kDcWaves)
+    switch (a->f / 128) {
+    case 2: MOE_DC_NW(2); break;
+    case 4: MOE_DC_NW(4); break;
+    case 6: MOE_DC_NW(6); break;
+    default: MOE_DC_NW(8); break;
+    }
+#undef MOE_DC_NW
+#undef MOE_DC
+    return check_launch();
 }
 
 size_t float_h_bytes(int T, int f, int k) { return ((size_t)T * k + T) * (size_t)f * sizeof(_Float16); }

@@ -40,8 +40,12 @@ def pointer_table(packed: torch.Tensor) -> torch.Tensor:
 
 class MoELayer:
     def __init__(self, Wr, bias, experts, shared, *, d, f, k, wfmt, act_mode, max_T, device="cuda",
-                 y_dtype=None, experts_are_packed=False, expert_ptrs=None):
+                 y_dtype=None, experts_are_packed=False, expert_ptrs=None, fuse_combine=True):
         self.device = torch.device(device)
+        # forward through moe_expert_ffn_combine (down projection and weighted
+        # sum in one kernel where one exists); False: moe_expert_ffn then
+        # moe_combine, which leave y_perm / y_shared filled
+        self.fuse_combine = fuse_combine
         self.d, self.f, self.k, self.wfmt, self.act_mode = d, f, k, wfmt, act_mode
         self.Wr = torch.as_tensor(np.ascontiguousarray(Wr, dtype=np.float32)).to(self.device)
         self.E = self.Wr.shape[0]
@@ -102,12 +106,16 @@ class MoELayer:
                       counts=self.counts, offsets=self.offsets, sorted_idx=self.sorted_idx[:n],
                       active=self.active, y_perm=self.y_perm[:n], ws=ws, shared_blob=self.shared,
                       y_shared=self.y_shared[:T] if self.shared is not None else None, stream=stream)
+        o = self.out[:T] if out is None else out
         if self.act_mode == B.MOE_ACT_Q8:
             B.moe_quantize_act(x, self.xq[:T], self.sx[:T], stream)
-            B.moe_expert_ffn(xq=self.xq[:T], sx=self.sx[:T], **common)
+            common.update(xq=self.xq[:T], sx=self.sx[:T])
         else:
-            B.moe_expert_ffn(x=x, **common)
-        o = self.out[:T] if out is None else out
-        B.moe_combine(self.y_perm[:n], self.dest[:n], gates, self.y_shared[:T] if self.shared is not None else None,
-                      residual, o, stream)
+            common.update(x=x)
+        if self.fuse_combine:
+            B.moe_expert_ffn_combine(ids=ids, dest=self.dest[:n], gates=gates, residual=residual, out=o, **common)
+        else:
+            B.moe_expert_ffn(**common)
+            B.moe_combine(self.y_perm[:n], self.dest[:n], gates,
+                          self.y_shared[:T] if self.shared is not None else None, residual, o, stream)
         return o

@@ -149,11 +149,11 @@ class ExpertStack:
                       y_shared=None if self.shared is None else self.y_shared[:T], stream=stream)
         if self.act_mode == B.MOE_ACT_Q8:
             B.moe_quantize_act(xn, self.xq[:T], self.sx[:T], stream)
-            B.moe_expert_ffn(xq=self.xq[:T], sx=self.sx[:T], **common)
+            common.update(xq=self.xq[:T], sx=self.sx[:T])
         else:
-            B.moe_expert_ffn(x=xn, **common)
-        B.moe_combine(self.y_perm[:n], self.dest[:n], self.gates[:T],
-                      None if self.shared is None else self.y_shared[:T], h, out, stream)
+            common.update(x=xn)
+        B.moe_expert_ffn_combine(ids=self.ids[:T], dest=self.dest[:n], gates=self.gates[:T], residual=h, out=out,
+                                 **common)
 
     def forward(self, x: torch.Tensor, keep=(), copy_only=False, compute_only_tables=None, ids_out=None):
         """Run all layers on x ([T, d] fp32).  Returns (h_L, {l: (h_l, norm(h_l)) for l in keep}).

@@ -331,12 +331,65 @@ def test_route_permute_fused_equals_separate_calls(name, T):
             assert np.array_equal(a[kk], b[kk]), kk
 
 
+@pytest.mark.parametrize("T,f", [(1, 768), (2, 768), (4, 768), (8, 768), (4, 256), (3, 512), (5, 1024), (9, 768)])
+def test_ffn_combine_entry_matches_separate_calls_and_oracle(T, f):
+    """moe_expert_ffn_combine (T <= 8, int4: the down projection and the
+    gate-weighted sum in one kernel; T = 9: moe_expert_ffn then moe_combine)
+    against moe_expert_ffn with fp32 rows + moe_combine on the same routing,
+    with a residual, and against the oracle.  Both sides sum the same fp32
+    products, in different orders."""
+    L = synth.make_layer("decode_t4", T=T, overrides={"f": f})
+    res = np.random.Generator(np.random.PCG64(21)).standard_normal((T, L.cfg.d)).astype(np.float32)
+    G, out, st, o = run_layer(L, residual=res, y_dtype=torch.float32)
+    check_routing(st, o, L.cfg.E)
+    check_float(out, o["out"], "ffn + combine entry, T=%d f=%d" % (T, f))
+    G.fuse_combine = False
+    ref = host(G.forward(x_tensor(L), residual=torch.from_numpy(res).to(DEV)))
+    torch.cuda.synchronize()
+    ok, rel, mx = R.within_tolerance(out, ref, rel=1e-5, maxabs_frac=1e-5)
+    assert ok, "fused vs separate: rel-L2 %.3e, max-abs/RMS %.3e" % (rel, mx)
+
+
+def test_ffn_combine_entry_skips_ids_outside_range():
+    """An id outside [0, E) contributes nothing: the output equals the one with
+    that slot's gate set to zero (bit for bit: gate 0 adds an exact zero)."""
+    L = synth.make_layer("decode_t4", T=4)
+    c = L.cfg
+    G = gpu_layer(L, y_dtype=torch.float32)
+    xt = x_tensor(L)
+    T, k, E, n = c.T, c.k, c.E, c.T * c.k
+    G.forward(xt)
+    torch.cuda.synchronize()
+    ids0, gates0 = G.ids[:T].clone(), G.gates[:T].clone()
+
+    def run(ids, gates):
+        ws = G._ws_for(T)
+        B.moe_permute(ids, E, G.counts, G.offsets, G.sorted_idx[:n], G.dest[:n], G.active, ws)
+        out = torch.empty((T, c.d), dtype=torch.float32, device=DEV)
+        B.moe_expert_ffn_combine(T=T, d=c.d, f=c.f, E=E, k=k, wfmt=c.wfmt, act_mode=G.act_mode,
+                                 expert_ptrs=G.expert_ptrs, counts=G.counts, offsets=G.offsets,
+                                 sorted_idx=G.sorted_idx[:n], active=G.active, y_perm=G.y_perm[:n], ws=ws,
+                                 shared_blob=G.shared, y_shared=G.y_shared[:T], x=xt, ids=ids, dest=G.dest[:n],
+                                 gates=gates, out=out)
+        torch.cuda.synchronize()
+        return host(out)
+
+    bad = ids0.clone()
+    bad[1, 3] = -1
+    bad[2, 0] = E
+    zg = gates0.clone()
+    zg[1, 3] = 0.0
+    zg[2, 0] = 0.0
+    assert np.array_equal(run(bad, gates0), run(ids0, zg))
+
+
 @pytest.mark.parametrize("name", ["decode_t4", "tiny"])
 def test_ffn_phases_equal_whole_call(name):
     """moe_expert_ffn with phase 1 (gate/up) then phase 2 (down) on the same
     workspace gives bit-identical outputs to phase 0."""
     L = _layer(name)
     G = gpu_layer(L)
+    G.fuse_combine = False  # the separate calls leave y_perm filled
     xt = x_tensor(L)
     T, k = L.cfg.T, L.cfg.k
     G.forward(xt)

@@ -88,6 +88,17 @@ def test_invalid_arguments_rejected_before_any_hip_call():
     assert L.moe_expert_ffn(C.byref(a), None) == B.MOE_ERR_INVALID_ARG
     a.act_mode, a.T = 0, 0
     assert L.moe_expert_ffn(C.byref(a), None) == B.MOE_OK
+    # the FFN + combine entry: its own arguments first, then those of moe_expert_ffn
+    dummy = C.c_void_p(0x1000)
+    assert L.moe_expert_ffn_combine(None, dummy, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    a.T = 4
+    assert L.moe_expert_ffn_combine(C.byref(a), None, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_combine(C.byref(a), dummy, dummy, dummy, None, None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_combine(C.byref(a), dummy, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    a.phase = 1
+    assert L.moe_expert_ffn_combine(C.byref(a), dummy, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    a.phase, a.T = 0, 0
+    assert L.moe_expert_ffn_combine(C.byref(a), None, None, None, None, None, None) == B.MOE_OK
 
 
 def test_workspace_too_small_is_reported():
