@@ -1,10 +1,11 @@
 """Benchmark of the sparse-MoE FFN layer hot path on one MI355X.
 
-One step = one pass of the whole layer (moe_route_permute (routing and
-grouping) -> [moe_quantize_act] -> moe_expert_ffn_combine (expert FFN and the
-gate-weighted combine; for decode batches with int4 weights the down projection
-and the combine are one kernel)) over one batch of seeded synthetic input
-already resident in HBM.  Default workload: the decode layer
+One step = one pass of the whole layer over one batch of seeded synthetic
+input already resident in HBM: moe_route_permute (routing and grouping) ->
+[moe_quantize_act] -> moe_expert_ffn_combine (expert FFN and the gate-weighted
+combine); for decode batches (T <= 8, int4 weights) moe_route ->
+moe_expert_ffn_combine_slots, where every routed slot is its own work item and
+the down projection and the combine are one kernel.  Default workload: the decode layer
 (d=2048, 512 int4 experts + shared, top-10, f=768) at T=4 tokens, the MTP
 verify batch; ``--workload`` selects another layer (decode_t1, prefill, skew,
 tiny) or a 48-layer stack over the 4,500-slot expert pool (``stack``: the
@@ -158,15 +159,29 @@ def main():
             xs.append(torch.from_numpy(xb).to(dev))
     torch.cuda.synchronize()
 
+    # decode batches with int4 weights need no grouping of the slots: routing
+    # gives ids and gates, and every routed slot is its own FFN work item
+    by_slot = mode == B.MOE_ACT_FLOAT and cfg.wfmt == 4 and T <= 8
+
     def run_route(G, x):
         ws = G._ws_for(T)
         n = T * cfg.k
+        if by_slot:
+            B.moe_route(x, G.Wr, G.bias, cfg.k, G.ids[:T], G.gates[:T], ws)
+            return
         B.moe_route_permute(x, G.Wr, G.bias, cfg.k, G.ids[:T], G.gates[:T], G.counts, G.offsets,
                             G.sorted_idx[:n], G.dest[:n], G.active, ws)
         if mode == B.MOE_ACT_Q8:
             B.moe_quantize_act(x, G.xq[:T], G.sx[:T])
 
+    def run_slots(G, x, phase=0):
+        B.moe_expert_ffn_combine_slots(T=T, d=cfg.d, f=cfg.f, E=cfg.E, k=cfg.k, wfmt=cfg.wfmt, act_mode=mode,
+                                       expert_ptrs=G.expert_ptrs, ws=G._ws_for(T), ids=G.ids[:T], gates=G.gates[:T],
+                                       out=G.out[:T], x=x, shared_blob=G.shared, phase=phase)
+
     def run_ffn(G, x, phase=0):
+        if by_slot:
+            return run_slots(G, x, phase)
         n = T * cfg.k
         common = dict(T=T, d=cfg.d, f=cfg.f, E=cfg.E, k=cfg.k, wfmt=cfg.wfmt, act_mode=mode,
                       expert_ptrs=G.expert_ptrs, counts=G.counts, offsets=G.offsets, sorted_idx=G.sorted_idx[:n],
@@ -180,6 +195,8 @@ def main():
     def run_ffn_combine(G, x):
         # expert FFN and the weighted combine (one kernel for the down projection
         # and the sum where the library has it)
+        if by_slot:
+            return run_slots(G, x)
         n = T * cfg.k
         common = dict(T=T, d=cfg.d, f=cfg.f, E=cfg.E, k=cfg.k, wfmt=cfg.wfmt, act_mode=mode,
                       expert_ptrs=G.expert_ptrs, counts=G.counts, offsets=G.offsets, sorted_idx=G.sorted_idx[:n],
@@ -256,8 +273,9 @@ def main():
     timed(lambda i: run_all(gu_r, gu_graphs, rotate), 1)
     gu_ms = timed(lambda i: run_all(gu_r, gu_graphs, steps), 1) / steps
 
-    # algorithmic work per gate/up launch, from each copy's routing (fixed input per copy)
-    n_act = [int(G.active[0].item()) for G in layers]
+    # algorithmic work per gate/up launch, from each copy's routing (fixed input per copy):
+    # the distinct experts picked (the by-slot launch reads an expert once per slot)
+    n_act = [int(np.unique(G.ids[:T].cpu().numpy()).size) for G in layers]
     per = [gateup_algorithmic(cfg, n, T) for n in n_act]
     alg_bytes = float(np.mean([p[0] for p in per]))
     alg_ops = float(np.mean([p[1] for p in per]))
@@ -272,7 +290,8 @@ def main():
     if mode == B.MOE_ACT_Q8:
         roof["kernel"] = "ffn_q8_tiled<0> (moe_expert_ffn phase 1)" if cfg.wfmt == 4 else "ffn_q8_gateup (moe_expert_ffn phase 1)"
     else:
-        roof["kernel"] = ("ffn_gateup_tok16 (moe_expert_ffn phase 1)" if cfg.wfmt == 4 and T <= 16
+        roof["kernel"] = ("ffn_gateup_tok16 by slot (moe_expert_ffn_combine_slots phase 1)" if by_slot
+                          else "ffn_gateup_tok16 (moe_expert_ffn phase 1)" if cfg.wfmt == 4 and T <= 16
                           else "ffn_gateup_tok64 (moe_expert_ffn phase 1)" if T <= 64
                           else "ffn_float_gateup (moe_expert_ffn phase 1)")
     roof["kernel_ms"] = round(gu_ms, 5)

@@ -241,6 +241,31 @@ int moe_expert_ffn_combine(const moe_ffn_args* args, const int32_t* ids, const i
                            const float* residual, float* out, moe_stream_t stream);
 
 /*
+ * Decode batches without the grouping step: the same output as
+ * moe_route_permute + moe_expert_ffn_combine, bit for bit, from moe_route's
+ * ids and gates alone.  Every routed slot (t, j) is its own gate/up work item
+ * reading expert ids[t, j] (only the picked experts compute: "single RTX 5090
+ * runs a 125B model", on-demand expert scheduling); an expert picked by
+ * several tokens is read once per slot, which at a few tokens over hundreds
+ * of experts is rare.  The down projection and the weighted sum are the
+ * fused kernel of moe_expert_ffn_combine; slot (t, j) keeps h row t*k + j.
+ *   args: as for moe_expert_ffn; counts, offsets, sorted_idx, active, y_perm
+ *         and y_shared are not read (may be NULL); phase 0 = the whole call,
+ *         1 = the gate/up launch alone (h left in the workspace; gates,
+ *         residual and out unused);
+ *   ids [T, k], gates [T, k] (moe_route), residual [T, d] fp32 or NULL,
+ *   out [T, d] fp32 (may alias residual).  Ids outside [0, E) contribute nothing.
+ * Supported: float mode, int4 weights, T <= 8, d a power of two with
+ * T * d * 2 <= 64 KiB, f / 128 in {2, 4, 6, 8} and (k + 1) * f <= 16384
+ * (32768 for T <= 2); otherwise MOE_ERR_UNSUPPORTED before any launch.
+ * Errors: MOE_ERR_INVALID_ARG (phase other than 0 or 1, bad shapes, null x,
+ * expert_ptrs, ws, ids, gates or out), MOE_ERR_NO_MEMORY (workspace smaller
+ * than moe_workspace_size).
+ */
+int moe_expert_ffn_combine_slots(const moe_ffn_args* args, const int32_t* ids, const float* gates,
+                                 const float* residual, float* out, moe_stream_t stream);
+
+/*
  * Combine: out[t] = residual[t] + y_shared[t] + sum_{j<k} gates[t,j] * y_perm[dest[t*k+j]],
  * summed in j order (deterministic).
  *   y_perm [T*k, d] (y_dtype F32 or F16), dest [T*k], gates [T, k],

@@ -141,6 +141,11 @@ constexpr int kDownCombineMax = 8;
 bool down_combine_ok(const moe_ffn_args* a);
 int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t* ids, const int32_t* dest,
                         const float* gates, const float* residual, float* out, hipStream_t s);
+// decode without the grouping: gate/up per routed slot, then the fused down +
+// combine (h row of slot (t, j) = t k + j)
+bool ffn_combine_slots_ok(const moe_ffn_args* a);
+int launch_ffn_combine_slots(const moe_ffn_args* a, const Workspace& w, const int32_t* ids, const float* gates,
+                             const float* residual, float* out, hipStream_t s);
 int launch_ffn_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s);
 int launch_ffn_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s);
 size_t q8_tile_capacity(int T, int k, int E);  // int2 entries of the q8 tile list

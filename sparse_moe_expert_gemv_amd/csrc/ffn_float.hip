@@ -466,14 +466,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 // through buffer resources of size 0 when there is nothing to read, so that
 // the code stays straight-line and every wait is exact; only then the tokens
 // go to LDS.
-template <int NT, int S, typename XT, int NTH = 256>
+// BY_SLOT: no grouping; work slot a < T k is the routed slot a itself (expert
+// slot_ids[a], its one row written to h row a), slot T k the shared expert.
+template <int NT, int S, typename XT, int NTH = 256, bool BY_SLOT = false>
 __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x, int T, int d, int f, int k, int E,
                                                         const void* const* __restrict__ expert_ptrs,
                                                         const uint8_t* __restrict__ shared_blob,
                                                         const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ sorted_idx,
-                                                        const int32_t* __restrict__ active, _Float16* __restrict__ h) {
+                                                        const int32_t* __restrict__ active, _Float16* __restrict__ h,
+                                                        const int32_t* __restrict__ slot_ids) {
     extern __shared__ __align__(16) uint4 xs4[];  // [T][d / 8] fp16, chunk c of row r at (c ^ r); later [4][2][4][64] f32
     const int XC = d / 8;           // a power of two (checked by the launcher)
     const int lxc = __builtin_ctz(XC);
@@ -487,21 +490,37 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
     XChunk<XT> xr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xr[j].load(x + (size_t)min((int)threadIdx.x + j * NTH, nx - 1) * 8);
-    const int n_active = active[0];
-    const int e_raw = active[1 + min(a, E - 1)];
-    const int e_c = min(max(e_raw, 0), E - 1);
-    const uint8_t* pe = (const uint8_t*)expert_ptrs[e_c];
-    const int ce = counts[e_c], oe = offsets[e_c];
-    const bool routed = a < n_active;
-    const uint8_t* blob = routed ? pe : (a == n_active ? shared_blob : nullptr);
-    const int e = routed ? e_raw : -1;
-    const int c = routed ? ce : T, p0 = routed ? oe : T * k;
+    const uint8_t* blob;
+    int e, c, p0, slot_of;
+    if constexpr (BY_SLOT) {
+        const int n_slots = T * k;
+        const bool routed = a < n_slots;
+        const int e_raw = slot_ids[min(a, n_slots - 1)];
+        const bool valid = (unsigned)e_raw < (unsigned)E;
+        const uint8_t* pe = (const uint8_t*)expert_ptrs[valid ? e_raw : 0];
+        blob = routed ? (valid ? pe : nullptr) : (a == n_slots ? shared_blob : nullptr);
+        e = routed ? e_raw : -1;
+        c = routed ? 1 : T;
+        p0 = routed ? a : n_slots;
+        slot_of = a;  // the slot's single row belongs to token a / k
+    } else {
+        const int n_active = active[0];
+        const int e_raw = active[1 + min(a, E - 1)];
+        const int e_c = min(max(e_raw, 0), E - 1);
+        const uint8_t* pe = (const uint8_t*)expert_ptrs[e_c];
+        const int ce = counts[e_c], oe = offsets[e_c];
+        const bool routed = a < n_active;
+        blob = routed ? pe : (a == n_active ? shared_blob : nullptr);
+        e = routed ? e_raw : -1;
+        c = routed ? ce : T;
+        p0 = routed ? oe : T * k;
+        const __amdgpu_buffer_rsrc_t ir = buf_rsrc(sorted_idx, e >= 0 ? (uint32_t)(T * k * 4) : 0u);
+        // slot of each of the first 64 rows (row m of the slot belongs to token slot_of / k)
+        slot_of = __builtin_amdgcn_raw_buffer_load_b32(ir, (p0 + min(lane, max(c - 1, 0))) * 4, 0, 0);
+    }
     const bool work = blob != nullptr;  // no weights behind this expert: leave its rows untouched
     const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
     const __amdgpu_buffer_rsrc_t wr = buf_rsrc(blob, work ? (uint32_t)L.total : 0u);
-    const __amdgpu_buffer_rsrc_t ir = buf_rsrc(sorted_idx, e >= 0 ? (uint32_t)(T * k * 4) : 0u);
-    // slot of each of the first 64 rows (row m of the slot belongs to token slot_of / k)
-    const int slot_of = __builtin_amdgcn_raw_buffer_load_b32(ir, (p0 + min(lane, max(c - 1, 0))) * 4, 0, 0);
     const uint32_t tile0 = (uint32_t)(strip * (S * NT) + part * NT);
     const uint32_t og = (uint32_t)L.g.qoff + tile0 * 1024 + lane * 16;
     const uint32_t ou = (uint32_t)L.u.qoff + tile0 * 1024 + lane * 16;
@@ -610,14 +629,16 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
             const int cm = min(c, 64);
             for (int m = 0; m < cm; ++m)
                 if ((unsigned)__builtin_amdgcn_readlane(slot_of, m) - lo < (unsigned)k) h[(size_t)(p0 + m) * f + col] = hv;
-            for (int m = 64; m < c; ++m)
-                if (sorted_idx[p0 + m] / k == t) h[(size_t)(p0 + m) * f + col] = hv;
+            if constexpr (!BY_SLOT)
+                for (int m = 64; m < c; ++m)
+                    if (sorted_idx[p0 + m] / k == t) h[(size_t)(p0 + m) * f + col] = hv;
         }
     }
 }
 
-template <typename XT>
-static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, hipStream_t s) {
+template <typename XT, bool BY_SLOT = false>
+static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, hipStream_t s,
+                                const int32_t* slot_ids = nullptr) {
     const int nkt = a->d / 128;
     const int items = slots * (a->f / 16);
     // few items (a single token routes to k + 1 slots): four wavefronts per item
@@ -625,9 +646,9 @@ static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, h
     const dim3 grid(four ? items : (items + 3) / 4);
     const size_t lds = std::max<size_t>((size_t)a->T * a->d * sizeof(_Float16), 8 * 2 * 4 * 64 * sizeof(float));
 #define MOE_GU16(NT, S)                                                                                         \
-    ffn_gateup_tok16<NT, S, XT, S == 2 ? 512 : 256><<<grid, S == 2 ? 512 : 256, lds, s>>>((const XT*)a->x, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs, \
-                                                       (const uint8_t*)a->shared_blob, a->counts, a->offsets,    \
-                                                       a->sorted_idx, a->active, h)
+    ffn_gateup_tok16<NT, S, XT, S == 2 ? 512 : 256, BY_SLOT><<<grid, S == 2 ? 512 : 256, lds, s>>>(              \
+        (const XT*)a->x, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->counts, \
+        a->offsets, a->sorted_idx, a->active, h, slot_ids)
     if (four) {
         switch (nkt) {
         case 8: MOE_GU16(2, 4); return true;
@@ -796,7 +817,8 @@ static bool launch_down_tok16(const moe_ffn_args* a, const _Float16* h, int slot
 // outputs.  Each wavefront adds gate * y in
 // its slot order; the NW partial vectors meet in LDS and are added in
 // wavefront order after the residual (deterministic).  The expert outputs
-// stay in fp32: no y_perm rows are written or read back.
+// stay in fp32: no y_perm rows are written or read back.  dest == nullptr:
+// the slots were not grouped and slot j's h row is t k + j.
 constexpr int kDcMaxSlots = 65;  // k <= 64 routed slots + the shared expert
 constexpr int kDcChunks = 8;     // h chunks staged per thread: nj f / 8 <= kDcChunks * 64 * NW
 template <int NKT, int NW>
@@ -822,7 +844,7 @@ __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __re
             const int e = ids[(size_t)t * k + j];
             const bool ok = (unsigned)e < (unsigned)E;  // ids outside [0, E) are ignored, as in the grouping
             s_blob[j] = ok ? (const uint8_t*)expert_ptrs[e] : nullptr;
-            s_p[j] = ok ? dest[(size_t)t * k + j] : 0;
+            s_p[j] = !ok ? 0 : dest ? dest[(size_t)t * k + j] : t * k + j;  // no dest: h row = slot
             s_g[j] = gates[(size_t)t * k + j];
         } else {
             s_blob[j] = shared_blob;
@@ -931,6 +953,31 @@ int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t
 #undef MOE_DC_NW
 #undef MOE_DC
     return check_launch();
+}
+
+// the by-slot gate/up launch has an instance (the conditions of
+// launch_gateup_tok16 and of the token-dense path in run_float)
+static bool gateup_tok16_by_slot_ok(const moe_ffn_args* a) {
+    if (a->T > kTokMax || (size_t)a->T * a->d * 2 > 64 * 1024 || (a->d & (a->d - 1)) != 0) return false;
+    const int nkt = a->d / 128;
+    const int items = (a->T * a->k + (a->shared_blob ? 1 : 0)) * (a->f / 16);
+    if (items < 1024 && nkt % 4 == 0) return nkt == 8 || nkt == 16 || nkt == 32;
+    return nkt == 4 || nkt == 8 || nkt == 16 || nkt == 32;
+}
+
+bool ffn_combine_slots_ok(const moe_ffn_args* a) { return down_combine_ok(a) && gateup_tok16_by_slot_ok(a); }
+
+int launch_ffn_combine_slots(const moe_ffn_args* a, const Workspace& w, const int32_t* ids, const float* gates,
+                             const float* residual, float* out, hipStream_t s) {
+    if (!ffn_combine_slots_ok(a)) return MOE_ERR_UNSUPPORTED;
+    const int slots = a->T * a->k + (a->shared_blob ? 1 : 0);
+    _Float16* h = reinterpret_cast<_Float16*>(w.h);
+    const bool ok = a->x_dtype == MOE_DT_F32 ? launch_gateup_tok16<float, true>(a, h, slots, s, ids)
+                                             : launch_gateup_tok16<uint16_t, true>(a, h, slots, s, ids);
+    if (!ok) return MOE_ERR_UNSUPPORTED;
+    const int rc = check_launch();
+    if (rc || a->phase == 1) return rc;
+    return launch_down_combine(a, w, ids, nullptr, gates, residual, out, s);
 }
 
 size_t float_h_bytes(int T, int f, int k) { return ((size_t)T * k + T) * (size_t)f * sizeof(_Float16); }

@@ -350,6 +350,48 @@ def test_ffn_combine_entry_matches_separate_calls_and_oracle(T, f):
     assert ok, "fused vs separate: rel-L2 %.3e, max-abs/RMS %.3e" % (rel, mx)
 
 
+@pytest.mark.parametrize("T,f", [(1, 768), (2, 768), (4, 768), (8, 768), (3, 512)])
+def test_ffn_combine_slots_equals_grouped_path_and_oracle(T, f):
+    """moe_route + moe_expert_ffn_combine_slots (no grouping: every routed
+    slot its own work item) gives the same ids, gates and layer output, bit
+    for bit, as moe_route_permute + moe_expert_ffn_combine, and meets the
+    float bar against the oracle."""
+    L = synth.make_layer("decode_t4", T=T, overrides={"f": f})
+    c = L.cfg
+    res = np.random.Generator(np.random.PCG64(23)).standard_normal((T, c.d)).astype(np.float32)
+    G, out, st, o = run_layer(L, residual=res)
+    G2 = gpu_layer(L)
+    G2.by_slot = True
+    out2 = host(G2.forward(x_tensor(L), residual=torch.from_numpy(res).to(DEV)))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(G2.ids[:T]), st["ids"])
+    assert np.array_equal(host(G2.gates[:T]).view(np.uint32), st["gates"].view(np.uint32))
+    assert np.array_equal(out2, out)
+    check_float(out2, o["out"], "by-slot decode layer, T=%d f=%d" % (T, f))
+
+
+def test_ffn_combine_slots_phase1_then_whole_call():
+    """Phase 1 of the by-slot entry (gate/up alone) followed by the whole call
+    on the same workspace gives the whole call's output (the phase leaves the
+    workspace in a state the whole call does not depend on)."""
+    L = synth.make_layer("decode_t4", T=4)
+    c = L.cfg
+    G = gpu_layer(L)
+    G.by_slot = True
+    xt = x_tensor(L)
+    ref = host(G.forward(xt)).copy()
+    common = dict(T=c.T, d=c.d, f=c.f, E=c.E, k=c.k, wfmt=c.wfmt, act_mode=G.act_mode, expert_ptrs=G.expert_ptrs,
+                  ws=G._ws_for(c.T), ids=G.ids[:c.T], gates=G.gates[:c.T], out=G.out[:c.T], x=xt,
+                  shared_blob=G.shared)
+    G.out.zero_()
+    B.moe_expert_ffn_combine_slots(phase=1, **common)
+    torch.cuda.synchronize()
+    assert not np.any(host(G.out[:c.T]))  # phase 1 writes no output
+    B.moe_expert_ffn_combine_slots(**common)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(G.out[:c.T]), ref)
+
+
 def test_ffn_combine_entry_skips_ids_outside_range():
     """An id outside [0, E) contributes nothing: the output equals the one with
     that slot's gate set to zero (bit for bit: gate 0 adds an exact zero)."""

@@ -99,6 +99,24 @@ def test_invalid_arguments_rejected_before_any_hip_call():
     assert L.moe_expert_ffn_combine(C.byref(a), dummy, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
     a.phase, a.T = 0, 0
     assert L.moe_expert_ffn_combine(C.byref(a), None, None, None, None, None, None) == B.MOE_OK
+    # the by-slot decode entry: argument checks, then the supported shapes, all before any HIP call
+    a.T, a.x_dtype = 4, B.MOE_DT_BF16
+    assert L.moe_expert_ffn_combine_slots(None, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_combine_slots(C.byref(a), dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    a.x, a.expert_ptrs, a.ws = 0x1000, 0x1000, 0x1000
+    assert L.moe_expert_ffn_combine_slots(C.byref(a), None, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_combine_slots(C.byref(a), dummy, dummy, None, dummy, None) == B.MOE_ERR_NO_MEMORY
+    a.ws_bytes = 1 << 40
+    a.phase = 2
+    assert L.moe_expert_ffn_combine_slots(C.byref(a), dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    a.phase = 0
+    for field, value in (("T", 9), ("act_mode", B.MOE_ACT_Q8), ("wfmt", 8), ("f", 640), ("d", 1536)):
+        old = getattr(a, field)
+        setattr(a, field, value)
+        assert L.moe_expert_ffn_combine_slots(C.byref(a), dummy, dummy, None, dummy, None) == B.MOE_ERR_UNSUPPORTED, field
+        setattr(a, field, old)
+    a.T = 0
+    assert L.moe_expert_ffn_combine_slots(C.byref(a), None, None, None, None, None) == B.MOE_OK
 
 
 def test_workspace_too_small_is_reported():
