@@ -337,7 +337,7 @@ def bench_decode_stack(a):
     c = S.cfg
     store = build_host_store(S.pool, c.wfmt, c.d, c.f)
     G = ExpertStack(S.routers, S.shared_blobs(), store, S.index, S.resident, d=c.d, f=c.f, k=c.k, wfmt=c.wfmt,
-                    act_mode=B.MOE_ACT_FLOAT, max_T=c.T, biases=S.biases, miss_mode="host")
+                    act_mode=B.MOE_ACT_FLOAT, max_T=c.T, biases=S.biases, miss_mode="host", by_slot=True)
     x = torch.from_numpy(synth.bf16_bits_to_f32(S.x)).cuda()
     print("[bench] %s: %d layers x %d experts, %d resident, %d-blob host pool, T=%d (ready in %.1fs)"
           % (a.workload, c.n_layers, c.E, len(S.resident), c.n_pool_blobs, c.T, time.time() - t0),

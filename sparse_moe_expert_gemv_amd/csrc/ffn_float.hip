@@ -821,7 +821,8 @@ static bool launch_down_tok16(const moe_ffn_args* a, const _Float16* h, int slot
 // the slots were not grouped and slot j's h row is t k + j.
 constexpr int kDcMaxSlots = 65;  // k <= 64 routed slots + the shared expert
 constexpr int kDcChunks = 8;     // h chunks staged per thread: nj f / 8 <= kDcChunks * 64 * NW
-template <int NKT, int NW>
+constexpr int kDcStrips = 1;     // 16-row strips per workgroup (2 measured slower: fewer workgroups)
+template <int NKT, int NW, int RS = kDcStrips>
 __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __restrict__ h, int T, int d, int f,
                                                             int k, int E, const void* const* __restrict__ expert_ptrs,
                                                             const uint8_t* __restrict__ shared_blob,
@@ -833,10 +834,10 @@ __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __re
     __shared__ const uint8_t* s_blob[kDcMaxSlots];  // nullptr: the slot is ignored
     __shared__ int32_t s_p[kDcMaxSlots];
     __shared__ float s_g[kDcMaxSlots];
-    __shared__ float part[NW][16];
+    __shared__ float part[NW][16 * RS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n_strips = d / 16;
-    const int t = blockIdx.x / n_strips, strip = blockIdx.x % n_strips;
+    const int n_groups = d / (16 * RS);  // RS consecutive 16-row strips per workgroup
+    const int t = blockIdx.x / n_groups, strip = (blockIdx.x % n_groups) * RS;
     const int nj = k + (shared_blob ? 1 : 0);
     const int HC = f / 8;
     for (int j = threadIdx.x; j < nj; j += 64 * NW) {
@@ -856,15 +857,16 @@ __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __re
     const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
     const size_t qoff = L.dn.qoff + (size_t)strip * NKT * 1024 + lane * 16;
     const size_t soff = L.dn.soff + (size_t)strip * NKT * 128 + (lane & 15) * 8;
-    uint4v q[NKT], qn[NKT];
-    uint2v sc[NKT], scn[NKT];
-    auto issue = [&](int j, uint4v (&qq)[NKT], uint2v (&ss)[NKT]) {
+    constexpr int NQ = RS * NKT;  // the RS strips' tiles are consecutive in the blob
+    uint4v q[NQ], qn[NQ];
+    uint2v sc[NQ], scn[NQ];
+    auto issue = [&](int j, uint4v (&qq)[NQ], uint2v (&ss)[NQ]) {
         const uint8_t* blob = s_blob[j];
         if (blob == nullptr) return;
         const uint4v* pq = reinterpret_cast<const uint4v*>(blob + qoff);
         const uint2v* ps = reinterpret_cast<const uint2v*>(blob + soff);
 #pragma unroll
-        for (int i = 0; i < NKT; ++i) {
+        for (int i = 0; i < NQ; ++i) {
             ss[i] = gload_nt(ps + i * 16);
             qq[i] = gload_nt(pq + i * 64);
         }
@@ -888,33 +890,41 @@ __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __re
     __syncthreads();
     uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
     asm volatile("" : "+s"(mlo), "+s"(mhi), "+v"(magic));
-    float tot = 0.f;
+    float tot[RS];
+#pragma unroll
+    for (int r = 0; r < RS; ++r) tot[r] = 0.f;
     for (int j = wave; j < nj; j += NW) {
         if (j + NW < nj) issue(j + NW, qn, scn);
         __builtin_amdgcn_sched_barrier(0);  // the next slot's tiles are in flight before these products
         if (s_blob[j] != nullptr) {
             const uint4* hr = hrow + j * HC + (lane >> 4);
-            float4v acc = {0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < NKT; ++i)
+            for (int r = 0; r < RS; ++r) {
+                float4v acc = {0, 0, 0, 0};
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const half8 B = dequant4_scaled(q[i][b], scale_pair(sc[i], b), mlo, mhi, magic);
-                    const half8 A = __builtin_bit_cast(half8, hr[(i * 4 + b) * 4]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
-                }
-            tot = fmaf(s_g[j], acc[0], tot);  // lane l < 16: output row strip * 16 + l
+                for (int i = 0; i < NKT; ++i)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int n = r * NKT + i;
+                        const half8 B = dequant4_scaled(q[n][b], scale_pair(sc[n], b), mlo, mhi, magic);
+                        const half8 A = __builtin_bit_cast(half8, hr[(i * 4 + b) * 4]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
+                    }
+                tot[r] = fmaf(s_g[j], acc[0], tot[r]);  // lane l < 16: output row (strip + r) * 16 + l
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < NKT; ++i) {
+        for (int i = 0; i < NQ; ++i) {
             q[i] = qn[i];
             sc[i] = scn[i];
         }
     }
-    if (lane < 16) part[wave][lane] = tot;
+    if (lane < 16)
+#pragma unroll
+        for (int r = 0; r < RS; ++r) part[wave][16 * r + lane] = tot[r];
     __syncthreads();
-    if (threadIdx.x < 16) {
+    if (threadIdx.x < 16 * RS) {
         const size_t o = (size_t)t * d + strip * 16 + threadIdx.x;
         float sum = residual ? residual[o] : 0.f;
 #pragma unroll
@@ -927,7 +937,8 @@ bool down_combine_ok(const moe_ffn_args* a) {
     const int nkt = a->f / 128;
     const int nj = a->k + (a->shared_blob ? 1 : 0);
     const int nw = a->T <= 2 ? kDcWavesFew : kDcWaves;
-    return a->act_mode == MOE_ACT_FLOAT && a->wfmt == MOE_WFMT_I4B32 && a->T <= kDownCombineMax && a->d % 16 == 0 &&
+    return a->act_mode == MOE_ACT_FLOAT && a->wfmt == MOE_WFMT_I4B32 && a->T <= kDownCombineMax &&
+           a->d % (16 * kDcStrips) == 0 &&
            (nkt == 2 || nkt == 4 || nkt == 6 || nkt == 8) && (long)nj * (a->f / 8) <= (long)kDcChunks * 64 * nw;
 }
 
@@ -935,7 +946,7 @@ int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t
                         const float* gates, const float* residual, float* out, hipStream_t s) {
     if (!down_combine_ok(a)) return MOE_ERR_UNSUPPORTED;
     const _Float16* h = reinterpret_cast<const _Float16*>(w.h);
-    const dim3 grid(a->T * (a->d / 16));
+    const dim3 grid(a->T * (a->d / (16 * kDcStrips)));
     const uint8_t* sb = (const uint8_t*)a->shared_blob;
     const size_t lds = (size_t)(a->k + (sb ? 1 : 0)) * a->f * sizeof(_Float16);
 #define MOE_DC(NKT, NW)                                                                                          \

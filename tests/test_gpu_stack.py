@@ -177,12 +177,12 @@ def test_full_stack_48_layers_sampled():
 DSMALL = dict(T=4, d=512, E=64, k=4, f=256, n_layers=4, n_resident=100, n_pool_blobs=40)
 
 
-def _decode_stack_gpu(S):
+def _decode_stack_gpu(S, by_slot=False):
     c = S.cfg
     store = build_host_store(S.pool, c.wfmt, c.d, c.f)
     return ExpertStack(S.routers, S.shared_blobs() if c.has_shared else None, store, S.index, S.resident,
                        d=c.d, f=c.f, k=c.k, wfmt=c.wfmt, act_mode=B.MOE_ACT_FLOAT, max_T=c.T, biases=S.biases,
-                       miss_mode="host")
+                       miss_mode="host", by_slot=by_slot)
 
 
 def _check_decode_layer(S, l, h_in, xn_in):
@@ -201,14 +201,15 @@ def _resident_mask(S):
     return m.reshape(c.n_layers, c.E)
 
 
-@pytest.mark.parametrize("T", [1, 4])
-def test_small_decode_stack_host_misses_teacher_forced(T):
-    """Every layer teacher-forced against the oracle (ids and permutation bit-exact,
-    outputs within the float tolerance); across the layers the routing selects
-    both resident experts and misses, so both kinds of table entry are read."""
+@pytest.mark.parametrize("T,by_slot", [(1, False), (4, False), (1, True), (4, True)])
+def test_small_decode_stack_host_misses_teacher_forced(T, by_slot):
+    """Every layer teacher-forced against the oracle (ids bit-exact, outputs
+    within the float tolerance), grouped or by slot; across the layers the
+    routing selects both resident experts and misses, so both kinds of table
+    entry are read."""
     S = synth.make_stack(name="decode_stack", overrides=DSMALL, T=T)
     c = S.cfg
-    G = _decode_stack_gpu(S)
+    G = _decode_stack_gpu(S, by_slot)
     x = _x0(S)
     ids_l = []
     hL, kept = G.forward(x, keep=range(c.n_layers), ids_out=ids_l)
@@ -227,6 +228,21 @@ def test_small_decode_stack_host_misses_teacher_forced(T):
         n_miss += int((~res[l][used]).sum())
     assert n_hit > 0 and n_miss > 0, (n_hit, n_miss)
     G.close()
+
+
+def test_small_decode_stack_by_slot_equals_grouped_bitexact():
+    """The 4-layer decode stack by slot (no grouping) gives every layer's output
+    bit for bit as the grouped path."""
+    S = synth.make_stack(name="decode_stack", overrides=DSMALL)
+    outs = []
+    for by_slot in (False, True):
+        G = _decode_stack_gpu(S, by_slot)
+        hL, kept = G.forward(_x0(S), keep=range(S.cfg.n_layers))
+        torch.cuda.synchronize()
+        outs.append([kept[l][0].cpu().numpy() for l in range(S.cfg.n_layers)] + [hL.cpu().numpy()])
+        G.close()
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
 
 
 def test_small_decode_stack_host_reads_match_device_copy_bitexact():
