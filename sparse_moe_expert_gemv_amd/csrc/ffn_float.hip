@@ -641,8 +641,9 @@ static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, h
                                 const int32_t* slot_ids = nullptr) {
     const int nkt = a->d / 128;
     const int items = slots * (a->f / 16);
-    // few items (a single token routes to k + 1 slots): four wavefronts per item
-    const bool four = items < 1024 && nkt % 4 == 0;
+    // few items (a single token routes to k + 1 slots): four wavefronts per
+    // item where an instance exists, else two
+    const bool four = items < 1024 && (nkt == 8 || nkt == 16 || nkt == 32);
     const dim3 grid(four ? items : (items + 3) / 4);
     const size_t lds = std::max<size_t>((size_t)a->T * a->d * sizeof(_Float16), 8 * 2 * 4 * 64 * sizeof(float));
 #define MOE_GU16(NT, S)                                                                                         \
@@ -971,8 +972,6 @@ int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t
 static bool gateup_tok16_by_slot_ok(const moe_ffn_args* a) {
     if (a->T > kTokMax || (size_t)a->T * a->d * 2 > 64 * 1024 || (a->d & (a->d - 1)) != 0) return false;
     const int nkt = a->d / 128;
-    const int items = (a->T * a->k + (a->shared_blob ? 1 : 0)) * (a->f / 16);
-    if (items < 1024 && nkt % 4 == 0) return nkt == 8 || nkt == 16 || nkt == 32;
     return nkt == 4 || nkt == 8 || nkt == 16 || nkt == 32;
 }
 
