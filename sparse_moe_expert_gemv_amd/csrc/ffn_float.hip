@@ -810,7 +810,9 @@ static bool launch_down_tok16(const moe_ffn_args* a, const _Float16* h, int slot
 // Workgroup = (token t, 16 output rows); its NW wavefronts split the token's
 // k routed slots and the shared expert (slot j goes to wavefront j % NW).
 // The slots' expert pointers, gates and h rows are staged once per workgroup
-// (h rows in LDS, chunk c of slot j at j * f / 8 + c).  A wavefront streams
+// (h rows in LDS, chunk c of slot j at j * f / 8 + c, the high-nibble
+// positions divided by 16 as for the decode gate/up, whose seeded raw-quant
+// products and fp32 block scale this kernel uses too).  A wavefront streams
 // the 16-row down strip of each of its slots (all f / 128 quant tiles at
 // once), issuing the next slot's tiles before the products of the current
 // one (a second slot ahead measured slower); the A operand repeats the slot's
@@ -886,11 +888,13 @@ __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __re
 #pragma unroll
     for (int u = 0; u < kDcChunks; ++u) {
         const int idx = (int)threadIdx.x + u * 64 * NW;
-        if (idx < nh) hrow[idx] = __builtin_bit_cast(uint4, v[u]);
+        if (idx < nh) hrow[idx] = __builtin_bit_cast(uint4, pre16(__builtin_bit_cast(half8, v[u])));
     }
     __syncthreads();
     uint32_t mlo = 0x000F000Fu, mhi = 0x00F000F0u, magic = 0x64006400u;
     asm volatile("" : "+s"(mlo), "+s"(mhi), "+v"(magic));
+    const half8 Bc = offset_seed_b();
+    const float4v zero4 = {0, 0, 0, 0};
     float tot[RS];
 #pragma unroll
     for (int r = 0; r < RS; ++r) tot[r] = 0.f;
@@ -901,17 +905,21 @@ __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __re
             const uint4* hr = hrow + j * HC + (lane >> 4);
 #pragma unroll
             for (int r = 0; r < RS; ++r) {
-                float4v acc = {0, 0, 0, 0};
+                float y = 0.f;
 #pragma unroll
                 for (int i = 0; i < NKT; ++i)
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
+                        // exact block sum h . (q - 8): raw quants seeded with A . Bc,
+                        // then the row's block scale in fp32 (row 0 of the tile only)
                         const int n = r * NKT + i;
-                        const half8 B = dequant4_scaled(q[n][b], scale_pair(sc[n], b), mlo, mhi, magic);
                         const half8 A = __builtin_bit_cast(half8, hr[(i * 4 + b) * 4]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc, 0, 0, 0);
+                        const float4v dc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bc, zero4, 0, 0, 0);
+                        const float4v dq =
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(A, raw4(q[n][b], mlo, mhi, magic), dc, 0, 0, 0);
+                        y = fmaf(dq[0], scale_f32(sc[n], b), y);
                     }
-                tot[r] = fmaf(s_g[j], acc[0], tot[r]);  // lane l < 16: output row (strip + r) * 16 + l
+                tot[r] = fmaf(s_g[j], y, tot[r]);  // lane l < 16: output row (strip + r) * 16 + l
             }
         }
         __builtin_amdgcn_sched_barrier(0);

@@ -336,8 +336,10 @@ def test_ffn_combine_entry_matches_separate_calls_and_oracle(T, f):
     """moe_expert_ffn_combine (T <= 8, int4: the down projection and the
     gate-weighted sum in one kernel; T = 9: moe_expert_ffn then moe_combine)
     against moe_expert_ffn with fp32 rows + moe_combine on the same routing,
-    with a residual, and against the oracle.  Both sides sum the same fp32
-    products, in different orders."""
+    with a residual, and against the oracle.  The fused kernel takes exact
+    block sums h . (q - 8) and applies the block scale in fp32; the separate
+    down kernel rounds each (q - 8) * s to fp16 first (relative 2^-11 per
+    weight), so the two agree to that rounding, not bit for bit."""
     L = synth.make_layer("decode_t4", T=T, overrides={"f": f})
     res = np.random.Generator(np.random.PCG64(21)).standard_normal((T, L.cfg.d)).astype(np.float32)
     G, out, st, o = run_layer(L, residual=res, y_dtype=torch.float32)
@@ -346,7 +348,7 @@ def test_ffn_combine_entry_matches_separate_calls_and_oracle(T, f):
     G.fuse_combine = False
     ref = host(G.forward(x_tensor(L), residual=torch.from_numpy(res).to(DEV)))
     torch.cuda.synchronize()
-    ok, rel, mx = R.within_tolerance(out, ref, rel=1e-5, maxabs_frac=1e-5)
+    ok, rel, mx = R.within_tolerance(out, ref, rel=2e-4, maxabs_frac=1e-3)
     assert ok, "fused vs separate: rel-L2 %.3e, max-abs/RMS %.3e" % (rel, mx)
 
 
