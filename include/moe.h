@@ -14,6 +14,9 @@
  *
  * Call sequence for one layer (all enqueued on the caller's stream):
  *   moe_route -> moe_permute -> [moe_quantize_act] -> moe_expert_ffn -> moe_combine
+ * or, fused: moe_route_permute -> [moe_quantize_act] -> moe_expert_ffn_combine;
+ * for decode batches (float mode, int4, T <= 8) with no grouping at all:
+ *   moe_route -> moe_expert_ffn_combine_slots
  *
  * Conventions
  *  - Every tensor argument is a DEVICE pointer owned by the caller unless the

@@ -3,8 +3,10 @@
 ``MoELayer`` holds a layer's device-resident weights (router, packed expert
 blobs, device pointer table, shared expert) plus reusable buffers, and runs
 
-    moe_route -> moe_permute -> [moe_quantize_act] -> moe_expert_ffn -> moe_combine
+    moe_route_permute -> [moe_quantize_act] -> moe_expert_ffn_combine
 
+(or, with ``fuse_combine=False``, moe_expert_ffn then moe_combine; with
+``by_slot=True`` and a decode batch, moe_route -> moe_expert_ffn_combine_slots)
 on the current stream.  Device memory comes from PyTorch; all computation is in
 libmoe.so.
 """
