@@ -179,9 +179,16 @@ def main():
                                        expert_ptrs=G.expert_ptrs, ws=G._ws_for(T), ids=G.ids[:T], gates=G.gates[:T],
                                        out=G.out[:T], x=x, shared_blob=G.shared, phase=phase)
 
+    def run_route_slots(G, x, phase=0):
+        # the whole decode layer: router logits, gate/up selecting its slots' experts, down + combine
+        B.moe_route_ffn_combine_slots(T=T, d=cfg.d, f=cfg.f, E=cfg.E, k=cfg.k, wfmt=cfg.wfmt, act_mode=mode,
+                                      expert_ptrs=G.expert_ptrs, ws=G._ws_for(T), Wr=G.Wr, bias=G.bias,
+                                      ids=G.ids[:T], gates=G.gates[:T], out=G.out[:T], x=x, shared_blob=G.shared,
+                                      phase=phase)
+
     def run_ffn(G, x, phase=0):
         if by_slot:
-            return run_slots(G, x, phase)
+            return run_route_slots(G, x, phase)
         n = T * cfg.k
         common = dict(T=T, d=cfg.d, f=cfg.f, E=cfg.E, k=cfg.k, wfmt=cfg.wfmt, act_mode=mode,
                       expert_ptrs=G.expert_ptrs, counts=G.counts, offsets=G.offsets, sorted_idx=G.sorted_idx[:n],
@@ -209,6 +216,8 @@ def main():
             B.moe_expert_ffn_combine(x=x, **common)
 
     def run_step(G, x):
+        if by_slot:
+            return run_route_slots(G, x)
         run_route(G, x)
         run_ffn_combine(G, x)
 
@@ -257,10 +266,15 @@ def main():
 
     step_r = lambda r: run_step(layers[r], xs[r])
     gu_r = lambda r: run_ffn(layers[r], xs[r], phase=1)
-    step_graphs = gu_graphs = None
+    # by slot, the step's gate/up also selects the experts; its expert-FFN work
+    # alone (the same kernel reading the ids) is timed as well
+    alone_r = lambda r: run_slots(layers[r], xs[r], phase=1)
+    step_graphs = gu_graphs = alone_graphs = None
     if use_graph:
         step_graphs = (capture(step_r, range(rotate)), [capture(step_r, [r]) for r in range(rotate)])
         gu_graphs = (capture(gu_r, range(rotate)), [capture(gu_r, [r]) for r in range(rotate)])
+        if by_slot:
+            alone_graphs = (capture(alone_r, range(rotate)), [capture(alone_r, [r]) for r in range(rotate)])
         torch.cuda.synchronize()
 
     # region A: whole steps
@@ -272,6 +286,10 @@ def main():
     # the stream, rotating over the weight copies, between two HIP events
     timed(lambda i: run_all(gu_r, gu_graphs, rotate), 1)
     gu_ms = timed(lambda i: run_all(gu_r, gu_graphs, steps), 1) / steps
+    alone_ms = None
+    if by_slot:
+        timed(lambda i: run_all(alone_r, alone_graphs, rotate), 1)
+        alone_ms = timed(lambda i: run_all(alone_r, alone_graphs, steps), 1) / steps
 
     # algorithmic work per gate/up launch, from each copy's routing (fixed input per copy):
     # the distinct experts picked (the by-slot launch reads an expert once per slot)
@@ -279,6 +297,9 @@ def main():
     per = [gateup_algorithmic(cfg, n, T) for n in n_act]
     alg_bytes = float(np.mean([p[0] for p in per]))
     alg_ops = float(np.mean([p[1] for p in per]))
+    ffn_bytes = alg_bytes
+    if by_slot:
+        alg_bytes += T * cfg.E * 8  # the fused launch also reads the token's fp64 router logits
     if mode == B.MOE_ACT_Q8:
         achieved = alg_ops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
@@ -290,13 +311,19 @@ def main():
     if mode == B.MOE_ACT_Q8:
         roof["kernel"] = "ffn_q8_tiled<0> (moe_expert_ffn phase 1)" if cfg.wfmt == 4 else "ffn_q8_gateup (moe_expert_ffn phase 1)"
     else:
-        roof["kernel"] = ("ffn_gateup_tok16 by slot (moe_expert_ffn_combine_slots phase 1)" if by_slot
+        roof["kernel"] = ("ffn_gateup_tok16 by slot, selecting its experts (moe_route_ffn_combine_slots phase 1)"
+                          if by_slot
                           else "ffn_gateup_tok16 (moe_expert_ffn phase 1)" if cfg.wfmt == 4 and T <= 16
                           else "ffn_gateup_tok64 (moe_expert_ffn phase 1)" if T <= 64
                           else "ffn_float_gateup (moe_expert_ffn phase 1)")
     roof["kernel_ms"] = round(gu_ms, 5)
     roof["algorithmic_bytes_per_launch"] = int(alg_bytes)
     roof["algorithmic_ops_per_launch"] = int(alg_ops)
+    if alone_ms is not None:
+        a_gbs = ffn_bytes / (alone_ms * 1e-3) / 1e9
+        roof["expert_ffn_alone"] = {"kernel": "ffn_gateup_tok16 by slot, ids given (moe_expert_ffn_combine_slots phase 1)",
+                                    "kernel_ms": round(alone_ms, 5), "achieved": round(a_gbs, 1),
+                                    "frac": round(a_gbs / HBM_PEAK_GBS, 4)}
 
     cpu = None
     if not a.no_cpu_baseline:

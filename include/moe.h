@@ -16,7 +16,7 @@
  *   moe_route -> moe_permute -> [moe_quantize_act] -> moe_expert_ffn -> moe_combine
  * or, fused: moe_route_permute -> [moe_quantize_act] -> moe_expert_ffn_combine;
  * for decode batches (float mode, int4, T <= 8) with no grouping at all:
- *   moe_route -> moe_expert_ffn_combine_slots
+ *   moe_route -> moe_expert_ffn_combine_slots, or moe_route_ffn_combine_slots
  *
  * Conventions
  *  - Every tensor argument is a DEVICE pointer owned by the caller unless the
@@ -267,6 +267,29 @@ int moe_expert_ffn_combine(const moe_ffn_args* args, const int32_t* ids, const i
  */
 int moe_expert_ffn_combine_slots(const moe_ffn_args* args, const int32_t* ids, const float* gates,
                                  const float* residual, float* out, moe_stream_t stream);
+
+/*
+ * A whole decode layer after the router weights, in three launches: router
+ * logits, then the by-slot gate/up whose first wavefront per workgroup selects
+ * the slot's expert itself (the router's top-k of that token, as moe_route),
+ * then the down projection and the weighted sum as in
+ * moe_expert_ffn_combine_slots.  ids, gates and out equal, bit for bit, those
+ * of moe_route + moe_expert_ffn_combine_slots (and of the grouped path); the
+ * separate selection launch and its kernel boundary are saved, at the price
+ * of the top-k latency inside the gate/up launch.
+ *   args: as for moe_expert_ffn_combine_slots (x is also the router input);
+ *         phase 0 = the whole call, 1 = the gate/up launch alone with the
+ *         router logits left in the workspace by an earlier phase-0 call of
+ *         the same shape (ids and gates are written, residual and out unused);
+ *   Wr [E, d] fp32, bias [E] fp32 or NULL (as moe_route);
+ *   ids [T, k], gates [T, k]: outputs; residual [T, d] fp32 or NULL;
+ *   out [T, d] fp32 (may alias residual).
+ * Supported: the shapes of moe_expert_ffn_combine_slots (E <= 1024);
+ * otherwise MOE_ERR_UNSUPPORTED before any launch.  Errors as for
+ * moe_expert_ffn_combine_slots, plus MOE_ERR_INVALID_ARG for a null Wr.
+ */
+int moe_route_ffn_combine_slots(const moe_ffn_args* args, const float* Wr, const float* bias, int32_t* ids,
+                                float* gates, const float* residual, float* out, moe_stream_t stream);
 
 /*
  * Combine: out[t] = residual[t] + y_shared[t] + sum_{j<k} gates[t,j] * y_perm[dest[t*k+j]],

@@ -216,6 +216,28 @@ int moe_expert_ffn_combine_slots(const moe_ffn_args* a, const int32_t* ids, cons
     return launch_ffn_combine_slots(a, w, ids, gates, residual, out, as_stream(s));
 }
 
+int moe_route_ffn_combine_slots(const moe_ffn_args* a, const float* Wr, const float* bias, int32_t* ids,
+                                float* gates, const float* residual, float* out, moe_stream_t s) {
+    if (!a || (a->phase != 0 && a->phase != 1)) return MOE_ERR_INVALID_ARG;
+    if (a->T < 0 || !shape_ok(a->d, a->E, a->k) || a->f <= 0 || a->f % 128 ||
+        (a->wfmt != MOE_WFMT_I4B32 && a->wfmt != MOE_WFMT_I8B32) ||
+        (a->act_mode != MOE_ACT_FLOAT && a->act_mode != MOE_ACT_Q8) ||
+        (a->x_dtype != MOE_DT_F32 && a->x_dtype != MOE_DT_BF16))
+        return MOE_ERR_INVALID_ARG;
+    if (a->T == 0) return MOE_OK;
+    if (!a->x || !a->expert_ptrs || !a->ws || !Wr || !ids || !gates || !out) return MOE_ERR_INVALID_ARG;
+    Workspace w;
+    workspace_layout(a->T, a->d, a->f, a->E, a->k, a->act_mode, (char*)a->ws, &w);
+    if (a->ws_bytes < w.bytes) return MOE_ERR_NO_MEMORY;
+    if (!ffn_combine_slots_ok(a)) return MOE_ERR_UNSUPPORTED;
+    if (a->phase == 0) {  // phase 1: the router logits are already in the workspace
+        const int rc = launch_route_logits(a->x, a->x_dtype, a->T, a->d, Wr, bias, a->E, w.logits, as_stream(s));
+        if (rc) return rc;
+    }
+    return launch_ffn_combine_slots_topk(a, w, logit_planes(a->T, a->d, a->E), ids, gates, residual, out,
+                                         as_stream(s));
+}
+
 int moe_combine(const void* y_perm, int y_dtype, const int32_t* dest, const float* gates, const float* y_shared,
                 const float* residual, int T, int k, int d, float* out, moe_stream_t s) {
     if (T < 0 || k < 1 || d <= 0 || d % 4 || (y_dtype != MOE_DT_F32 && y_dtype != MOE_DT_F16))

@@ -146,6 +146,11 @@ int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t
 bool ffn_combine_slots_ok(const moe_ffn_args* a);
 int launch_ffn_combine_slots(const moe_ffn_args* a, const Workspace& w, const int32_t* ids, const float* gates,
                              const float* residual, float* out, hipStream_t s);
+int launch_ffn_combine_slots_topk(const moe_ffn_args* a, const Workspace& w, int planes, int32_t* ids, float* gates,
+                                  const float* residual, float* out, hipStream_t s);
+// router logits alone (double, into `logits`, logit_planes(T, d, E) k planes)
+int launch_route_logits(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E,
+                        double* logits, hipStream_t s);
 int launch_ffn_float(const moe_ffn_args* a, const Workspace& w, hipStream_t s);
 int launch_ffn_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s);
 size_t q8_tile_capacity(int T, int k, int E);  // int2 entries of the q8 tile list

@@ -24,6 +24,7 @@
 // Items are derived from device-side counts and the active-expert list: no
 // host synchronisation.
 #include "common.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
@@ -468,7 +469,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 // go to LDS.
 // BY_SLOT: no grouping; work slot a < T k is the routed slot a itself (expert
 // slot_ids[a], its one row written to h row a), slot T k the shared expert.
-template <int NT, int S, typename XT, int NTH = 256, bool BY_SLOT = false>
+// TOPK > 0 (with BY_SLOT): the slot's expert is selected here instead, by the
+// router's top-k of token a / k over the logits (TOPK values per lane); the
+// first wavefront ranks the token's logits and also writes its ids and gates.
+template <int NT, int S, typename XT, int NTH = 256, bool BY_SLOT = false, int TOPK = 0>
 __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x, int T, int d, int f, int k, int E,
                                                         const void* const* __restrict__ expert_ptrs,
                                                         const uint8_t* __restrict__ shared_blob,
@@ -476,7 +480,9 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
                                                         const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ sorted_idx,
                                                         const int32_t* __restrict__ active, _Float16* __restrict__ h,
-                                                        const int32_t* __restrict__ slot_ids) {
+                                                        const int32_t* __restrict__ slot_ids,
+                                                        const double* __restrict__ logits, int planes,
+                                                        int32_t* __restrict__ ids_out, float* __restrict__ gates_out) {
     extern __shared__ __align__(16) uint4 xs4[];  // [T][d / 8] fp16, chunk c of row r at (c ^ r); later [4][2][4][64] f32
     const int XC = d / 8;           // a power of two (checked by the launcher)
     const int lxc = __builtin_ctz(XC);
@@ -495,7 +501,19 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
     if constexpr (BY_SLOT) {
         const int n_slots = T * k;
         const bool routed = a < n_slots;
-        const int e_raw = slot_ids[min(a, n_slots - 1)];
+        int e_raw;
+        if constexpr (TOPK > 0) {
+            __shared__ RankScratch rs;
+            __shared__ int32_t s_sel[64];
+            const int ts = min(a, n_slots - 1) / k;
+            if (wave == 0)
+                topk_rank<TOPK>(logits + (size_t)ts * E, E, k, ids_out + (size_t)ts * k, gates_out + (size_t)ts * k,
+                                s_sel, rs, planes, (size_t)T * E);
+            __syncthreads();
+            e_raw = s_sel[min(a, n_slots - 1) - ts * k];
+        } else {
+            e_raw = slot_ids[min(a, n_slots - 1)];
+        }
         const bool valid = (unsigned)e_raw < (unsigned)E;
         const uint8_t* pe = (const uint8_t*)expert_ptrs[valid ? e_raw : 0];
         blob = routed ? (valid ? pe : nullptr) : (a == n_slots ? shared_blob : nullptr);
@@ -636,9 +654,10 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
     }
 }
 
-template <typename XT, bool BY_SLOT = false>
+template <typename XT, bool BY_SLOT = false, int TOPK = 0>
 static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, hipStream_t s,
-                                const int32_t* slot_ids = nullptr) {
+                                const int32_t* slot_ids = nullptr, const double* logits = nullptr, int planes = 1,
+                                int32_t* ids_out = nullptr, float* gates_out = nullptr) {
     const int nkt = a->d / 128;
     const int items = slots * (a->f / 16);
     // few items (a single token routes to k + 1 slots): four wavefronts per
@@ -647,9 +666,9 @@ static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, h
     const dim3 grid(four ? items : (items + 3) / 4);
     const size_t lds = std::max<size_t>((size_t)a->T * a->d * sizeof(_Float16), 8 * 2 * 4 * 64 * sizeof(float));
 #define MOE_GU16(NT, S)                                                                                         \
-    ffn_gateup_tok16<NT, S, XT, S == 2 ? 512 : 256, BY_SLOT><<<grid, S == 2 ? 512 : 256, lds, s>>>(              \
+    ffn_gateup_tok16<NT, S, XT, S == 2 ? 512 : 256, BY_SLOT, TOPK><<<grid, S == 2 ? 512 : 256, lds, s>>>(        \
         (const XT*)a->x, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->counts, \
-        a->offsets, a->sorted_idx, a->active, h, slot_ids)
+        a->offsets, a->sorted_idx, a->active, h, slot_ids, logits, planes, ids_out, gates_out)
     if (four) {
         switch (nkt) {
         case 8: MOE_GU16(2, 4); return true;
@@ -992,6 +1011,29 @@ int launch_ffn_combine_slots(const moe_ffn_args* a, const Workspace& w, const in
     _Float16* h = reinterpret_cast<_Float16*>(w.h);
     const bool ok = a->x_dtype == MOE_DT_F32 ? launch_gateup_tok16<float, true>(a, h, slots, s, ids)
                                              : launch_gateup_tok16<uint16_t, true>(a, h, slots, s, ids);
+    if (!ok) return MOE_ERR_UNSUPPORTED;
+    const int rc = check_launch();
+    if (rc || a->phase == 1) return rc;
+    return launch_down_combine(a, w, ids, nullptr, gates, residual, out, s);
+}
+
+// routing + by-slot FFN + combine for decode batches: the router logits are
+// in the workspace (w.logits, `planes` k planes); the gate/up kernel selects
+// each slot's expert from them and writes ids and gates for the combine
+int launch_ffn_combine_slots_topk(const moe_ffn_args* a, const Workspace& w, int planes, int32_t* ids, float* gates,
+                                  const float* residual, float* out, hipStream_t s) {
+    if (!ffn_combine_slots_ok(a) || a->E > 1024) return MOE_ERR_UNSUPPORTED;
+    const int slots = a->T * a->k + (a->shared_blob ? 1 : 0);
+    _Float16* h = reinterpret_cast<_Float16*>(w.h);
+    bool ok;
+    if (a->E <= 512)
+        ok = a->x_dtype == MOE_DT_F32
+                 ? launch_gateup_tok16<float, true, 8>(a, h, slots, s, nullptr, w.logits, planes, ids, gates)
+                 : launch_gateup_tok16<uint16_t, true, 8>(a, h, slots, s, nullptr, w.logits, planes, ids, gates);
+    else
+        ok = a->x_dtype == MOE_DT_F32
+                 ? launch_gateup_tok16<float, true, 16>(a, h, slots, s, nullptr, w.logits, planes, ids, gates)
+                 : launch_gateup_tok16<uint16_t, true, 16>(a, h, slots, s, nullptr, w.logits, planes, ids, gates);
     if (!ok) return MOE_ERR_UNSUPPORTED;
     const int rc = check_launch();
     if (rc || a->phase == 1) return rc;

@@ -6,8 +6,9 @@ blobs, device pointer table, shared expert) plus reusable buffers, and runs
     moe_route_permute -> [moe_quantize_act] -> moe_expert_ffn_combine
 
 (or, with ``fuse_combine=False``, moe_expert_ffn then moe_combine; with
-``by_slot=True`` and a decode batch, moe_route -> moe_expert_ffn_combine_slots)
-on the current stream.  Device memory comes from PyTorch; all computation is in
+``by_slot=True`` and a decode batch, moe_route_ffn_combine_slots, or with
+``select_in_ffn=False`` moe_route -> moe_expert_ffn_combine_slots) on the
+current stream.  Device memory comes from PyTorch; all computation is in
 libmoe.so.
 """
 from __future__ import annotations
@@ -42,16 +43,19 @@ def pointer_table(packed: torch.Tensor) -> torch.Tensor:
 
 class MoELayer:
     def __init__(self, Wr, bias, experts, shared, *, d, f, k, wfmt, act_mode, max_T, device="cuda",
-                 y_dtype=None, experts_are_packed=False, expert_ptrs=None, fuse_combine=True, by_slot=False):
+                 y_dtype=None, experts_are_packed=False, expert_ptrs=None, fuse_combine=True, by_slot=False,
+                 select_in_ffn=True):
         self.device = torch.device(device)
         # forward through moe_expert_ffn_combine (down projection and weighted
         # sum in one kernel where one exists); False: moe_expert_ffn then
         # moe_combine, which leave y_perm / y_shared filled
         self.fuse_combine = fuse_combine
-        # decode batches (float mode, int4, T <= 8): moe_route then
-        # moe_expert_ffn_combine_slots, with no grouping of the slots (counts,
-        # offsets, sorted_idx, dest and active are then not written)
+        # decode batches (float mode, int4, T <= 8): no grouping of the slots
+        # (counts, offsets, sorted_idx, dest and active are then not written);
+        # the gate/up launch selects the experts itself (moe_route_ffn_combine_slots),
+        # or with select_in_ffn=False moe_route then moe_expert_ffn_combine_slots
         self.by_slot = by_slot
+        self.select_in_ffn = select_in_ffn
         self.d, self.f, self.k, self.wfmt, self.act_mode = d, f, k, wfmt, act_mode
         self.Wr = torch.as_tensor(np.ascontiguousarray(Wr, dtype=np.float32)).to(self.device)
         self.E = self.Wr.shape[0]
@@ -107,11 +111,14 @@ class MoELayer:
         n = T * k
         if self.by_slot and self.act_mode == B.MOE_ACT_FLOAT and self.wfmt == 4 and T <= 8:
             o = self.out[:T] if out is None else out
-            B.moe_route(x, self.Wr, self.bias, k, ids, gates, ws, stream)
-            B.moe_expert_ffn_combine_slots(T=T, d=self.d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
-                                           expert_ptrs=self.expert_ptrs if expert_ptrs is None else expert_ptrs,
-                                           ws=ws, ids=ids, gates=gates, out=o, x=x, residual=residual,
-                                           shared_blob=self.shared, stream=stream)
+            common = dict(T=T, d=self.d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
+                          expert_ptrs=self.expert_ptrs if expert_ptrs is None else expert_ptrs, ws=ws, ids=ids,
+                          gates=gates, out=o, x=x, residual=residual, shared_blob=self.shared, stream=stream)
+            if self.select_in_ffn:
+                B.moe_route_ffn_combine_slots(Wr=self.Wr, bias=self.bias, **common)
+            else:
+                B.moe_route(x, self.Wr, self.bias, k, ids, gates, ws, stream)
+                B.moe_expert_ffn_combine_slots(**common)
             return o
         B.moe_route_permute(x, self.Wr, self.bias, k, ids, gates, self.counts, self.offsets, self.sorted_idx[:n],
                             self.dest[:n], self.active, ws, stream)

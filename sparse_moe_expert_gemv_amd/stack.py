@@ -54,8 +54,8 @@ class ExpertStack:
         miss_mode    "stage": misses copied per layer into staging buffers;
                      "host": misses read in place from the pinned host store
         by_slot      decode batches (float mode, int4, T <= 8) without usage
-                     counters: moe_route + moe_expert_ffn_combine_slots, no
-                     grouping of the slots (same outputs, bit for bit)
+                     counters: moe_route_ffn_combine_slots, no grouping of the
+                     slots (same outputs, bit for bit)
         """
         self.by_slot = by_slot
         assert miss_mode in ("stage", "host")
@@ -142,11 +142,11 @@ class ExpertStack:
         B.moe_rmsnorm(h, xn, self.eps, stream)
         bias = None if self.bias is None else self.bias[l]
         if self.by_slot and self.usage is None and self.act_mode == B.MOE_ACT_FLOAT and self.wfmt == 4 and T <= 8:
-            B.moe_route(xn, self.Wr[l], bias, k, self.ids[:T], self.gates[:T], self.ws, stream)
-            B.moe_expert_ffn_combine_slots(T=T, d=self.d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
-                                           expert_ptrs=self.tables[l] if table is None else table, ws=self.ws,
-                                           ids=self.ids[:T], gates=self.gates[:T], out=out, x=xn, residual=h,
-                                           shared_blob=None if self.shared is None else self.shared[l], stream=stream)
+            B.moe_route_ffn_combine_slots(T=T, d=self.d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
+                                          expert_ptrs=self.tables[l] if table is None else table, ws=self.ws,
+                                          Wr=self.Wr[l], bias=bias, ids=self.ids[:T], gates=self.gates[:T], out=out,
+                                          x=xn, residual=h,
+                                          shared_blob=None if self.shared is None else self.shared[l], stream=stream)
             return
         B.moe_route_permute(xn, self.Wr[l], bias, k, self.ids[:T], self.gates[:T], self.counts, self.offsets,
                             self.sorted_idx[:n], self.dest[:n], self.active, self.ws, stream)

@@ -352,18 +352,23 @@ def test_ffn_combine_entry_matches_separate_calls_and_oracle(T, f):
     assert ok, "fused vs separate: rel-L2 %.3e, max-abs/RMS %.3e" % (rel, mx)
 
 
-@pytest.mark.parametrize("T,f", [(1, 768), (2, 768), (4, 768), (8, 768), (3, 512)])
-def test_ffn_combine_slots_equals_grouped_path_and_oracle(T, f):
-    """moe_route + moe_expert_ffn_combine_slots (no grouping: every routed
-    slot its own work item) gives the same ids, gates and layer output, bit
-    for bit, as moe_route_permute + moe_expert_ffn_combine, and meets the
-    float bar against the oracle."""
+@pytest.mark.parametrize("T,f,select_in_ffn", [(1, 768, True), (2, 768, True), (4, 768, True), (8, 768, True),
+                                                (3, 512, True), (4, 768, False), (1, 256, False), (8, 1024, True)])
+def test_ffn_combine_slots_equals_grouped_path_and_oracle(T, f, select_in_ffn):
+    """The by-slot decode paths (no grouping: every routed slot its own work
+    item), moe_route_ffn_combine_slots (the gate/up launch selects its experts)
+    and moe_route + moe_expert_ffn_combine_slots, give the same ids, gates and
+    layer output, bit for bit, as moe_route_permute + moe_expert_ffn_combine,
+    and meet the float bar against the oracle."""
     L = synth.make_layer("decode_t4", T=T, overrides={"f": f})
     c = L.cfg
     res = np.random.Generator(np.random.PCG64(23)).standard_normal((T, c.d)).astype(np.float32)
     G, out, st, o = run_layer(L, residual=res)
     G2 = gpu_layer(L)
     G2.by_slot = True
+    G2.select_in_ffn = select_in_ffn
+    G2.ids.fill_(-5)
+    G2.gates.fill_(-1.0)
     out2 = host(G2.forward(x_tensor(L), residual=torch.from_numpy(res).to(DEV)))
     torch.cuda.synchronize()
     assert np.array_equal(host(G2.ids[:T]), st["ids"])
@@ -392,6 +397,17 @@ def test_ffn_combine_slots_phase1_then_whole_call():
     B.moe_expert_ffn_combine_slots(**common)
     torch.cuda.synchronize()
     assert np.array_equal(host(G.out[:c.T]), ref)
+    # moe_route_ffn_combine_slots: phase 1 (gate/up alone, logits left in the
+    # workspace by the whole call) selects the same ids and gates again
+    ids0, gates0 = host(G.ids[:c.T]).copy(), host(G.gates[:c.T]).copy()
+    G.ids.fill_(-3)
+    G.gates.fill_(0.0)
+    G.out.zero_()
+    B.moe_route_ffn_combine_slots(phase=1, Wr=G.Wr, bias=G.bias, **common)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(G.ids[:c.T]), ids0)
+    assert np.array_equal(host(G.gates[:c.T]).view(np.uint32), gates0.view(np.uint32))
+    assert not np.any(host(G.out[:c.T]))
 
 
 def test_ffn_combine_entry_skips_ids_outside_range():

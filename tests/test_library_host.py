@@ -117,6 +117,17 @@ def test_invalid_arguments_rejected_before_any_hip_call():
         setattr(a, field, old)
     a.T = 0
     assert L.moe_expert_ffn_combine_slots(C.byref(a), None, None, None, None, None) == B.MOE_OK
+    # routing + by-slot FFN + combine: null router weights or outputs, then the shapes
+    a.T = 4
+    assert L.moe_route_ffn_combine_slots(C.byref(a), None, None, dummy, dummy, None, dummy, None) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_route_ffn_combine_slots(C.byref(a), dummy, None, None, dummy, None, dummy, None) == \
+        B.MOE_ERR_INVALID_ARG
+    a.T = 9
+    assert L.moe_route_ffn_combine_slots(C.byref(a), dummy, None, dummy, dummy, None, dummy, None) == \
+        B.MOE_ERR_UNSUPPORTED
+    a.T = 0
+    assert L.moe_route_ffn_combine_slots(C.byref(a), None, None, None, None, None, None, None) == B.MOE_OK
 
 
 def test_workspace_too_small_is_reported():
