@@ -377,6 +377,26 @@ def test_ffn_combine_slots_equals_grouped_path_and_oracle(T, f, select_in_ffn):
     check_float(out2, o["out"], "by-slot decode layer, T=%d f=%d" % (T, f))
 
 
+@pytest.mark.parametrize("select_in_ffn", [True, False])
+def test_ffn_combine_slots_many_experts_large_k(select_in_ffn):
+    """By slot with E = 1024 and k = 32 (two tokens): the selection inside the
+    gate/up launch takes its 16-values-per-lane instance and the top-k path
+    for k > 16; ids, gates and output bit for bit as the grouped path."""
+    L = synth.make_layer("decode_t4", T=2, overrides={"E": 1024, "k": 32})
+    c = L.cfg
+    G, out, st, o = run_layer(L)
+    check_routing(st, o, c.E)
+    G2 = gpu_layer(L)
+    G2.by_slot = True
+    G2.select_in_ffn = select_in_ffn
+    out2 = host(G2.forward(x_tensor(L)))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(G2.ids[:c.T]), st["ids"])
+    assert np.array_equal(host(G2.gates[:c.T]).view(np.uint32), st["gates"].view(np.uint32))
+    assert np.array_equal(out2, out)
+    check_float(out2, o["out"], "by-slot decode layer, E=1024 k=32")
+
+
 def test_ffn_combine_slots_phase1_then_whole_call():
     """Phase 1 of the by-slot entry (gate/up alone) followed by the whole call
     on the same workspace gives the whole call's output (the phase leaves the
