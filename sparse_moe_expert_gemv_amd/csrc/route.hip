@@ -61,31 +61,37 @@ __device__ __forceinline__ int wave_prefix_incl(int v) {
     return v;
 }
 
-// The four wavefronts each own a contiguous range of the slots (a multiple of
-// 64): per-range expert histograms, one scan of the totals over the experts,
-// per-range base positions, then every wavefront places its own slots in
-// ascending order (ballot ranking within 64-slot chunks), so the grouping is
-// stable and the four ranges are placed concurrently.
+// The NWR wavefronts of the workgroup each own a contiguous range of the slots
+// (a multiple of 64): per-range expert histograms, one scan of the totals over
+// the experts, per-range base positions, then every wavefront places its own
+// slots in ascending order (ballot ranking within 64-slot chunks), so the
+// grouping is stable and the ranges are placed concurrently.
+template <int NWR>
 __device__ void block_permute(const int32_t* s_ids, int n, int E, int32_t* counts, int32_t* offsets,
                               int32_t* sorted_idx, int32_t* dest, int32_t* active, int32_t (*s_wc)[1024],
                               int32_t* s_part, int32_t* s_flag) {
+    constexpr int NTH = 64 * NWR, EPT = 1024 / NTH;  // threads; experts per thread in the scan
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rng = ((n + 255) / 256) * 64;  // slots per wavefront range
+    const int rng = ((n + NTH - 1) / NTH) * 64;  // slots per wavefront range
     const int f_lo = min(n, wave * rng), f_hi = min(n, f_lo + rng);
-    for (int i = tid; i < 4 * 1024; i += 256) (&s_wc[0][0])[i] = 0;
+    for (int i = tid; i < NWR * 1024; i += NTH) (&s_wc[0][0])[i] = 0;
     __syncthreads();
     for (int f = f_lo + lane; f < f_hi; f += 64) {
         const int id = s_ids[f];
         if ((unsigned)id < (unsigned)E) atomicAdd(&s_wc[wave][id], 1);
     }
     __syncthreads();
-    // totals of 4 experts per thread, exclusive scan over the experts (wavefront
-    // scans, then the totals of the preceding wavefronts)
-    int c4[4], p = 0, fl = 0;
+    // totals of EPT experts per thread, exclusive scan over the experts
+    // (wavefront scans, then the totals of the preceding wavefronts)
+    int c4[EPT], p = 0, fl = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = tid * 4 + i;
-        c4[i] = e < E ? s_wc[0][e] + s_wc[1][e] + s_wc[2][e] + s_wc[3][e] : 0;
+    for (int i = 0; i < EPT; ++i) {
+        const int e = tid * EPT + i;
+        int c = 0;
+        if (e < E)
+#pragma unroll
+            for (int w = 0; w < NWR; ++w) c += s_wc[w][e];
+        c4[i] = c;
         p += c4[i];
         fl += c4[i] > 0;
     }
@@ -101,8 +107,8 @@ __device__ void block_permute(const int32_t* s_ids, int n, int E, int32_t* count
         frun += s_flag[w];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = tid * 4 + i;
+    for (int i = 0; i < EPT; ++i) {
+        const int e = tid * EPT + i;
         if (e < E) {
             counts[e] = c4[i];
             offsets[e] = run;
@@ -110,7 +116,7 @@ __device__ void block_permute(const int32_t* s_ids, int n, int E, int32_t* count
             // base position of expert e in each range: the slots of e in earlier ranges come first
             int b = run;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < NWR; ++w) {
                 const int cw = s_wc[w][e];
                 s_wc[w][e] = b;
                 b += cw;
@@ -118,7 +124,7 @@ __device__ void block_permute(const int32_t* s_ids, int n, int E, int32_t* count
             run += c4[i];
         }
     }
-    if (tid == 255) {
+    if (tid == NTH - 1) {
         offsets[E] = run;
         active[0] = frun;
     }
@@ -297,22 +303,25 @@ __device__ void permute_rank64(const int32_t* s_ids, int n, int E, int32_t* coun
 // Permutation of up to kBlockPermMax slots by one workgroup (ids staged in
 // LDS, then the block-level grouping above): one launch instead of three.
 constexpr int kBlockPermMax = 4096;
-__global__ __launch_bounds__(256) void perm_block(const int32_t* __restrict__ ids, int n, int E,
-                                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ sorted_idx, int32_t* __restrict__ dest,
-                                                  int32_t* __restrict__ active) {
+constexpr int kPermBlockWaves = 8;  // wavefront ranges of perm_block (the in-selection grouping uses 4)
+__global__ __launch_bounds__(64 * kPermBlockWaves) void perm_block(const int32_t* __restrict__ ids, int n, int E,
+                                                                   int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ sorted_idx,
+                                                                   int32_t* __restrict__ dest,
+                                                                   int32_t* __restrict__ active) {
     __shared__ int32_t s_ids[kBlockPermMax];
-    __shared__ int32_t s_wc[4][1024];
-    __shared__ int32_t s_part[4], s_flag[4];
-    for (int i = threadIdx.x; i < n; i += 256) s_ids[i] = ids[i];
+    __shared__ int32_t s_wc[kPermBlockWaves][1024];
+    __shared__ int32_t s_part[kPermBlockWaves], s_flag[kPermBlockWaves];
+    for (int i = threadIdx.x; i < n; i += 64 * kPermBlockWaves) s_ids[i] = ids[i];
     __syncthreads();
-    block_permute(s_ids, n, E, counts, offsets, sorted_idx, dest, active, s_wc, s_part, s_flag);
+    block_permute<kPermBlockWaves>(s_ids, n, E, counts, offsets, sorted_idx, dest, active, s_wc, s_part, s_flag);
 }
 
 int launch_permute_block(const int32_t* ids, int n, int E, int32_t* counts, int32_t* offsets, int32_t* sorted_idx,
                          int32_t* dest, int32_t* active, hipStream_t s) {
     if (n > kBlockPermMax) return MOE_ERR_UNSUPPORTED;
-    perm_block<<<1, 256, 0, s>>>(ids, n, E, counts, offsets, sorted_idx, dest, active);
+    perm_block<<<1, 64 * kPermBlockWaves, 0, s>>>(ids, n, E, counts, offsets, sorted_idx, dest, active);
     return check_launch();
 }
 
@@ -341,7 +350,7 @@ __global__ __launch_bounds__(256) void route_select_small(const double* __restri
         if (T * k <= 64)
             permute_rank64(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_keys, s_sorted);
         else
-            block_permute(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_wc, s_part, s_flag);
+            block_permute<4>(s_ids, T * k, E, counts, offsets, sorted_idx, dest, active, s_wc, s_part, s_flag);
     }
 }
 
