@@ -42,6 +42,16 @@ MUTANTS = [
     ("binary16 subnormal exponent", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
     ("down matrix transposed", "X->wd[(size_t)o * f + n]", "X->wd[(size_t)(n % d) * f + (o % f)]"),
     ("clamp at 128 (equivalent)", "if (r > 127.0f) r = 127.0f;", "if (r > 128.0f) r = 128.0f;"),
+    # the int8-activation second half: requantised h and the int8 down projection
+    ("h block scales 0.2% high", "quant8_row(hf, f, hq, hs);",
+     "quant8_row(hf, f, hq, hs); for (int b_ = 0; b_ < f / 32; ++b_) hs[b_] *= 1.002f;"),
+    ("g and u rounded to fp32 before SwiGLU", "hf[n] = (float)(silu(g[n]) * u[n]);",
+     "hf[n] = (float)(silu((double)(float)g[n]) * (double)(float)u[n]);"),
+    ("int8 down scaled by the x block scales", "y[o] = q8_dot(hq, hs,", "y[o] = q8_dot(hq, xs,"),
+    ("int8 block sum drops its last element", "for (int i = 0; i < 32; ++i) blk +=",
+     "for (int i = 0; i < 31; ++i) blk +="),
+    ("h code off by one at the top", "q[b * 32 + i] = (int8_t)v;",
+     "q[b * 32 + i] = (int8_t)(v == 127 ? 126 : v);"),
 ]
 
 

@@ -4,7 +4,14 @@ Nothing here is shared with the oracle or the HIP library:
   * exact router logits by integer arithmetic on the dyadic fp32 inputs;
   * a numpy decoder of the canonical expert blob;
   * a dense, masked float64 brute force of the whole layer (every expert is
-    evaluated for every token and masked by the exact top-k).
+    evaluated for every token and masked by the exact top-k);
+  * the int8-activation ("Q8") expert in numpy: its own per-32 quantiser
+    (fp32 amax / 127, ties-to-even, clamp +-127), exact int64 block sums
+    scaled by both block scales in float64, h rounded to fp32 and requantised
+    the same way before the int8 down projection.  The pages' prefill step
+    multiplies int8 activations by the quantised weights without
+    dequantising them ("Strata benchmarks", bottleneck analysis (1), the
+    MMQ int8 tensor-core row of the prefill optimisation table).
 """
 from __future__ import annotations
 
@@ -53,8 +60,10 @@ def logits_to_float(zrow: list) -> np.ndarray:
     return np.array([float(Fraction(v, 1 << (2 * _SHIFT))) for v in zrow], dtype=np.float64)
 
 
-def decode_blob(blob: np.ndarray, wfmt: int, d: int, f: int):
-    """numpy decoder of the canonical blob -> (Wg [f,d], Wu [f,d], Wd [d,f]) float64."""
+def blob_parts(blob: np.ndarray, wfmt: int, d: int, f: int):
+    """numpy decoder of the canonical blob -> signed quants (int64) and block
+    scales (float64) of the three matrices: ((qg, sg), (qu, su), (qd, sd)),
+    qg/qu [f,d], qd [d,f], scales [rows, K/32]."""
     n = d * f
     qb = n // 2 if wfmt == 4 else n
     sb = (n // 32) * 2
@@ -73,10 +82,13 @@ def decode_blob(blob: np.ndarray, wfmt: int, d: int, f: int):
     def scales(off, R, K):
         return blob[off:off + sb].view(np.float16).astype(np.float64).reshape(R, K // 32)
 
-    def mat(qoff, soff, R, K):
-        return quants(qoff, R, K) * np.repeat(scales(soff, R, K), 32, axis=1)
+    return ((quants(0, f, d), scales(3 * qb, f, d)), (quants(qb, f, d), scales(3 * qb + sb, f, d)),
+            (quants(2 * qb, d, f), scales(3 * qb + 2 * sb, d, f)))
 
-    return (mat(0, 3 * qb, f, d), mat(qb, 3 * qb + sb, f, d), mat(2 * qb, 3 * qb + 2 * sb, d, f))
+
+def decode_blob(blob: np.ndarray, wfmt: int, d: int, f: int):
+    """numpy decoder of the canonical blob -> (Wg [f,d], Wu [f,d], Wd [d,f]) float64."""
+    return tuple(q * np.repeat(s, 32, axis=1) for q, s in blob_parts(blob, wfmt, d, f))
 
 
 def silu(z):
@@ -111,6 +123,67 @@ def brute_force_layer(x, Wr, bias, experts, shared, wfmt, d, f, k, residual=None
         out += mask[:, e:e + 1] * dense_ffn(x, decode_blob(experts[e], wfmt, d, f))
     if shared is not None:
         out += dense_ffn(x, decode_blob(shared, wfmt, d, f))
+    return np.array(ids, dtype=np.int32), out
+
+
+def quant8_blocks(a: np.ndarray):
+    """Per-32 int8 quantisation of the rows of a float32 matrix [R, K]:
+    s = amax / 127 as an IEEE float32 quotient, q = rint(a / s) in float32
+    (ties to even) clamped to +-127, and s = 0, q = 0 for an all-zero block.
+    Returns (q int64 [R, K], s float32 [R, K/32])."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    R, K = a.shape
+    blk = a.reshape(R, K // 32, 32)
+    s = (np.abs(blk).max(axis=2) / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint(blk / s[:, :, None])
+    q = np.where(s[:, :, None] == 0, 0.0, np.clip(r, -127.0, 127.0)).astype(np.int64)
+    return q.reshape(R, K), s
+
+
+def block_scaled_products(qa, sa, qw, sw) -> np.ndarray:
+    """out[m, n] = sum over 32-blocks b of sa[m, b] * sw[n, b] * (exact integer
+    sum over the block of qa[m, .] * qw[n, .]); float64, [M, N]."""
+    M, K = qa.shape
+    N = qw.shape[0]
+    nb = K // 32
+    blk = np.einsum("mbi,nbi->mnb", qa.reshape(M, nb, 32), qw.reshape(N, nb, 32))  # int64, exact
+    terms = np.asarray(sa, np.float64)[:, None, :] * np.asarray(sw, np.float64)[None, :, :] * blk
+    return terms.sum(axis=2)
+
+
+def q8_ffn(X: np.ndarray, blob: np.ndarray, wfmt: int, d: int, f: int):
+    """One expert in int8-activation mode on the rows of X [M, d] (fp32).
+    Returns (y [M, d], g [M, f], u [M, f]) in float64."""
+    (qg, sg), (qu, su), (qd, sd) = blob_parts(blob, wfmt, d, f)
+    xq, xs = quant8_blocks(X)
+    g = block_scaled_products(xq, xs, qg, sg)
+    u = block_scaled_products(xq, xs, qu, su)
+    h = (silu(g) * u).astype(np.float32)
+    hq, hs = quant8_blocks(h)
+    return block_scaled_products(hq, hs, qd, sd), g, u
+
+
+def brute_force_layer_q8(x, Wr, bias, experts, shared, wfmt, d, f, k, residual=None):
+    """The dense masked brute force of the layer with int8-activation experts."""
+    x = np.asarray(x, dtype=np.float32)
+    T = x.shape[0]
+    E = Wr.shape[0]
+    z = exact_logits(x, Wr, bias)
+    mask = np.zeros((T, E))
+    ids = []
+    for t in range(T):
+        top = exact_topk(z[t], k)
+        ids.append(top)
+        zf = logits_to_float([z[t][e] for e in top])
+        p = np.exp(zf - zf[0])
+        mask[t, top] = (p / p.sum()).astype(np.float32).astype(np.float64)
+    out = np.zeros((T, d)) if residual is None else residual.astype(np.float64).copy()
+    for e in range(E):
+        if mask[:, e].any():
+            out += mask[:, e:e + 1] * q8_ffn(x, experts[e], wfmt, d, f)[0]
+    if shared is not None:
+        out += q8_ffn(x, shared, wfmt, d, f)[0]
     return np.array(ids, dtype=np.int32), out
 
 

@@ -277,6 +277,59 @@ def test_ffn_q8_error_bound_vs_float():
     assert 1e-4 < r < 3e-2
 
 
+@pytest.mark.parametrize("wfmt", [synth.WFMT_I4B32, synth.WFMT_I8B32])
+def test_ffn_q8_matches_independent_int8_brute_force(wfmt):
+    """Int8-activation expert vs the numpy brute force of tests/refmath.py
+    (its own quantiser of x and of h, exact int64 block sums times both block
+    scales, h rounded to fp32 before requantisation): gate, up and output
+    agree to 1e-12 relative.  Catches an error in the h block scale or codes,
+    g/u rounded to fp32 before SwiGLU, a wrong scale or block in the int8 down
+    projection, and a dropped block element."""
+    d, f = 256, 128
+    rng = np.random.Generator(np.random.PCG64(11))
+    x = rng.standard_normal((24, d)).astype(np.float32)
+    x[3] = 0.0                      # an all-zero row: every scale 0, output exactly 0
+    x[5, 64:96] = 0.0               # one all-zero block inside a row
+    for e in range(3):
+        blob = synth.gen_expert_blob(np.random.Generator(np.random.PCG64(100 + e)), d, f, wfmt)
+        y, g, u = oracle.expert_ffn(x, blob, wfmt, f, oracle.ACT_Q8, return_gu=True)
+        yr, gr, ur = R.q8_ffn(x, blob, wfmt, d, f)
+        for got, ref in ((g, gr), (u, ur), (y, yr)):
+            assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+        assert np.all(y[3] == 0.0)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_layer_q8_matches_dense_masked_brute_force(shared):
+    """Whole tiny layer in int8-activation mode vs the dense masked brute
+    force with the int8 expert of tests/refmath.py (ids exact, output to the
+    fp32 rounding of the stored result)."""
+    L = synth.make_layer("tiny", overrides={"has_shared": shared})
+    x = L.x_f32()
+    res = np.random.Generator(np.random.PCG64(9)).standard_normal(x.shape).astype(np.float32) if shared else None
+    o = oracle.moe_layer(x, L.Wr, L.bias, L.experts, L.shared, L.cfg.wfmt, L.cfg.f, L.cfg.k,
+                         act_mode=oracle.ACT_Q8, residual=res)
+    ids, ref = R.brute_force_layer_q8(x, L.Wr, L.bias, L.experts, L.shared, L.cfg.wfmt, L.cfg.d, L.cfg.f,
+                                      L.cfg.k, residual=res)
+    assert np.array_equal(o["ids"], ids)
+    assert np.max(np.abs(o["out"] - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+def test_int8_brute_force_quantiser_pins():
+    """The brute force's own quantiser against hand values (so the two int8
+    implementations cannot share a mistake): scale 1 for a block whose amax
+    is 127, ties to even, zero block, clamp never exceeded."""
+    x = np.zeros((1, 64), np.float32)
+    x[0, :8] = [127.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -0.5]
+    q, s = R.quant8_blocks(x)
+    assert s[0, 0] == np.float32(1.0) and s[0, 1] == 0.0
+    assert list(q[0, :8]) == [127, 2, 4, -2, -4, 0, 2, 0] and np.all(q[0, 32:] == 0)
+    # block sums times scales: one block of ones against a row of twos, scales 0.5 and 0.25
+    qa = np.ones((1, 32), np.int64)
+    qw = np.full((1, 32), 2, np.int64)
+    assert R.block_scaled_products(qa, np.array([[0.5]]), qw, np.array([[0.25]]))[0, 0] == 0.5 * 0.25 * 64
+
+
 # ------------------------------------------------------------------ layer ----
 
 @pytest.mark.parametrize("shared", [False, True])
