@@ -44,7 +44,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA, TOPS
 WORKLOADS = ("decode_t4", "decode_t1", "prefill", "skew", "tiny", "stack", "decode_stack", "decode_stack_t1",
-             "decode_stack_drift", "copy")
+             "decode_stack_drift", "copy", "peak")
 
 
 def parse():
@@ -126,6 +126,8 @@ def main():
         return bench_decode_stack(a)
     if name == "copy":
         return bench_copy(a)
+    if name == "peak":
+        return bench_peak(a)
     big = name == "prefill"
     steps = a.steps if a.steps is not None else (20 if big else 200)
     warmup = a.warmup if a.warmup is not None else (3 if big else 20)
@@ -616,6 +618,84 @@ def bench_copy(a):
     print(json.dumps({"workload": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
                       "ms_per_copy": round(dt * 1e3, 3), "GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}),
           flush=True)
+
+
+def bench_peak(a):
+    """Measured ceilings (calibration kernels of libmoe_probe.so): the issue
+    rate of each matrix-core instruction the FFN kernels use, the plain fp32
+    FMA rate of the vector unit, the rate of one int8 32x32x32 MFMA per block
+    followed by the exact two-operation block-scale epilogue (and by a
+    one-operation one), and a non-temporal HBM read stream over 4 GiB.
+    Workgroups of 256 threads; ``waves/SIMD`` = grid / 256 (one wavefront of
+    each workgroup per SIMD).  Best rate over the grid sizes tried."""
+    import ctypes
+    import torch
+    from sparse_moe_expert_gemv_amd import build as _b
+    if not os.path.exists(_b.PROBE_LIB):
+        raise RuntimeError("libmoe_probe.so is not built (python -m sparse_moe_expert_gemv_amd.build)")
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.moe_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    out = torch.empty(n_cu * 16 * 256, dtype=torch.float32, device="cuda")
+
+    def run(kind, grid, iters, inp=None, nbytes=0, reps=5):
+        def launch():
+            rc = lib.moe_probe_run(kind, grid, iters, 1, out.data_ptr(), inp, nbytes, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError("moe_probe_run(kind=%d) returned %d" % (kind, rc))
+        launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    res = {}
+    # (kind, name, ops per instruction per wavefront, instructions per iteration, unit)
+    mfma = [(0, "mfma_i8_32x32x32", 32 * 32 * 32 * 2, 4, "TOPS"), (1, "mfma_i8_16x16x64", 16 * 16 * 64 * 2, 4, "TOPS"),
+            (2, "mfma_f16_32x32x16", 32 * 32 * 16 * 2, 4, "TFLOPS"),
+            (3, "mfma_f16_16x16x32", 16 * 16 * 32 * 2, 4, "TFLOPS"),
+            (5, "i8_32x32x32_plus_two_fp32_fma_per_output", 32 * 32 * 32 * 2, 2, "TOPS (int8 MFMA ops)"),
+            (7, "i8_32x32x32_plus_one_fp32_fma_per_output", 32 * 32 * 32 * 2, 2, "TOPS (int8 MFMA ops)")]
+    for kind, nm, ops, per_it, unit in mfma:
+        best = None
+        for w in (1, 2, 4):
+            grid, iters = n_cu * w, 4000 // w
+            t = run(kind, grid, iters)
+            rate = grid * 4 * iters * per_it * ops / t / 1e12
+            if best is None or rate > best[0]:
+                best = (rate, w, t)
+        res[nm] = {"rate": round(best[0], 1), "unit": unit, "waves_per_simd": best[1], "ms": round(best[2] * 1e3, 3)}
+    best = None
+    for w in (1, 2, 4):
+        grid, iters = n_cu * w, 40000 // w
+        t = run(4, grid, iters)
+        rate = grid * 256 * iters * 16 * 2 / t / 1e12
+        if best is None or rate > best[0]:
+            best = (rate, w, t)
+    res["valu_fma_f32"] = {"rate": round(best[0], 1), "unit": "TFLOPS (v_fma_f32, not packed)",
+                           "waves_per_simd": best[1], "ms": round(best[2] * 1e3, 3)}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    best = None
+    for w in (2, 4, 8, 16):
+        grid = n_cu * w
+        t = run(6, grid, 0, buf.data_ptr(), nbytes, reps=3)
+        gbs = nbytes / t / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, w, t)
+    res["hbm_stream_read"] = {"rate": round(best[0], 1), "unit": "GB/s", "workgroups_per_cu": best[1],
+                              "bytes": nbytes, "ms": round(best[2] * 1e3, 3)}
+    del buf
+    print(json.dumps({"workload": "peak", "compute_units": n_cu, "datasheet": {
+        "int8_mfma_TOPS": INT8_PEAK_TOPS, "f16_mfma_TFLOPS": 2500.0, "fp32_vector_TFLOPS": 157.3,
+        "hbm_GBps": HBM_PEAK_GBS}, "measured": res}), flush=True)
 
 
 def time_it(fn, reps=1):

@@ -1,4 +1,6 @@
-"""Build the gfx950 C-ABI library libmoe.so in-tree with hipcc.
+"""Build the gfx950 C-ABI library libmoe.so in-tree with hipcc, and the
+calibration kernels (libmoe_probe.so, measured instruction rates and HBM read
+stream; not part of the layer library).
 
     python -m sparse_moe_expert_gemv_amd.build        # or build() from Python
 """
@@ -15,6 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PROBE_SRC = os.path.join(PKG, "probe", "peak.hip")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -61,7 +65,21 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *CFLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBE_SRC, " ".join(cmd), r.stderr))
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print("built", PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
