@@ -311,7 +311,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name)}
     if mode == B.MOE_ACT_Q8:
-        roof["kernel"] = "ffn_q8_tiled<0> (moe_expert_ffn phase 1)" if cfg.wfmt == 4 else "ffn_q8_gateup (moe_expert_ffn phase 1)"
+        roof["kernel"] = "ffn_i4_gateup (moe_expert_ffn phase 1)" if cfg.wfmt == 4 else "ffn_q8_gateup (moe_expert_ffn phase 1)"
     else:
         roof["kernel"] = ("ffn_gateup_tok16 by slot, selecting its experts (moe_route_ffn_combine_slots phase 1)"
                           if by_slot
@@ -663,23 +663,26 @@ def bench_peak(a):
             (5, "i8_32x32x32_plus_two_fp32_fma_per_output", 32 * 32 * 32 * 2, 2, "TOPS (int8 MFMA ops)"),
             (7, "i8_32x32x32_plus_one_fp32_fma_per_output", 32 * 32 * 32 * 2, 2, "TOPS (int8 MFMA ops)")]
     for kind, nm, ops, per_it, unit in mfma:
-        best = None
-        for w in (1, 2, 4):
+        best, by_w = None, {}
+        for w in (1, 2, 3, 4):
             grid, iters = n_cu * w, 4000 // w
             t = run(kind, grid, iters)
             rate = grid * 4 * iters * per_it * ops / t / 1e12
+            by_w[w] = round(rate, 1)
             if best is None or rate > best[0]:
                 best = (rate, w, t)
-        res[nm] = {"rate": round(best[0], 1), "unit": unit, "waves_per_simd": best[1], "ms": round(best[2] * 1e3, 3)}
-    best = None
-    for w in (1, 2, 4):
+        res[nm] = {"rate": round(best[0], 1), "unit": unit, "waves_per_simd": best[1], "ms": round(best[2] * 1e3, 3),
+                   "rate_by_waves_per_simd": by_w}
+    best, by_w = None, {}
+    for w in (1, 2, 3, 4):
         grid, iters = n_cu * w, 40000 // w
         t = run(4, grid, iters)
         rate = grid * 256 * iters * 16 * 2 / t / 1e12
+        by_w[w] = round(rate, 1)
         if best is None or rate > best[0]:
             best = (rate, w, t)
     res["valu_fma_f32"] = {"rate": round(best[0], 1), "unit": "TFLOPS (v_fma_f32, not packed)",
-                           "waves_per_simd": best[1], "ms": round(best[2] * 1e3, 3)}
+                           "waves_per_simd": best[1], "ms": round(best[2] * 1e3, 3), "rate_by_waves_per_simd": by_w}
     nbytes = 4 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(3)

@@ -208,10 +208,15 @@ typedef struct moe_ffn_args {
  * in fp32 to each exact block sum by the int4 gate/up kernel for T <= 16 and
  * by the general kernels (T > 64); the other small-batch kernels fold it into
  * the weights, rounding each (q - 8) * s to fp16 once (relative error at most
- * 2^-11 per weight).  MOE_ACT_Q8: int8 x int8 matrix cores with exact
- * per-block integer sums, both block scales applied in fp32; the SwiGLU
- * intermediate is requantised to int8 per 32 features before the down
- * projection.
+ * 2^-11 per weight).  MOE_ACT_Q8 (the pages' int8 prefill step, "Strata
+ * benchmarks", prefill optimisation table): gate/up on int8 x int8 matrix
+ * cores with exact per-block integer sums, both block scales applied in fp32;
+ * the SwiGLU intermediate is requantised to int8 per 32 features.  The down
+ * projection with int8 weights is exact in the same way; with int4 weights it
+ * multiplies fp16 operands holding the dequantised values (h codes times their
+ * scale, weights times theirs, each rounded once to fp16) with fp32
+ * accumulation, which adds about 3.5e-4 relative error to the expert output
+ * and no quantisation decision.
  * Errors: MOE_ERR_INVALID_ARG (null pointers, shapes not multiples of the
  * quantisation block, a workspace smaller than moe_workspace_size);
  * MOE_ERR_UNSUPPORTED for float-mode shapes no kernel covers: more than 64

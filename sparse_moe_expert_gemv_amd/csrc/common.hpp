@@ -92,6 +92,12 @@ __device__ __forceinline__ V gload_nt(const V* p) {
 }
 constexpr int kBufNT = 2;  // cache-policy operand of a buffer load: non-temporal
 
+// Buffer resource over [base, base + bytes): loads through it are bounds
+// checked and return zeros outside the range (bytes = 0: nothing is read).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // ---- error plumbing -----------------------------------------------------------
@@ -107,7 +113,7 @@ struct Workspace {
     double* logits;     // [P, T, E] (P k planes)         route
     int32_t* hist;      // [ceil(T*k / kPermChunk), E]    permute
     int32_t* tiles;     // q8 tile list (int2) + count    ffn
-    void* h;            // SwiGLU intermediate [T*k + T, f]: fp16 (float mode) or int8 (q8)
+    void* h;            // SwiGLU intermediate [T*k + T, f]: fp16 (float mode, q8 with int4 weights) or int8 (q8, int8 weights)
     float* hs;          // q8: [T*k + T, f/32] block scales of h
     size_t route_bytes, permute_bytes, bytes;
 };

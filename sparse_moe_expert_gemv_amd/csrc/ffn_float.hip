@@ -455,11 +455,6 @@ template <> struct XChunk<_Float16> {
     __device__ __forceinline__ half8 cvt_pre16() const { return pre16(cvt()); }
 };
 
-// Buffer resource over [base, base + bytes): loads through it are bounds
-// checked and return zeros outside the range (bytes = 0: nothing is read).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // Order of the start: token chunks requested first; slot metadata in two
 // dependent rounds (the list entry is read before the list length is known,

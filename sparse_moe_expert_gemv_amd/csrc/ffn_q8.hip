@@ -1,29 +1,35 @@
 // Grouped SwiGLU expert FFN, int8-activation mode (prefill chunks).
 //
 // Per expert, the tokens routed to it form a dense M x K tile (about 160 rows
-// for an 8,192-token chunk over 512 experts with top-10), so both projections
-// run on int8 matrix cores: v_mfma_i32_32x32x32_i8, one instruction per
-// 32-wide quantisation block (A = 32 tokens x 32 k, B = 32 k x 32 weight
-// rows).  The Strata pages report moving expert matmuls to an int8
-// tensor-core kernel that needs no dequantisation ("Strata benchmarks",
-// prefill optimisation table); here the int4 weights become int8 while they
-// are staged in LDS, once per workgroup and k-chunk.
+// for an 8,192-token chunk over 512 experts with top-10).  The Strata pages
+// report moving expert matmuls to an int8 tensor-core kernel that needs no
+// dequantisation ("Strata benchmarks", prefill optimisation table).
 //
-// Block sums are exact integers |P| < 2^22 (the tiled int4 kernels stage the
-// quants as 16 q and the scales as s / 16; 16 |P| <= 16 * 32 * 127 * 8 is
-// still below 2^22).  The MFMA accumulator is seeded
-// with the bit pattern of 1.5 * 2^23, so the int32 result read as fp32 is
-// exactly 1.5 * 2^23 + P.  With the weight row's block scale sw constant per
-// lane, t = fma(D, sw, -1.5 * 2^23 * sw) = sw * P (one rounding; the constant
-// is exact), then acc += sx * t with the token's block scale: two VALU
-// operations per output and block.
+// Gate/up runs on int8 matrix cores: v_mfma_i32_32x32x32_i8, one instruction
+// per 32-wide quantisation block (A = 32 tokens x 32 k, B = 32 k x 32 weight
+// rows); the int4 weights become int8 while they are staged in LDS.  Block
+// sums are exact integers |P| < 2^22 (the int4 kernel stages the quants as
+// 16 q and the scales as s / 16; 16 |P| <= 16 * 32 * 127 * 8 is still below
+// 2^22).  The MFMA accumulator is seeded with the bit pattern of 1.5 * 2^23,
+// so the int32 result read as fp32 is exactly 1.5 * 2^23 + P.  With the
+// weight row's block scale sw constant per lane, t = fma(D, sw,
+// -1.5 * 2^23 * sw) = sw * P (one rounding; the constant is exact), then
+// acc += sx * t with the token's block scale: two VALU operations per output
+// and block.  h = silu(g) * u is then requantised to int8 per 32 features
+// (scale amax / 127), as the method defines; exact block sums keep those
+// codes equal to the definition's except at rounding ties.
 //
-// gate/up: a workgroup owns 64 features of f (gate rows + up rows = 128
-// weight rows) for up to 128 tokens of one expert (one 32-token m-tile per
-// wavefront), and writes h = silu(g) * u requantised to int8 per 32 features
-// (per-token scale amax/127, ties-to-even), the down projection's A operand.
-// down: a workgroup owns 128 output rows for the same token tile.
+// The int8 down projection's result feeds no further quantisation.  With int4
+// weights it runs on v_mfma_f32_32x32x16_f16 over fp16 operands holding the
+// dequantised values (the requantised h codes times their scale, the int4
+// weights times theirs, each rounded once to fp16), with no per-block
+// epilogue: on this chip the two-sided block-scale epilogue, not the matrix
+// core, bounds an exact int8 product.  With int8 weights both projections use
+// the exact int8 form (kernels ffn_q8_gateup / ffn_q8_down below).
+#include <type_traits>
+
 #include "common.hpp"
+#include "wave.hpp"
 
 namespace moe {
 
@@ -329,36 +335,38 @@ __global__ __launch_bounds__(256) void ffn_q8_down(const int8_t* __restrict__ hq
     }
 }
 
-// ---- int4 weights: token tiles of up to 192 rows staged in LDS ---------------
-// A work item is (tile, 128 weight rows): gate/up takes 64 features of f (their
-// 64 gate rows and 64 up rows), down takes 128 output rows.  Every k-chunk of
-// 128 (one packed int4 tile per strip, four 32-blocks) stages the tile's int8
-// activation rows, the 128 weight rows (int4 -> int8) and both sets of block
-// scales in LDS; wavefront w multiplies m-tiles 3 (w / 2) .. +2 (32 tokens
-// each) by n-tiles (w & 1) and 2 + (w & 1) (gate and up rows of the same 32
-// features, or two halves of the output rows), so SwiGLU needs no exchange.
-// Work items of one tile share blockIdx % 8, i.e. one XCD and its L2, which
-// then serves the tile's activation rows to all of them.  The next chunk is
-// read into registers while the current one is multiplied.  The per-block
-// arithmetic (magic-seeded int32 MFMA, t = sw * P, acc += sa * t, blocks in
-// order) is the same as above, so the results are identical.
-constexpr int kTM = 6;     // m-tiles of 32 tokens per tile (192 rows)
-constexpr int kTKC = 128;  // k per chunk
+// ---- int4 weights: token tiles of up to 192 rows, 512-thread workgroups ------
+// A work item is (tile, weight group): gate/up takes 128 features of f (their
+// 128 gate rows and 128 up rows), down takes 256 output rows.  Eight
+// wavefronts; wavefront w multiplies token tiles 3 (w / 4) .. +2 (32 tokens
+// each) by the weight tiles of feature group w % 4, so the two wavefronts a
+// SIMD holds (w and w + 4) cover all token tiles of one feature group and the
+// SIMDs stay balanced whatever the tile's row count.  Per k-chunk the token
+// rows, the weight rows and both sets of block scales are staged in LDS,
+// double buffered: chunk c + 1 is read into registers while chunk c is
+// multiplied, written to the other buffer afterwards, and one barrier per
+// chunk separates the two.  Loads go through buffer resources with per-lane
+// offsets computed once per work item.  The work items of one tile share
+// blockIdx % 8, i.e. one XCD, whose L2 then serves the tile's token rows to
+// all of them.
+constexpr int kTM = 6;           // token tiles of 32 per tile (192 rows)
+constexpr int kTR = kTM * 32;
+constexpr int kPThreads = 512;
+constexpr int kGUFeat = 128;     // features of f per gate/up work item (256 weight rows)
+constexpr int kDNRows = 256;     // output rows per down work item
 
-struct TileSmem {
-    uint4 a[kTM * 32][kTKC / 16];   // int8 rows, 16-byte chunk c of row r at (c ^ (r & 7))
-    uint4 w[128][kTKC / 16];        // int8 weight rows, same swizzle
-    float sa[kTKC / 32][kTM * 32];  // activation block scales
-    float sw[kTKC / 32][128];       // weight block scales
-};
+// 16-byte chunk c (0..7) of LDS row r is stored at position c ^ ((r >> 1) & 7):
+// the sixteen rows read by one quarter-wavefront then hit sixteen distinct
+// 16-byte bank groups of the 256 B the LDS serves per cycle.
+__device__ __forceinline__ int chunk_swz(int r) { return (r >> 1) & 7; }
 
-// Tiles of <= kTM * 32 rows, balanced per expert: (slot, m0, rows, 0) with
-// slot = position in the active list, or n_active for the shared expert.
+// Tiles of <= kTR rows, balanced per expert: (slot, m0, rows, 0) with slot =
+// position in the active list, or n_active for the shared expert.
 __global__ __launch_bounds__(1024) void q8_tile_plan(const int32_t* __restrict__ counts,
                                                      const int32_t* __restrict__ active, int T, int has_shared,
                                                      int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
     __shared__ int32_t sc[1024];
-    constexpr int cap = kTM * 32;
+    constexpr int cap = kTR;
     const int a = threadIdx.x;
     const int n_active = active[0];
     const int c = a < n_active ? counts[active[1 + a]] : 0;
@@ -400,25 +408,103 @@ __device__ __forceinline__ void int4_word_to_i8x16(uint32_t v, uint32_t& w0, uin
     w1 = __builtin_amdgcn_perm(hi, lo, 0x07050301u);              // k4 k5 k6 k7
 }
 
-// MODE 0: gate/up, A = x (int8 per 32-block), output h requantised; MODE 1: down, A = h, output y
-template <int MODE, typename YT>
-__global__ __launch_bounds__(256) void ffn_q8_tiled(const int8_t* __restrict__ aq, const float* __restrict__ as_,
-                                                    int T, int d, int f, int k,
-                                                    const void* const* __restrict__ expert_ptrs,
-                                                    const uint8_t* __restrict__ shared_blob,
-                                                    const int32_t* __restrict__ offsets,
-                                                    const int32_t* __restrict__ sorted_idx,
-                                                    const int32_t* __restrict__ active,
-                                                    const int4* __restrict__ tiles,
-                                                    const int32_t* __restrict__ n_tiles_p, int8_t* __restrict__ hq,
-                                                    float* __restrict__ hs, YT* __restrict__ y_perm,
-                                                    float* __restrict__ y_shared) {
-    __shared__ TileSmem S;
-    __shared__ int32_t s_row[kTM * 32];  // source row of each tile row (token for gate/up, h row for down)
+// One packed int4 word -> four fp16 pairs (k0 k1) (k2 k3) (k4 k5) (k6 k7) of
+// q * s: (w >> 4 j) & 0x000F000F puts the nibbles of k 2j and 2j + 1 in the
+// two halves, 0x6400 makes each the fp16 1024 + u, subtracting 1032 gives q
+// exactly, and the product with the fp16 block scale rounds once.
+__device__ __forceinline__ void int4_word_to_f16(uint32_t v, half2v s2, uint32_t (&out)[4]) {
+    const half2v off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t b = ((v >> (4 * jj)) & 0x000F000Fu) | 0x64006400u;
+        const half2v q = __builtin_bit_cast(half2v, b) + off;
+        out[jj] = __builtin_bit_cast(uint32_t, q * s2);
+    }
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits16 & 0xFFFFu));
+}
+
+struct GUStage {
+    uint4 w[2 * kGUFeat][8];  // int8 16 q weight rows (gate 0..127, up 128..255), 128 k
+    uint4 a[kTR][8];          // int8 token rows, 128 k
+    float sw[4][2 * kGUFeat]; // weight block scales / 16
+};
+typedef float GUScales[4][kTR];  // token block scales of a stage
+
+// One k-chunk (four 32-wide blocks) of a gate/up wavefront: NM token tiles
+// (from mt0) times its gate and up weight tiles.  Within a block the token
+// operand and scales of tile m + 1 are requested before the MFMAs and the
+// epilogue of tile m; the block loop itself is not unrolled (that would not
+// fit in the registers).
+template <int NM>
+__device__ __forceinline__ void gu_chunk(const GUStage& G, const GUScales& SA, int lane, int rg, int ru, int mt0,
+                                         const int16v& cmagic, float16v (&acc)[3][2]) {
+#pragma unroll 1
+    for (int b = 0; b < 4; ++b) {
+        const int kq = 2 * b + (lane >> 5);  // 16-byte chunk holding this lane's 16 k of block b
+        int4v A[2];
+        float sa[2][16];
+        auto fetch = [&](int m) {
+            const int row = (mt0 + m) * 32 + (lane & 31);
+            A[m & 1] = __builtin_bit_cast(int4v, G.a[row][kq ^ chunk_swz(row)]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = *reinterpret_cast<const float4*>(&SA[b][(mt0 + m) * 32 + 8 * q + 4 * (lane >> 5)]);
+                sa[m & 1][4 * q + 0] = v.x; sa[m & 1][4 * q + 1] = v.y;
+                sa[m & 1][4 * q + 2] = v.z; sa[m & 1][4 * q + 3] = v.w;
+            }
+        };
+        const int4v Bg = __builtin_bit_cast(int4v, G.w[rg][kq ^ chunk_swz(rg)]);
+        const int4v Bu = __builtin_bit_cast(int4v, G.w[ru][kq ^ chunk_swz(ru)]);
+        const float swg = G.sw[b][rg], swu = G.sw[b][ru];
+        const float ncg = -kMagic * swg, ncu = -kMagic * swu;
+        fetch(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const int16v Dg = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[m & 1], Bg, cmagic, 0, 0, 0);
+            const int16v Du = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[m & 1], Bu, cmagic, 0, 0, 0);
+            if (m + 1 < NM) fetch(m + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float tg = fmaf(__int_as_float(Dg[r]), swg, ncg);
+                const float tu = fmaf(__int_as_float(Du[r]), swu, ncu);
+                acc[m][0][r] = fmaf(tg, sa[m & 1][r], acc[m][0][r]);
+                acc[m][1][r] = fmaf(tu, sa[m & 1][r], acc[m][1][r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+struct GURegs {
+    uint4v w[2];   // packed int4 weights of two (strip, lane) units
+    uint32_t ws;   // two fp16 weight block scales
+};
+
+// Gate/up, int8 activations x int4 weights on v_mfma_i32_32x32x32_i8, one
+// instruction per 32-wide quantisation block.  The accumulator is seeded with
+// the bits of 1.5 * 2^23, so the int32 result read as fp32 is exactly
+// 1.5 * 2^23 + P for the block sum P (16 |P| < 2^22); t = fma(D, sw,
+// -1.5 * 2^23 * sw) = sw * P with one rounding (the constant is exact: sw has
+// an 11-bit significand), then acc = fma(t, sx, acc).  Then h = silu(g) * u is
+// requantised per (token, 32 features) to int8 codes q with scale s = amax /
+// 127, and the down projection's operand fp16(q * s) is written.
+__global__ __launch_bounds__(kPThreads, 1) void ffn_i4_gateup(
+    const int8_t* __restrict__ xq, const float* __restrict__ sx, int T, int d, int f, int k,
+    const void* const* __restrict__ expert_ptrs, const uint8_t* __restrict__ shared_blob,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_idx, const int32_t* __restrict__ active,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, _Float16* __restrict__ h_out) {
+    // two LDS stages as separate variables: the compiler then knows that the
+    // loads filling one do not alias the reads of the other
+    __shared__ GUStage S0, S1;
+    __shared__ GUScales SA0, SA1;
+    __shared__ int32_t s_row[kTR];  // token of each tile row
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int K = MODE == 0 ? d : f;
-    const int n_groups = MODE == 0 ? f / 64 : d / 128;
+    const int n_groups = f / kGUFeat;
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int ti = (j / n_groups) * 8 + xcd, grp = j % n_groups;
     if (ti >= n_tiles_p[0]) return;
@@ -431,166 +517,336 @@ __global__ __launch_bounds__(256) void ffn_q8_tiled(const int8_t* __restrict__ a
     const int p0 = routed ? offsets[e] : T * k;
     const int m0 = tl.y, mc = tl.z;
     const int nmt = (mc + 31) >> 5;
-    for (int i = threadIdx.x; i < kTM * 32; i += 256) {
+    for (int i = threadIdx.x; i < kTR; i += kPThreads) {
         const int m = min(i, mc - 1);  // rows past the tile repeat its last row (results discarded)
-        if (MODE == 0) s_row[i] = routed ? sorted_idx[p0 + m0 + m] / k : m0 + m;
-        else s_row[i] = p0 + m0 + m;
+        s_row[i] = routed ? sorted_idx[p0 + m0 + m] / k : m0 + m;
     }
     const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
-    const int nkt = K / 128;
-    const int nb = K / 32;
+    const int nkt = d / 128;
+    const int nb = d / 32;
+    const __amdgpu_buffer_rsrc_t wr = buf_rsrc(blob, (uint32_t)L.total);
+    const __amdgpu_buffer_rsrc_t xr = buf_rsrc(xq, (uint32_t)((size_t)T * d));
+    const __amdgpu_buffer_rsrc_t sr = buf_rsrc(sx, (uint32_t)((size_t)T * nb * 4));
     __syncthreads();
-    // staging registers: activations 6 x 16 B, weights 2 lane words, weight scales 8 B, activation scales 16 B
-    uint4v ra[6];
-    uint4v rw[2];
-    uint2v rsw = {0u, 0u};
-    float4v rsa = {0.f, 0.f, 0.f, 0.f};
-    auto load_chunk = [&](int c) {
+    // per-lane load offsets (the chunk's offset is the wave-uniform soffset)
+    uint32_t wq_off[2], xa_off[3];
 #pragma unroll
-        for (int q = 0; q < 6; ++q) {
-            const int idx = threadIdx.x + q * 256, row = idx >> 3, ch = idx & 7;
-            ra[q] = gload(reinterpret_cast<const uint4v*>(aq + (size_t)s_row[row] * K + c * kTKC) + ch);
-        }
+    for (int q = 0; q < 2; ++q) {
+        const int idx = threadIdx.x + q * kPThreads, st = idx >> 6, ll = idx & 63;
+        const MatLayout& M = st < 8 ? L.g : L.u;
+        wq_off[q] = (uint32_t)(M.qoff + (size_t)(grp * 8 + (st & 7)) * nkt * 1024 + ll * 16);
+    }
+    uint32_t ws_off;
+    {
+        const int st = threadIdx.x >> 5;
+        const MatLayout& M = st < 8 ? L.g : L.u;
+        ws_off = (uint32_t)(M.soff + (size_t)(grp * 8 + (st & 7)) * nkt * 128 + (threadIdx.x & 31) * 4);
+    }
+    // token rows and their block scales go from global memory straight to LDS:
+    // instruction q of wavefront w fills rows 8 (3 w + q) .. +7 (lane l: row
+    // + l / 8, position l % 8, which holds chunk (l % 8) ^ swizzle of the row),
+    // and wavefronts 0..5 fill the 768 block scales of the chunk ([4][192],
+    // 64 per instruction)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int idx = threadIdx.x + q * 256, st = idx >> 6, ll = idx & 63;
-            const MatLayout& M = MODE == 0 ? (st < 4 ? L.g : L.u) : L.dn;
-            const int strip = MODE == 0 ? grp * 4 + (st & 3) : grp * 8 + st;
-            rw[q] = gload_nt(reinterpret_cast<const uint4v*>(blob + M.qoff + ((size_t)strip * nkt + c) * 1024) + ll);
+    for (int q = 0; q < 3; ++q) {
+        const int row = 8 * (3 * wave + q) + (lane >> 3);
+        xa_off[q] = (uint32_t)s_row[row] * (uint32_t)d + (uint32_t)(((lane & 7) ^ chunk_swz(row)) * 16);
+    }
+    uint32_t sa_off[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int idx = min(wave * 128 + q * 64 + lane, 4 * kTR - 1), bb = idx / kTR, row = idx % kTR;
+        sa_off[q] = (uint32_t)s_row[row] * (uint32_t)nb * 4 + bb * 4;
+    }
+    auto dma_chunk = [&](GUStage& G, GUScales& SA, int c) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)&G.a[8 * (3 * wave + q)][0],
+                                                     16, xa_off[q], c * 128, 0, 0);
+        if (wave < 6) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    sr, (__attribute__((address_space(3))) void*)(&SA[0][0] + wave * 128 + q * 64), 4, sa_off[q],
+                    c * 16, 0, 0);
         }
-        if (threadIdx.x < 128) {
-            const int st = threadIdx.x >> 4, rr = threadIdx.x & 15;
-            const MatLayout& M = MODE == 0 ? (st < 4 ? L.g : L.u) : L.dn;
-            const int strip = MODE == 0 ? grp * 4 + (st & 3) : grp * 8 + st;
-            rsw = gload_nt(reinterpret_cast<const uint2v*>(blob + M.soff + ((size_t)strip * nkt + c) * 128 + rr * 8));
-        }
-        if (threadIdx.x < kTM * 32)
-            rsa = gload(reinterpret_cast<const float4v*>(as_ + (size_t)s_row[threadIdx.x] * nb + c * 4));
     };
-    auto store_chunk = [&]() {
+    auto load_chunk = [&](GURegs& R, int c) {
 #pragma unroll
-        for (int q = 0; q < 6; ++q) {
-            const int idx = threadIdx.x + q * 256, row = idx >> 3, ch = idx & 7;
-            S.a[row][ch ^ (row & 7)] = __builtin_bit_cast(uint4, ra[q]);
-        }
+        for (int q = 0; q < 2; ++q)
+            R.w[q] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wr, wq_off[q], c * 1024, kBufNT));
+        R.ws = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wr, ws_off, c * 128, kBufNT);
+    };
+    auto store_chunk = [&](GUStage& G, const GURegs& R) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int idx = threadIdx.x + q * 256, st = idx >> 6, ll = idx & 63;
-            const int row = st * 16 + (ll & 15), kq = ll >> 4;  // bytes 8 kq .. 8 kq + 7 of each block
+            const int idx = threadIdx.x + q * kPThreads, st = idx >> 6, ll = idx & 63;
+            const int row = st * 16 + (ll & 15), jq = ll >> 4;  // bytes 8 jq .. 8 jq + 7 of each block
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 uint32_t w0, w1;
-                int4_word_to_i8x16(rw[q][b], w0, w1);
-                const int ch = 2 * b + (kq >> 1);
-                uint2* dst = reinterpret_cast<uint2*>(&S.w[row][ch ^ (row & 7)]) + (kq & 1);
-                *dst = make_uint2(w0, w1);
+                int4_word_to_i8x16(R.w[q][b], w0, w1);
+                const int ch = 2 * b + (jq >> 1);
+                reinterpret_cast<uint2*>(&G.w[row][ch ^ chunk_swz(row)])[jq & 1] = make_uint2(w0, w1);
             }
         }
-        if (threadIdx.x < 128) {
-            // fp16 scales by integer extraction (a bit cast of a vector element to a half pair is avoided),
-            // divided by 16 for the staged quants 16 q
-            const int row = threadIdx.x;
-            const uint32_t w01 = rsw[0], w23 = rsw[1];
-            S.sw[0][row] = 0.0625f * (float)__builtin_bit_cast(_Float16, (unsigned short)(w01 & 0xFFFFu));
-            S.sw[1][row] = 0.0625f * (float)__builtin_bit_cast(_Float16, (unsigned short)(w01 >> 16));
-            S.sw[2][row] = 0.0625f * (float)__builtin_bit_cast(_Float16, (unsigned short)(w23 & 0xFFFFu));
-            S.sw[3][row] = 0.0625f * (float)__builtin_bit_cast(_Float16, (unsigned short)(w23 >> 16));
-        }
-        if (threadIdx.x < kTM * 32) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) S.sa[b][threadIdx.x] = rsa[b];
+        {
+            const int st = threadIdx.x >> 5, wd = threadIdx.x & 31;
+            const int row = st * 16 + (wd >> 1), b0 = 2 * (wd & 1);
+            G.sw[b0][row] = 0.0625f * f16_bits_to_float(R.ws);
+            G.sw[b0 + 1][row] = 0.0625f * f16_bits_to_float(R.ws >> 16);
         }
     };
-    const int mt0 = 3 * (wave >> 1);
-    const int nt0 = MODE == 0 ? (wave & 1) : 2 * (wave & 1);
-    const int nt1 = MODE == 0 ? 2 + (wave & 1) : 2 * (wave & 1) + 1;
-    // the magic accumulator seed is made opaque so that it stays in registers
-    // instead of being rebuilt before every MFMA
-    int16v cmagic = {(int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
-                     (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
-                     (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits,
-                     (int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits};
-    asm volatile("" : "+v"(cmagic));
-    float16v acc[3][2];
+
+    const int fg = wave & 3, mt0 = 3 * (wave >> 2);
+    const int rg = fg * 32 + (lane & 31), ru = kGUFeat + fg * 32 + (lane & 31);  // this lane's gate / up weight row
+    const int nkc = d / 128;
+    // The wavefront's loop is instantiated for its number of token tiles (as in
+    // the down kernel); every instance stages its share and meets the barriers.
+    auto run = [&](auto nm_c) {
+        constexpr int NM = decltype(nm_c)::value;
+        // the magic accumulator seed is made opaque so that it stays in
+        // registers instead of being rebuilt before every MFMA
+        int16v cmagic;
 #pragma unroll
-    for (int m = 0; m < 3; ++m)
+        for (int r = 0; r < 16; ++r) cmagic[r] = (int)kMagicBits;
+        asm volatile("" : "+v"(cmagic));
+        float16v acc[3][2];
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
-    const int nkc = K / kTKC;
-    load_chunk(0);
-    for (int c = 0; c < nkc; ++c) {
-        if (c > 0) __syncthreads();  // the previous chunk is no longer read
-        store_chunk();
-        __syncthreads();
-        if (c + 1 < nkc) load_chunk(c + 1);  // the next chunk is in flight during the products
-        __builtin_amdgcn_sched_barrier(0);
+            for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int kq = 2 * b + (lane >> 5);  // 16-byte chunk holding this lane's 16 k of block b
-            int4v B[2];
-            float sw[2], nc[2];
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int row = (n == 0 ? nt0 : nt1) * 32 + (lane & 31);
-                B[n] = __builtin_bit_cast(int4v, S.w[row][kq ^ (row & 7)]);
-                sw[n] = S.sw[b][row];
-                nc[n] = -kMagic * sw[n];
+                for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+        GURegs R;
+        load_chunk(R, 0);
+        dma_chunk(S0, SA0, 0);
+        store_chunk(S0, R);
+        __syncthreads();  // also waits for this wavefront's LDS-bound loads
+        // chunk c in S0 (even) or S1 (odd); chunk c + 1 is read into the other
+        // stage during the products, which was last read before the previous
+        // barrier
+        for (int c = 0; c < nkc; c += 2) {
+            if (c + 1 < nkc) {
+                load_chunk(R, c + 1);
+                dma_chunk(S1, SA1, c + 1);
             }
-#pragma unroll
-            for (int m = 0; m < 3; ++m) {
-                if (mt0 + m >= nmt) continue;
-                const int row = (mt0 + m) * 32 + (lane & 31);
-                const int4v A = __builtin_bit_cast(int4v, S.a[row][kq ^ (row & 7)]);
-                float sa[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4*>(&S.sa[b][(mt0 + m) * 32 + 8 * q + 4 * (lane >> 5)]);
-                    sa[4 * q + 0] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (NM > 0) gu_chunk<NM>(S0, SA0, lane, rg, ru, mt0, cmagic, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if (c + 1 < nkc) store_chunk(S1, R);
+            __syncthreads();
+            if (c + 1 < nkc) {
+                if (c + 2 < nkc) {
+                    load_chunk(R, c + 2);
+                    dma_chunk(S0, SA0, c + 2);
                 }
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    const int16v D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[n], cmagic, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float t = fmaf(__int_as_float(D[r]), sw[n], nc[n]);
-                        acc[m][n][r] = fmaf(t, sa[r], acc[m][n][r]);
-                    }
-                }
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (NM > 0) gu_chunk<NM>(S1, SA1, lane, rg, ru, mt0, cmagic, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                if (c + 2 < nkc) store_chunk(S0, R);
+                __syncthreads();
             }
         }
-    }
-    if (MODE == 0) {
-        // h = silu(g) * u, requantised per (token, 32 features of this wavefront)
-        const int feat = grp * 64 + (wave & 1) * 32 + (lane & 31);
+        // h = silu(g) * u, requantised per (token, 32 features of this
+        // wavefront): the 32 features of a token are the lanes of one
+        // half-wavefront
+        const int feat = grp * kGUFeat + fg * 32 + (lane & 31);
 #pragma unroll
-        for (int m = 0; m < 3; ++m) {
-            if (mt0 + m >= nmt) continue;
+        for (int m = 0; m < NM; ++m) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float hv = silu_q(acc[m][0][r]) * acc[m][1][r];
+                const float g = acc[m][0][r];
+                const float hv = g * acc[m][1][r] * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
                 float amax = fabsf(hv);
-#pragma unroll
-                for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+                amax = fmaxf(amax, __uint_as_float(lane_xor<1>(__float_as_uint(amax))));
+                amax = fmaxf(amax, __uint_as_float(lane_xor<2>(__float_as_uint(amax))));
+                amax = fmaxf(amax, __uint_as_float(lane_xor<4>(__float_as_uint(amax))));
+                amax = fmaxf(amax, __uint_as_float(lane_xor<8>(__float_as_uint(amax))));
+                amax = fmaxf(amax, __uint_as_float(lane_xor<16>(__float_as_uint(amax))));
                 const float sc = amax / 127.0f;
-                int q = 0;
-                if (sc != 0.0f) q = (int)fminf(fmaxf(rintf(hv / sc), -127.0f), 127.0f);
+                float q = 0.0f;
+                if (sc != 0.0f) q = fminf(fmaxf(rintf(hv * (127.0f * __builtin_amdgcn_rcpf(amax))), -127.0f), 127.0f);
                 const int mrow = (mt0 + m) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (mrow < mc) {
-                    const size_t hrow = (size_t)(p0 + m0 + mrow);
-                    hq[hrow * f + feat] = (int8_t)q;
-                    if ((lane & 31) == 0) hs[hrow * (f / 32) + grp * 2 + (wave & 1)] = sc;
-                }
+                if (mrow < mc) h_out[(size_t)(p0 + m0 + mrow) * f + feat] = (_Float16)(q * sc);
             }
         }
-    } else {
+    };
+    switch (min(max(nmt - mt0, 0), 3)) {  // wave-uniform
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        default: run(std::integral_constant<int, 0>{}); break;
+    }
+}
+
+struct DNStage {
+    uint4 w[kDNRows][8];  // fp16 q * s weight rows, 64 k
+    uint4 a[kTR][8];      // fp16 h rows, 64 k
+};
+
+struct DNRegs {
+    uint2v w[2];   // packed int4 words of two (strip, lane) units
+    uint32_t s[2]; // their two fp16 block scales
+    uint4v a[3];   // three 16-byte pieces of h rows
+};
+
+// One k-chunk (four 16-wide MFMA steps) of a down wavefront: NM token tiles
+// (from mt0) times its two weight tiles, as 4 NM steps pipelined by one: the
+// LDS operands of step i + 1 are requested before the MFMAs of step i.
+template <int NM>
+__device__ __forceinline__ void dn_chunk(const DNStage& G, int lane, int r0, int r1, int mt0, float16v (&acc)[3][2]) {
+    constexpr int NS = 4 * NM;
+    half8 A[2], B0[2], B1[2];
+    auto fetch_b = [&](int st) {
+        const int kq = 2 * st + (lane >> 5);  // 16-byte chunk holding this lane's 8 k of step st
+        B0[st & 1] = __builtin_bit_cast(half8, G.w[r0][kq ^ chunk_swz(r0)]);
+        B1[st & 1] = __builtin_bit_cast(half8, G.w[r1][kq ^ chunk_swz(r1)]);
+    };
+    auto fetch_a = [&](int i) {
+        const int st = i / NM, m = i % NM;
+        const int kq = 2 * st + (lane >> 5);
+        const int row = (mt0 + m) * 32 + (lane & 31);
+        A[i & 1] = __builtin_bit_cast(half8, G.a[row][kq ^ chunk_swz(row)]);
+    };
+    fetch_b(0);
+    fetch_a(0);
 #pragma unroll
-        for (int m = 0; m < 3; ++m) {
-            if (mt0 + m >= nmt) continue;
+    for (int i = 0; i < NS; ++i) {
+        const int st = i / NM, m = i % NM;
+        if (i + 1 < NS) {
+            if ((i + 1) % NM == 0) fetch_b(st + 1);
+            fetch_a(i + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the reads of step i + 1 stay ahead of the MFMAs of step i
+        acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i & 1], B0[st & 1], acc[m][0], 0, 0, 0);
+        acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i & 1], B1[st & 1], acc[m][1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Down projection on v_mfma_f32_32x32x16_f16 over operands that hold the
+// dequantised values: fp16(q * s) of the int8 codes of h (written by the
+// gate/up kernel) and fp16(q * s) of the int4 weights, built while the weight
+// rows are staged in LDS.  Products accumulate in fp32 over all of f; nothing
+// downstream is requantised, so the fp16 rounding of the two operands
+// (2^-11 relative each) only adds to the output's error.
+template <typename YT>
+__global__ __launch_bounds__(kPThreads, 1) void ffn_i4_down(
+    const _Float16* __restrict__ h, int T, int d, int f, int k, const void* const* __restrict__ expert_ptrs,
+    const uint8_t* __restrict__ shared_blob, const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, YT* __restrict__ y_perm,
+    float* __restrict__ y_shared) {
+    __shared__ DNStage S[2];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_groups = (d + kDNRows - 1) / kDNRows;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int ti = (j / n_groups) * 8 + xcd, grp = j % n_groups;
+    if (ti >= n_tiles_p[0]) return;
+    const int4 tl = tiles[ti];
+    const int n_active = active[0];
+    const bool routed = tl.x < n_active;
+    const int e = routed ? active[1 + tl.x] : -1;
+    const uint8_t* blob = routed ? (const uint8_t*)expert_ptrs[e] : shared_blob;
+    if (blob == nullptr) return;
+    const int p0 = routed ? offsets[e] : T * k;
+    const int m0 = tl.y, mc = tl.z;
+    const int nmt = (mc + 31) >> 5;
+    const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
+    const int nkt = f / 128;
+    const int n_strips = d / 16;
+    const __amdgpu_buffer_rsrc_t wr = buf_rsrc(blob, (uint32_t)L.total);
+    const __amdgpu_buffer_rsrc_t hr = buf_rsrc(h, (uint32_t)(((size_t)T * k + T) * f * 2));
+    uint32_t wq_off[2], ws_off[2], ha_off[3];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int idx = threadIdx.x + q * kPThreads, st = idx >> 6, ll = idx & 63;
+        const int strip = min(grp * 16 + st, n_strips - 1);  // strips past d repeat the last one (not written)
+        wq_off[q] = (uint32_t)(L.dn.qoff + (size_t)strip * nkt * 1024 + ll * 16);
+        ws_off[q] = (uint32_t)(L.dn.soff + (size_t)strip * nkt * 128 + (ll & 15) * 8);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const int idx = threadIdx.x + q * kPThreads, row = idx >> 3;
+        ha_off[q] = (uint32_t)(p0 + m0 + min(row, mc - 1)) * (uint32_t)f * 2 + (idx & 7) * 16;
+    }
+    // chunk c covers k = 64 c .. 64 c + 63: half (c & 1) of packed tile c >> 1
+    auto load_chunk = [&](DNRegs& R, int c) {
+        const int kt = c >> 1, hh = c & 1;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            R.w[q] = __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(wr, wq_off[q], kt * 1024 + hh * 8, kBufNT));
+            R.s[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(wr, ws_off[q], kt * 128 + hh * 4, kBufNT);
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            R.a[q] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(hr, ha_off[q], c * 128, 0));
+    };
+    auto store_chunk = [&](DNStage& G, const DNRegs& R) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int idx = threadIdx.x + q * kPThreads, st = idx >> 6, ll = idx & 63;
+            const int row = st * 16 + (ll & 15), jq = ll >> 4;
+#pragma unroll
+            for (int bl = 0; bl < 2; ++bl) {  // blocks 2 hh + bl: k_local = 32 bl + 8 jq .. +7
+                const uint32_t sb = (R.s[q] >> (16 * bl)) & 0xFFFFu;
+                const half2v s2 = __builtin_bit_cast(half2v, sb | (sb << 16));
+                uint32_t o[4];
+                int4_word_to_f16(R.w[q][bl], s2, o);
+                const int ch = 4 * bl + jq;
+                G.w[row][ch ^ chunk_swz(row)] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const int idx = threadIdx.x + q * kPThreads, row = idx >> 3, ch = idx & 7;
+            G.a[row][ch ^ chunk_swz(row)] = __builtin_bit_cast(uint4, R.a[q]);
+        }
+    };
+    const int og = wave & 3, mt0 = 3 * (wave >> 2);
+    const int r0 = og * 64 + (lane & 31), r1 = r0 + 32;  // this lane's two weight rows (output rows)
+    const int nkc = f / 64;
+    // The wavefront's loop is instantiated for its number of token tiles, so
+    // that each instance is straight-line code (and the register allocation of
+    // one does not constrain another).  Every instance stages its share of each
+    // chunk and meets the same barriers.
+    auto run = [&](auto nm_c) {
+        constexpr int NM = decltype(nm_c)::value;
+        float16v acc[3][2];
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+        // two chunks in flight: while chunk c is multiplied from one LDS
+        // buffer, chunk c + 1 waits in registers to be written to the other and
+        // chunk c + 2 is being read; one barrier per chunk
+        DNRegs R0, R1;
+        load_chunk(R0, 0);
+        if (nkc > 1) load_chunk(R1, 1);
+        store_chunk(S[0], R0);
+        __syncthreads();
+        if (nkc > 2) load_chunk(R0, 2);
+        for (int c = 0; c < nkc; c += 2) {
+            if constexpr (NM > 0) dn_chunk<NM>(S[0], lane, r0, r1, mt0, acc);  // chunk c
+            if (c + 1 < nkc) store_chunk(S[1], R1);                          // chunk c + 1
+            __syncthreads();
+            if (c + 3 < nkc) load_chunk(R1, c + 3);
+            if (c + 1 < nkc) {
+                if constexpr (NM > 0) dn_chunk<NM>(S[1], lane, r0, r1, mt0, acc);  // chunk c + 1
+                if (c + 2 < nkc) store_chunk(S[0], R0);                          // chunk c + 2
+                __syncthreads();
+                if (c + 4 < nkc) load_chunk(R0, c + 4);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
-                const int o = grp * 128 + (n == 0 ? nt0 : nt1) * 32 + (lane & 31);
+                const int o = grp * kDNRows + (n == 0 ? r0 : r1);
+                if (o >= d) continue;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int mrow = (mt0 + m) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -600,6 +856,12 @@ __global__ __launch_bounds__(256) void ffn_q8_tiled(const int8_t* __restrict__ a
                 }
             }
         }
+    };
+    switch (min(max(nmt - mt0, 0), 3)) {  // wave-uniform
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        default: run(std::integral_constant<int, 0>{}); break;
     }
 }
 
@@ -613,27 +875,29 @@ static int run_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
     if constexpr (WFMT == MOE_WFMT_I4B32) {
         // tiles of <= 192 rows; work items of one tile on one XCD (grid rounded to 8 tiles)
         int4* t4 = reinterpret_cast<int4*>(w.tiles);
-        const long max_tiles = (long)std::min(a->E, a->T * a->k) + (long)a->T * a->k / (kTM * 32) +
-                               (a->shared_blob ? a->T / (kTM * 32) + 1 : 0);
+        _Float16* h16 = reinterpret_cast<_Float16*>(w.h);
+        const long max_tiles = (long)std::min(a->E, a->T * a->k) + (long)a->T * a->k / kTR +
+                               (a->shared_blob ? a->T / kTR + 1 : 0);
         const long gt = (max_tiles + 7) / 8 * 8;
         if (a->phase != 2) {
             q8_tile_plan<<<1, 1024, 0, s>>>(a->counts, a->active, a->T, a->shared_blob ? 1 : 0, t4, n_tiles);
             rc = check_launch();
             if (rc) return rc;
-            ffn_q8_tiled<0, float><<<(unsigned)(gt * (a->f / 64)), 256, 0, s>>>(
+            ffn_i4_gateup<<<(unsigned)(gt * (a->f / kGUFeat)), kPThreads, 0, s>>>(
                 a->xq, a->sx, a->T, a->d, a->f, a->k, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->offsets,
-                a->sorted_idx, a->active, t4, n_tiles, hq, w.hs, nullptr, nullptr);
+                a->sorted_idx, a->active, t4, n_tiles, h16);
             rc = check_launch();
             if (rc || a->phase == 1) return rc;
         }
+        const unsigned g2 = (unsigned)(gt * ((a->d + kDNRows - 1) / kDNRows));
         if (a->y_dtype == MOE_DT_F32)
-            ffn_q8_tiled<1, float><<<(unsigned)(gt * (a->d / 128)), 256, 0, s>>>(
-                hq, w.hs, a->T, a->d, a->f, a->k, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->offsets,
-                a->sorted_idx, a->active, t4, n_tiles, nullptr, nullptr, (float*)a->y_perm, a->y_shared);
+            ffn_i4_down<float><<<g2, kPThreads, 0, s>>>(h16, a->T, a->d, a->f, a->k, a->expert_ptrs,
+                                                        (const uint8_t*)a->shared_blob, a->offsets, a->active, t4,
+                                                        n_tiles, (float*)a->y_perm, a->y_shared);
         else
-            ffn_q8_tiled<1, _Float16><<<(unsigned)(gt * (a->d / 128)), 256, 0, s>>>(
-                hq, w.hs, a->T, a->d, a->f, a->k, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->offsets,
-                a->sorted_idx, a->active, t4, n_tiles, nullptr, nullptr, (_Float16*)a->y_perm, a->y_shared);
+            ffn_i4_down<_Float16><<<g2, kPThreads, 0, s>>>(h16, a->T, a->d, a->f, a->k, a->expert_ptrs,
+                                                           (const uint8_t*)a->shared_blob, a->offsets, a->active, t4,
+                                                           n_tiles, (_Float16*)a->y_perm, a->y_shared);
         return check_launch();
     }
     if (a->phase != 2) {

@@ -44,6 +44,7 @@ def check_routing(st, o, E):
 
 def check_float(got, ref, what):
     ok, rel, mx = R.within_tolerance(got, ref)
+    print("[parity] %s: rel-L2 %.3e, max-abs/RMS %.3e" % (what, rel, mx), flush=True)
     assert ok, "%s: rel-L2 %.3e, max-abs/RMS %.3e" % (what, rel, mx)
 
 
