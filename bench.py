@@ -1,7 +1,9 @@
 """Benchmark of the sparse-MoE FFN layer hot path on one MI355X.
 
 One step = one pass of the whole layer over one batch of seeded synthetic
-input already resident in HBM: moe_route_permute (routing and grouping) ->
+input already resident in HBM.  The default run measures both halves of the
+metric: the decode layer at T=4 (the line's value) and, nested under
+"prefill", the 8,192-token prefill chunk (its own seeded layer).  Steps: moe_route_permute (routing and grouping) ->
 [moe_quantize_act] -> moe_expert_ffn_combine (expert FFN and the gate-weighted
 combine); for decode batches (T <= 8, int4 weights) moe_route ->
 moe_expert_ffn_combine_slots, where every routed slot is its own work item and
@@ -19,11 +21,11 @@ expert weights from HBM rather than from the 256 MB Infinity Cache.  Each
 copy's step is captured in a HIP graph; one graph holds one step on every copy
 in turn, so that host launch overhead is paid once per ``--rotate`` steps.
 Two timed regions, both bracketed by a device synchronisation: (A) ``--steps``
-whole-layer steps, which give ``value`` and ``ms_per_step``; (B) ``--steps``
-back-to-back launches of the dominant kernel alone (the expert gate/up
-projection, ``moe_expert_ffn`` phase 1, rotating over the weight copies, also
-replayed from graphs) between two HIP events on its launch stream, whose mean
-launch time gives the roofline figure.
+whole-layer steps, which give ``value`` and ``ms_per_step``; (B) at least 25
+whole rotations of back-to-back launches of the dominant kernel alone (the
+expert gate/up projection, rotating over the weight copies, also replayed from
+graphs) between two HIP events on its launch stream, whose mean launch time
+gives the roofline figure.
 
 Prints one JSON line (rank 0).  ``--gpus`` above 1 is not supported: the
 benchmark runs on one GPU.
@@ -57,6 +59,7 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true", help="decode_t4 only: skip the nested prefill measurement")
     p.add_argument("--seed", type=int, default=0)
     return p.parse_args()
 
@@ -111,10 +114,6 @@ def main():
         sys.exit(2)
     import torch
 
-    import synth
-    from sparse_moe_expert_gemv_amd import binding as B
-    from sparse_moe_expert_gemv_amd.layer import MoELayer, pack_blobs, pointer_table
-
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     name = a.workload
@@ -128,10 +127,31 @@ def main():
         return bench_copy(a)
     if name == "peak":
         return bench_peak(a)
+    line = bench_layer(a, name, a.steps, a.warmup, a.rotate, with_cpu=not a.no_cpu_baseline)
+    if name == "decode_t4" and not a.no_prefill:
+        # the metric's other half: the 8,192-token prefill chunk of the same
+        # model, timed in the same run (its own seeded layer)
+        torch.cuda.empty_cache()
+        pf = bench_layer(a, "prefill", None, None, None, with_cpu=False)
+        line["prefill"] = {k: pf[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "config",
+                                              "roofline")}
+    print(json.dumps(line), flush=True)
+
+
+def bench_layer(a, name, steps, warmup, rotate, with_cpu):
+    """One layer workload (decode_t4, decode_t1, prefill, skew, tiny): the
+    bench line's fields as a dict."""
+    import torch
+
+    import synth
+    from sparse_moe_expert_gemv_amd import binding as B
+    from sparse_moe_expert_gemv_amd.layer import MoELayer, pack_blobs, pointer_table
+
+    dev = torch.device("cuda:0")
     big = name == "prefill"
-    steps = a.steps if a.steps is not None else (20 if big else 200)
-    warmup = a.warmup if a.warmup is not None else (3 if big else 20)
-    rotate = a.rotate if a.rotate is not None else (2 if big else 8)
+    steps = steps if steps is not None else (20 if big else 200)
+    warmup = warmup if warmup is not None else (3 if big else 20)
+    rotate = rotate if rotate is not None else (2 if big else 8)
     t_gen = time.time()
     L = synth.make_layer(name, seed=a.seed)
     cfg = L.cfg
@@ -284,14 +304,18 @@ def main():
     total_ms = timed(lambda i: run_all(step_r, step_graphs, steps), 1)
     ms_step = total_ms / steps
 
-    # region B: the dominant kernel (gate/up) alone: --steps back-to-back launches on
-    # the stream, rotating over the weight copies, between two HIP events
+    # region B: the dominant kernel (gate/up) alone: back-to-back launches on the
+    # stream, rotating over the weight copies, between two HIP events; always a
+    # fixed number of whole rotations (at least 25 chain replays, whatever
+    # --steps is), so that host submission gaps between graph replays do not
+    # enter the per-launch time
+    n_kernel = max(25, -(-steps // rotate)) * rotate
     timed(lambda i: run_all(gu_r, gu_graphs, rotate), 1)
-    gu_ms = timed(lambda i: run_all(gu_r, gu_graphs, steps), 1) / steps
+    gu_ms = timed(lambda i: run_all(gu_r, gu_graphs, n_kernel), 1) / n_kernel
     alone_ms = None
     if by_slot:
         timed(lambda i: run_all(alone_r, alone_graphs, rotate), 1)
-        alone_ms = timed(lambda i: run_all(alone_r, alone_graphs, steps), 1) / steps
+        alone_ms = timed(lambda i: run_all(alone_r, alone_graphs, n_kernel), 1) / n_kernel
 
     # algorithmic work per gate/up launch, from each copy's routing (fixed input per copy):
     # the distinct experts picked (the by-slot launch reads an expert once per slot)
@@ -319,6 +343,7 @@ def main():
                           else "ffn_gateup_tok64 (moe_expert_ffn phase 1)" if T <= 64
                           else "ffn_float_gateup (moe_expert_ffn phase 1)")
     roof["kernel_ms"] = round(gu_ms, 5)
+    roof["kernel_launches_timed"] = n_kernel
     roof["algorithmic_bytes_per_launch"] = int(alg_bytes)
     roof["algorithmic_ops_per_launch"] = int(alg_ops)
     if alone_ms is not None:
@@ -327,8 +352,9 @@ def main():
                                     "kernel_ms": round(alone_ms, 5), "achieved": round(a_gbs, 1),
                                     "frac": round(a_gbs / HBM_PEAK_GBS, 4)}
 
+    del layers, xs, step_graphs, gu_graphs, alone_graphs, packed0
     cpu = None
-    if not a.no_cpu_baseline:
+    if with_cpu:
         cpu = cpu_baseline(L, a.cpu_seconds)
 
     value = T / (ms_step * 1e-3)
@@ -345,7 +371,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    return line
 
 
 def bench_decode_stack(a):
