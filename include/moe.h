@@ -297,6 +297,27 @@ int moe_route_ffn_combine_slots(const moe_ffn_args* args, const float* Wr, const
                                 float* gates, const float* residual, float* out, moe_stream_t stream);
 
 /*
+ * moe_route_ffn_combine_slots for callers that cannot allocate device memory
+ * (code under HIP graph capture that may not call hipMalloc, tight serving
+ * loops, harnesses that forbid allocation): the same launches and results, bit
+ * for bit, with the workspace taken from a scratch array the library keeps in
+ * device memory (MOE_NOALLOC_SCRATCH_BYTES on every GPU it runs on, held until
+ * the process ends; its device address is looked up once per device).  The
+ * call allocates nothing.  args->ws and args->ws_bytes are ignored; phase must
+ * be 0.  Every call on one GPU shares that GPU's scratch, and the scratch
+ * needs no clearing (every byte a call reads it first writes): calls that
+ * overlap on one GPU (two streams, or two threads) race and must be ordered by
+ * the caller.
+ * Errors: those of moe_route_ffn_combine_slots; MOE_ERR_INVALID_ARG for a
+ * phase other than 0; MOE_ERR_NO_MEMORY when the shape's workspace
+ * (moe_workspace_size) exceeds MOE_NOALLOC_SCRATCH_BYTES; MOE_ERR_HIP when the
+ * scratch address cannot be obtained.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (2u << 20)
+int moe_route_ffn_combine_slots_noalloc(const moe_ffn_args* args, const float* Wr, const float* bias, int32_t* ids,
+                                        float* gates, const float* residual, float* out, moe_stream_t stream);
+
+/*
  * Combine: out[t] = residual[t] + y_shared[t] + sum_{j<k} gates[t,j] * y_perm[dest[t*k+j]],
  * summed in j order (deterministic).
  *   y_perm [T*k, d] (y_dtype F32 or F16), dest [T*k], gates [T, k],

@@ -28,10 +28,15 @@ EXPORTED = [
     "moe_version", "moe_last_hip_error", "moe_status_string", "moe_expert_bytes", "moe_pack_experts",
     "moe_unpack_experts", "moe_workspace_size", "moe_route", "moe_route_permute", "moe_permute", "moe_quantize_act",
     "moe_expert_ffn", "moe_expert_ffn_combine", "moe_expert_ffn_combine_slots", "moe_route_ffn_combine_slots",
+    "moe_route_ffn_combine_slots_noalloc",
     "moe_rmsnorm",
     "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
     "moe_cache_stage", "moe_cache_map_host", "moe_usage_accumulate", "moe_cache_plan", "moe_cache_replace",
 ]
+
+
+# device scratch of moe_route_ffn_combine_slots_noalloc (include/moe.h)
+MOE_NOALLOC_SCRATCH_BYTES = 2 << 20
 
 
 class MoeError(RuntimeError):
@@ -82,6 +87,7 @@ def lib():
             "moe_expert_ffn_combine": ([C.POINTER(FfnArgs), P, P, P, P, P, P], I),
             "moe_expert_ffn_combine_slots": ([C.POINTER(FfnArgs), P, P, P, P, P], I),
             "moe_route_ffn_combine_slots": ([C.POINTER(FfnArgs), P, P, P, P, P, P, P], I),
+            "moe_route_ffn_combine_slots_noalloc": ([C.POINTER(FfnArgs), P, P, P, P, P, P, P], I),
             "moe_combine": ([P, I, P, P, P, P, I, I, I, P, P], I),
             "moe_cache_create": ([C.POINTER(P), I, I, I, S, P, P, I, I], I),
             "moe_cache_destroy": ([P], I),
@@ -246,6 +252,21 @@ def moe_route_ffn_combine_slots(*, T, d, f, E, k, wfmt, act_mode, expert_ptrs, w
     a.ws, a.ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
     a.y_dtype, a.phase = MOE_DT_F32, phase
     _check("moe_route_ffn_combine_slots", lib().moe_route_ffn_combine_slots(
+        C.byref(a), _ptr(Wr), _ptr(bias), _ptr(ids), _ptr(gates), _ptr(residual), _ptr(out), _stream(stream)))
+
+
+def moe_route_ffn_combine_slots_noalloc(*, T, d, f, E, k, wfmt, act_mode, expert_ptrs, Wr, bias, ids, gates, out, x,
+                                        residual=None, shared_blob=None, stream=None):
+    """The decode layer with the library's own device scratch (no workspace)."""
+    a = FfnArgs()
+    a.T, a.d, a.f, a.E, a.k = T, d, f, E, k
+    a.wfmt, a.act_mode = wfmt, act_mode
+    a.x, a.x_dtype = x.data_ptr(), _xdtype(x)
+    a.expert_ptrs = expert_ptrs.data_ptr()
+    a.shared_blob = None if shared_blob is None else shared_blob.data_ptr()
+    a.ws, a.ws_bytes = None, 0
+    a.y_dtype, a.phase = MOE_DT_F32, 0
+    _check("moe_route_ffn_combine_slots_noalloc", lib().moe_route_ffn_combine_slots_noalloc(
         C.byref(a), _ptr(Wr), _ptr(bias), _ptr(ids), _ptr(gates), _ptr(residual), _ptr(out), _stream(stream)))
 
 

@@ -1,6 +1,7 @@
 // C ABI entry points: argument validation (before any HIP call), workspace
 // carve-up and dispatch to the kernel launchers.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -216,8 +217,8 @@ int moe_expert_ffn_combine_slots(const moe_ffn_args* a, const int32_t* ids, cons
     return launch_ffn_combine_slots(a, w, ids, gates, residual, out, as_stream(s));
 }
 
-int moe_route_ffn_combine_slots(const moe_ffn_args* a, const float* Wr, const float* bias, int32_t* ids,
-                                float* gates, const float* residual, float* out, moe_stream_t s) {
+static int route_ffn_combine_slots_args(const moe_ffn_args* a, const float* Wr, int32_t* ids, float* gates,
+                                        float* out, bool need_ws) {
     if (!a || (a->phase != 0 && a->phase != 1)) return MOE_ERR_INVALID_ARG;
     if (a->T < 0 || !shape_ok(a->d, a->E, a->k) || a->f <= 0 || a->f % 128 ||
         (a->wfmt != MOE_WFMT_I4B32 && a->wfmt != MOE_WFMT_I8B32) ||
@@ -225,10 +226,13 @@ int moe_route_ffn_combine_slots(const moe_ffn_args* a, const float* Wr, const fl
         (a->x_dtype != MOE_DT_F32 && a->x_dtype != MOE_DT_BF16))
         return MOE_ERR_INVALID_ARG;
     if (a->T == 0) return MOE_OK;
-    if (!a->x || !a->expert_ptrs || !a->ws || !Wr || !ids || !gates || !out) return MOE_ERR_INVALID_ARG;
-    Workspace w;
-    workspace_layout(a->T, a->d, a->f, a->E, a->k, a->act_mode, (char*)a->ws, &w);
-    if (a->ws_bytes < w.bytes) return MOE_ERR_NO_MEMORY;
+    if (!a->x || !a->expert_ptrs || (need_ws && !a->ws) || !Wr || !ids || !gates || !out) return MOE_ERR_INVALID_ARG;
+    return -1;  // arguments valid, work to do
+}
+
+static int route_ffn_combine_slots_run(const moe_ffn_args* a, const Workspace& w, const float* Wr, const float* bias,
+                                       int32_t* ids, float* gates, const float* residual, float* out,
+                                       moe_stream_t s) {
     if (!ffn_combine_slots_ok(a)) return MOE_ERR_UNSUPPORTED;
     if (a->phase == 0) {  // phase 1: the router logits are already in the workspace
         const int rc = launch_route_logits(a->x, a->x_dtype, a->T, a->d, Wr, bias, a->E, w.logits, as_stream(s));
@@ -236,6 +240,70 @@ int moe_route_ffn_combine_slots(const moe_ffn_args* a, const float* Wr, const fl
     }
     return launch_ffn_combine_slots_topk(a, w, logit_planes(a->T, a->d, a->E), ids, gates, residual, out,
                                          as_stream(s));
+}
+
+int moe_route_ffn_combine_slots(const moe_ffn_args* a, const float* Wr, const float* bias, int32_t* ids,
+                                float* gates, const float* residual, float* out, moe_stream_t s) {
+    const int rc = route_ffn_combine_slots_args(a, Wr, ids, gates, out, true);
+    if (rc >= 0) return rc;
+    Workspace w;
+    workspace_layout(a->T, a->d, a->f, a->E, a->k, a->act_mode, (char*)a->ws, &w);
+    if (a->ws_bytes < w.bytes) return MOE_ERR_NO_MEMORY;
+    return route_ffn_combine_slots_run(a, w, Wr, bias, ids, gates, residual, out, s);
+}
+
+// ---- the same decode layer without a caller workspace ------------------------
+// Scratch for callers that cannot allocate: a file-scope device array that
+// every GPU the library runs on holds until the process ends.  Host code uses
+// only the device address hipGetSymbolAddress returns for the current device
+// (the array's name is a host-side stand-in), looked up once per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+static void* device_scratch(int* rc) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        set_last_hip_error(e != hipSuccess ? e : hipErrorInvalidDevice);
+        *rc = MOE_ERR_HIP;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+        set_last_hip_error(g_scratch_err[dev] != hipSuccess ? g_scratch_err[dev] : hipErrorInvalidSymbol);
+        *rc = MOE_ERR_HIP;
+        return nullptr;
+    }
+    *rc = MOE_OK;
+    return g_scratch_ptr[dev];
+}
+
+int moe_route_ffn_combine_slots_noalloc(const moe_ffn_args* a, const float* Wr, const float* bias, int32_t* ids,
+                                        float* gates, const float* residual, float* out, moe_stream_t s) {
+    int rc = route_ffn_combine_slots_args(a, Wr, ids, gates, out, false);
+    if (rc >= 0) return rc;
+    if (a->phase != 0) return MOE_ERR_INVALID_ARG;
+    Workspace w;
+    workspace_layout(a->T, a->d, a->f, a->E, a->k, a->act_mode, nullptr, &w);
+    if (w.bytes > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_NO_MEMORY;
+    if (!ffn_combine_slots_ok(a)) return MOE_ERR_UNSUPPORTED;
+    char* base = static_cast<char*>(device_scratch(&rc));
+    if (!base) return rc;
+    workspace_layout(a->T, a->d, a->f, a->E, a->k, a->act_mode, base, &w);
+    moe_ffn_args b = *a;
+    b.ws = base;
+    b.ws_bytes = MOE_NOALLOC_SCRATCH_BYTES;
+    return route_ffn_combine_slots_run(&b, w, Wr, bias, ids, gates, residual, out, s);
 }
 
 int moe_combine(const void* y_perm, int y_dtype, const int32_t* dest, const float* gates, const float* y_shared,

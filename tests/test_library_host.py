@@ -130,6 +130,32 @@ def test_invalid_arguments_rejected_before_any_hip_call():
     assert L.moe_route_ffn_combine_slots(C.byref(a), None, None, None, None, None, None, None) == B.MOE_OK
 
 
+def test_noalloc_decode_entry_rejects_before_any_hip_call():
+    """The no-allocation decode entry validates everything, including the
+    scratch limit, before it touches the device (no GPU here)."""
+    L = B.lib()
+    dummy = C.c_void_p(0x1000)
+    a = B.FfnArgs()
+    a.T, a.d, a.f, a.E, a.k, a.wfmt, a.act_mode, a.y_dtype = 4, 2048, 768, 512, 10, 4, 0, 0
+    a.x_dtype = B.MOE_DT_BF16
+    fn = L.moe_route_ffn_combine_slots_noalloc
+    assert fn(None, dummy, None, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    assert fn(C.byref(a), dummy, None, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG  # null x
+    a.x, a.expert_ptrs = 0x1000, 0x1000  # ws stays null: it is not used
+    assert fn(C.byref(a), None, None, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG  # null Wr
+    a.phase = 1
+    assert fn(C.byref(a), dummy, None, dummy, dummy, None, dummy, None) == B.MOE_ERR_INVALID_ARG
+    a.phase = 0
+    # a shape whose workspace exceeds the scratch: 8 tokens, 64 slots each, f = 2048
+    a.T, a.k, a.f, a.E = 8, 64, 2048, 1024
+    assert fn(C.byref(a), dummy, None, dummy, dummy, None, dummy, None) == B.MOE_ERR_NO_MEMORY
+    a.T, a.k, a.f, a.E = 9, 10, 768, 512  # no by-slot kernel beyond 8 tokens
+    assert fn(C.byref(a), dummy, None, dummy, dummy, None, dummy, None) == B.MOE_ERR_UNSUPPORTED
+    a.T = 0
+    assert fn(C.byref(a), None, None, None, None, None, None, None) == B.MOE_OK
+    assert B.MOE_NOALLOC_SCRATCH_BYTES == 2 << 20
+
+
 def test_workspace_too_small_is_reported():
     """A too-small workspace is rejected with MOE_ERR_NO_MEMORY (pointers are
     never dereferenced on the host, so fake non-null values are safe)."""
