@@ -60,6 +60,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline leg")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true", help="decode_t4 only: skip the nested prefill measurement")
+    p.add_argument("--no-split", action="store_true", help="decode stacks: skip the host-core miss split sweep")
     p.add_argument("--seed", type=int, default=0)
     return p.parse_args()
 
@@ -392,7 +393,8 @@ def bench_decode_stack(a):
     c = S.cfg
     store = build_host_store(S.pool, c.wfmt, c.d, c.f)
     G = ExpertStack(S.routers, S.shared_blobs(), store, S.index, S.resident, d=c.d, f=c.f, k=c.k, wfmt=c.wfmt,
-                    act_mode=B.MOE_ACT_FLOAT, max_T=c.T, biases=S.biases, miss_mode="host", by_slot=True)
+                    act_mode=B.MOE_ACT_FLOAT, max_T=c.T, biases=S.biases, miss_mode="host", by_slot=True,
+                    cpu_blobs=S.pool)
     x = torch.from_numpy(synth.bf16_bits_to_f32(S.x)).cuda()
     print("[bench] %s: %d layers x %d experts, %d resident, %d-blob host pool, T=%d (ready in %.1fs)"
           % (a.workload, c.n_layers, c.E, len(S.resident), c.n_pool_blobs, c.T, time.time() - t0),
@@ -441,6 +443,34 @@ def bench_decode_stack(a):
     ms_comp = timed(g_comp, steps)
     value = c.T / (ms_step * 1e-3)
     extra = ms_step - ms_comp
+    # the pages' split of the misses: a share pcie_frac read by the GPU over the
+    # host link, the rest computed on host cores while the GPU computes the
+    # layer (eager: every layer waits for its routing on the host)
+    split = None
+    if a.workload in ("decode_stack", "decode_stack_t1") and not a.no_split:
+        G.set_pcie_frac(1.0)
+        threads = max(1, min(16, os.cpu_count() or 1))
+        fracs, ms_split, items = [1.0, 0.75, 0.5, 0.25, 0.0], [], []
+        for fr in fracs:
+            G.set_pcie_frac(fr, threads)
+            for _ in range(2):
+                G.forward(x)
+            torch.cuda.synchronize()
+            G.cpu_items = 0
+            n = max(3, steps // 4)
+            t0 = time.perf_counter()
+            for _ in range(n):
+                G.forward(x)
+            torch.cuda.synchronize()
+            ms_split.append(round(1e3 * (time.perf_counter() - t0) / n, 3))
+            items.append(round(G.cpu_items / n, 2))
+            print("[bench] %s split pcie_frac=%.2f: %.3f ms/step, %.1f host items/step"
+                  % (a.workload, fr, ms_split[-1], items[-1]), file=sys.stderr, flush=True)
+        G.set_pcie_frac(1.0)
+        best = int(np.argmin(ms_split))
+        split = {"pcie_frac": fracs, "ms_per_step_eager": ms_split, "host_items_per_step": items,
+                 "host_threads": threads, "best_pcie_frac": fracs[best],
+                 "best_tokens_per_s": round(c.T / (ms_split[best] * 1e-3), 2)}
     line = {
         "metric": "MoE-layer tokens/s (8192-tok prefill; 1-4 tok decode); % HBM BW / MFMA peak",
         "value": round(value, 2), "unit": "tokens/s (48-layer decode stack)", "n_gpus": 1, "steps": steps,
@@ -456,7 +486,8 @@ def bench_decode_stack(a):
                          "host_bytes_per_step": int(miss_bytes),
                          "all_resident_ms": round(ms_comp, 4),
                          "host_read_ms": round(extra, 4),
-                         "host_read_GBps": round(miss_bytes / (extra * 1e-3) / 1e9, 2) if extra > 0 else None},
+                         "host_read_GBps": round(miss_bytes / (extra * 1e-3) / 1e9, 2) if extra > 0 else None,
+                         "split_misses_with_host_cores": split},
         "roofline": None,
         "cpu_baseline": None,
     }

@@ -318,6 +318,33 @@ int moe_route_ffn_combine_slots_noalloc(const moe_ffn_args* args, const float* W
                                         float* gates, const float* residual, float* out, moe_stream_t stream);
 
 /*
+ * Host-core execution of missed experts ("How Strata works", three-tier
+ * division and adaptive expert cache: experts the GPU has not cached are
+ * computed by the CPU from system memory while the GPU computes the cached
+ * ones; "Strata benchmarks", calibration: the share of misses copied to the
+ * GPU and the number of CPU expert threads are the knobs).  HOST memory and
+ * host cores only; no HIP call.
+ *
+ * moe_host_pool_create(n_threads, &pool): a persistent pool of n_threads
+ * (1..256, the calling thread counts as one) that moe_host_expert_ffn uses.
+ * moe_host_pool_destroy(pool): joins and frees it (NULL is a no-op).
+ *
+ * moe_host_expert_ffn: for each item i, in the given order,
+ *   out[item_token[i], :] += item_gate[i] * FFN_{item_blob[i]}(x[item_token[i], :])
+ * with FFN(x) = Wd (silu(Wg x) * (Wu x)) over a CANONICAL expert blob
+ * (item_blob[i], host pointer; wfmt I4B32 or I8B32).  x [T, d] and out [T, d]
+ * are fp32 host arrays.  Arithmetic in fp32 (block sums times the fp16 block
+ * scale); the result does not depend on the pool size.
+ * Errors: MOE_ERR_INVALID_ARG (null pool or pointers, shapes not multiples of
+ * 32, a token outside [0, T), a null blob), MOE_ERR_NO_MEMORY.
+ */
+typedef struct moe_host_pool moe_host_pool;
+int moe_host_pool_create(int n_threads, moe_host_pool** pool);
+int moe_host_pool_destroy(moe_host_pool* pool);
+int moe_host_expert_ffn(moe_host_pool* pool, int n_items, const int32_t* item_token, const float* item_gate,
+                        const void* const* item_blob, int wfmt, int T, int d, int f, const float* x, float* out);
+
+/*
  * Combine: out[t] = residual[t] + y_shared[t] + sum_{j<k} gates[t,j] * y_perm[dest[t*k+j]],
  * summed in j order (deterministic).
  *   y_perm [T*k, d] (y_dtype F32 or F16), dest [T*k], gates [T, k],

@@ -11,6 +11,8 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+import numpy as np
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
@@ -28,7 +30,7 @@ EXPORTED = [
     "moe_version", "moe_last_hip_error", "moe_status_string", "moe_expert_bytes", "moe_pack_experts",
     "moe_unpack_experts", "moe_workspace_size", "moe_route", "moe_route_permute", "moe_permute", "moe_quantize_act",
     "moe_expert_ffn", "moe_expert_ffn_combine", "moe_expert_ffn_combine_slots", "moe_route_ffn_combine_slots",
-    "moe_route_ffn_combine_slots_noalloc",
+    "moe_route_ffn_combine_slots_noalloc", "moe_host_pool_create", "moe_host_pool_destroy", "moe_host_expert_ffn",
     "moe_rmsnorm",
     "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
     "moe_cache_stage", "moe_cache_map_host", "moe_usage_accumulate", "moe_cache_plan", "moe_cache_replace",
@@ -88,6 +90,9 @@ def lib():
             "moe_expert_ffn_combine_slots": ([C.POINTER(FfnArgs), P, P, P, P, P], I),
             "moe_route_ffn_combine_slots": ([C.POINTER(FfnArgs), P, P, P, P, P, P, P], I),
             "moe_route_ffn_combine_slots_noalloc": ([C.POINTER(FfnArgs), P, P, P, P, P, P, P], I),
+            "moe_host_pool_create": ([I, C.POINTER(P)], I),
+            "moe_host_pool_destroy": ([P], I),
+            "moe_host_expert_ffn": ([P, I, P, P, P, I, I, I, I, P, P], I),
             "moe_combine": ([P, I, P, P, P, P, I, I, I, P, P], I),
             "moe_cache_create": ([C.POINTER(P), I, I, I, S, P, P, I, I], I),
             "moe_cache_destroy": ([P], I),
@@ -373,3 +378,31 @@ def moe_cache_plan(resident, score, max_swaps, margin=0.0):
     _check("moe_cache_plan", lib().moe_cache_plan(res.size, res.ctypes.data, sc.ctypes.data, max_swaps,
                                                   float(margin), ev.ctypes.data, ad.ctypes.data, C.byref(n)))
     return ev[:n.value].copy(), ad[:n.value].copy()
+
+
+class HostPool:
+    """Host threads for moe_host_expert_ffn (the CPU share of missed experts)."""
+
+    def __init__(self, n_threads: int):
+        h = C.c_void_p()
+        _check("moe_host_pool_create", lib().moe_host_pool_create(int(n_threads), C.byref(h)))
+        self.h = h
+        self.n_threads = int(n_threads)
+
+    def expert_ffn(self, item_token, item_gate, item_blob_ptrs, wfmt, x, out, d, f):
+        """out[item_token[i]] += item_gate[i] * FFN_i(x[item_token[i]]); x, out: fp32 numpy [T, d]
+        (out updated in place); item_blob_ptrs: host addresses of canonical blobs."""
+        n = len(item_token)
+        tok = np.ascontiguousarray(item_token, dtype=np.int32)
+        g = np.ascontiguousarray(item_gate, dtype=np.float32)
+        ptrs = (C.c_void_p * max(n, 1))(*[int(p) for p in item_blob_ptrs])
+        assert x.dtype == np.float32 and out.dtype == np.float32 and x.flags.c_contiguous and out.flags.c_contiguous
+        _check("moe_host_expert_ffn", lib().moe_host_expert_ffn(
+            self.h, n, tok.ctypes.data_as(C.c_void_p), g.ctypes.data_as(C.c_void_p), C.cast(ptrs, C.c_void_p),
+            int(wfmt), int(x.shape[0]), int(d), int(f), x.ctypes.data_as(C.c_void_p),
+            out.ctypes.data_as(C.c_void_p)))
+
+    def close(self):
+        if self.h:
+            lib().moe_host_pool_destroy(self.h)
+            self.h = C.c_void_p()

@@ -34,7 +34,13 @@ CFLAGS = [
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip") or f.endswith(".cpp"))
+
+
+# host-only C++ (the host expert FFN): g++, vectorised per CPU by function
+# multiversioning (target_clones), no HIP
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O3", "-fPIC", "-std=c++17", "-pthread", "-fno-fast-math", "-mprefer-vector-width=512", "-Wall", "-I", INCLUDE]
 
 
 # per-file extra flags: MFMA results stay in VGPRs, since the epilogues read every element
@@ -45,7 +51,10 @@ FILE_FLAGS = {"ffn_q8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
@@ -58,7 +67,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-pthread", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))

@@ -17,6 +17,15 @@ layer computes ("Strata benchmarks", prefill optimisation table).  Here:
   it, so a decode pass needs no staging, no side stream and no host round trip
   (the pages' "single RTX 5090 runs a 125B model" report: only the experts the
   gating network picks are computed);
+* or (decode, ``pcie_frac < 1``) the misses of each layer are split: a share
+  ``pcie_frac`` of the missed experts is read over the host link by the GPU
+  as above, the rest is computed by host cores from the canonical blobs in
+  system memory (``moe_host_expert_ffn``) while the GPU computes the rest of
+  the layer, and the host results are added to the layer output on the GPU
+  (``moe_combine``).  This is the pages' split of cached experts on the GPU
+  and missed ones on the CPU ("How Strata works", three-tier division;
+  "Strata benchmarks", calibration: the share of misses copied to the GPU
+  and the number of CPU expert threads);
 * the residency can adapt (``AdaptiveResidency``): per-layer selection
   counters on the device, aged into scores on the host, and swaps of the
   weakest resident experts for the strongest missing ones;
@@ -31,6 +40,7 @@ All device memory comes from PyTorch; all computation is in libmoe.so.
 """
 from __future__ import annotations
 
+import os
 import time
 
 import numpy as np
@@ -43,7 +53,7 @@ from .layer import pack_blobs
 class ExpertStack:
     def __init__(self, routers, shared_blobs, host_store: torch.Tensor, host_index: np.ndarray, resident_ids,
                  *, d, f, k, wfmt, act_mode, max_T, staging_slots=None, device="cuda", eps=1e-6,
-                 biases=None, miss_mode="stage", by_slot=False):
+                 biases=None, miss_mode="stage", by_slot=False, cpu_blobs=None, pcie_frac=1.0, cpu_threads=None):
         """
         routers      list of L fp32 arrays [E, d]
         shared_blobs [L, bytes] canonical uint8 (numpy) or None
@@ -56,6 +66,12 @@ class ExpertStack:
         by_slot      decode batches (float mode, int4, T <= 8) without usage
                      counters: moe_route_ffn_combine_slots, no grouping of the
                      slots (same outputs, bit for bit)
+        cpu_blobs    canonical host blobs [n_blobs, bytes] (numpy, rows as in
+                     host_store) for the host-core share of the misses
+        pcie_frac    decode with miss_mode "host" and by_slot: the share of a
+                     layer's missed experts the GPU reads over the host link;
+                     the others are computed on host cores (1.0: all on the GPU)
+        cpu_threads  host threads for that share (default: up to 16)
         """
         self.by_slot = by_slot
         assert miss_mode in ("stage", "host")
@@ -96,10 +112,31 @@ class ExpertStack:
                 self.cache.map_host(l, self.host_ptrs[l], self.tables[l])
         torch.cuda.synchronize()
         self.usage = None  # [L, E] int32 selection counters once enable_usage() is called
+        self.resident_mask = np.zeros((self.L, self.E), dtype=bool)
+        if resident_ids:
+            g = np.asarray(resident_ids, dtype=np.int64)
+            self.resident_mask[g // self.E, g % self.E] = True
+        self.cpu_blobs = None if cpu_blobs is None else np.ascontiguousarray(cpu_blobs, dtype=np.uint8)
+        self.cpu_pool = None
+        self.pcie_frac = 1.0
+        self.cpu_items = 0        # host-computed (token, slot) items since the last reset
+        self.cpu_experts = 0      # host-computed distinct experts since the last reset
+        self.set_pcie_frac(pcie_frac, cpu_threads)
         self.side = torch.cuda.Stream(device=self.device)
         self.staged = [torch.cuda.Event() for _ in range(self.L)]
         self.done = [torch.cuda.Event() for _ in range(self.L)]
         self._alloc(max_T)
+
+    def set_pcie_frac(self, frac, cpu_threads=None):
+        """Share of each decode layer's missed experts read by the GPU (the rest on host cores)."""
+        frac = float(frac)
+        assert 0.0 <= frac <= 1.0
+        if frac < 1.0:
+            assert self.miss_mode == "host" and self.by_slot and self.cpu_blobs is not None
+            assert self.cpu_blobs.shape[1] == self.eb
+            if self.cpu_pool is None:
+                self.cpu_pool = B.HostPool(cpu_threads or max(1, min(16, os.cpu_count() or 1)))
+        self.pcie_frac = frac
 
     def _alloc(self, T):
         dev, d, f, E, k = self.device, self.d, self.f, self.E, self.k
@@ -120,6 +157,18 @@ class ExpertStack:
         self.hbuf = [torch.empty((T, d), dtype=torch.float32, device=dev) for _ in range(2)]
         self.xn = torch.empty((T, d), dtype=torch.float32, device=dev)
         self.ws = torch.empty(B.moe_workspace_size(T, d, f, E, k, self.act_mode), dtype=torch.uint8, device=dev)
+        # host share of the misses: pinned staging of ids, gates and inputs, the host
+        # results, and the one-row combine that adds them
+        self.h_ids = torch.empty((T, k), dtype=torch.int32, pin_memory=True)
+        self.h_gates = torch.empty((T, k), dtype=torch.float32, pin_memory=True)
+        self.h_x = torch.empty((T, d), dtype=torch.float32, pin_memory=True)
+        self.h_gpu_ids = torch.empty((T, k), dtype=torch.int32, pin_memory=True)
+        self.h_cpu_out = torch.empty((T, d), dtype=torch.float32, pin_memory=True)
+        self.gpu_ids = torch.empty((T, k), **i32)
+        self.cpu_out = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.row_dest = torch.arange(T, dtype=torch.int32, device=dev)
+        self.row_gate = torch.ones((T, 1), dtype=torch.float32, device=dev)
+        self.routed_ev = torch.cuda.Event()
 
     def enable_usage(self):
         """Count, per layer and expert, how often the routing selects it (device int32)."""
@@ -141,7 +190,10 @@ class ExpertStack:
         xn = self.xn[:T]
         B.moe_rmsnorm(h, xn, self.eps, stream)
         bias = None if self.bias is None else self.bias[l]
-        if self.by_slot and self.usage is None and self.act_mode == B.MOE_ACT_FLOAT and self.wfmt == 4 and T <= 8:
+        decode = self.by_slot and self.usage is None and self.act_mode == B.MOE_ACT_FLOAT and self.wfmt == 4 and T <= 8
+        if decode and self.pcie_frac < 1.0 and table is None:
+            return self._layer_split(l, h, out, xn, bias, stream)
+        if decode:
             B.moe_route_ffn_combine_slots(T=T, d=self.d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
                                           expert_ptrs=self.tables[l] if table is None else table, ws=self.ws,
                                           Wr=self.Wr[l], bias=bias, ids=self.ids[:T], gates=self.gates[:T], out=out,
@@ -165,6 +217,50 @@ class ExpertStack:
             common.update(x=xn)
         B.moe_expert_ffn_combine(ids=self.ids[:T], dest=self.dest[:n], gates=self.gates[:T], residual=h, out=out,
                                  **common)
+
+    def _layer_split(self, l, h, out, xn, bias, stream):
+        """Decode layer with the host-core share of the misses (see set_pcie_frac)."""
+        T, k, E, d = h.shape[0], self.k, self.E, self.d
+        B.moe_route(xn, self.Wr[l], bias, k, self.ids[:T], self.gates[:T], self.ws, stream)
+        st = torch.cuda.current_stream(self.device) if stream is None else stream
+        with torch.cuda.stream(st):
+            self.h_ids[:T].copy_(self.ids[:T], non_blocking=True)
+            self.h_gates[:T].copy_(self.gates[:T], non_blocking=True)
+            self.h_x[:T].copy_(xn, non_blocking=True)
+            self.routed_ev.record(st)
+        self.routed_ev.synchronize()
+        ids = self.h_ids[:T].numpy()
+        miss = ~self.resident_mask[l][ids]
+        if miss.any():
+            me, cnt = np.unique(ids[miss], return_counts=True)
+            order = np.lexsort((me, -cnt))  # GPU share: experts picked by most tokens first, then lower id
+            n_gpu = int(round(self.pcie_frac * len(me)))
+            cpu_set = np.zeros(E, dtype=bool)
+            cpu_set[me[order[n_gpu:]]] = True
+        else:
+            cpu_set = np.zeros(E, dtype=bool)
+        on_cpu = cpu_set[ids]
+        gid = self.h_gpu_ids[:T].numpy()
+        gid[...] = np.where(on_cpu, -1, ids)  # ids outside [0, E) are skipped by the FFN
+        common = dict(T=T, d=d, f=self.f, E=E, k=k, wfmt=self.wfmt, act_mode=self.act_mode,
+                      expert_ptrs=self.tables[l], ws=self.ws,
+                      shared_blob=None if self.shared is None else self.shared[l], x=xn, stream=stream)
+        with torch.cuda.stream(st):
+            self.gpu_ids[:T].copy_(self.h_gpu_ids[:T], non_blocking=True)
+        B.moe_expert_ffn_combine_slots(ids=self.gpu_ids[:T], gates=self.gates[:T], residual=h, out=out, **common)
+        if not on_cpu.any():
+            return
+        tt, jj = np.nonzero(on_cpu)
+        ptrs = self.cpu_blobs.ctypes.data + self.eb * self.host_index[l, ids[tt, jj]]
+        hout = self.h_cpu_out[:T].numpy()
+        hout[...] = 0.0
+        self.cpu_pool.expert_ffn(tt, self.h_gates[:T].numpy()[tt, jj], ptrs, self.wfmt, self.h_x[:T].numpy(), hout,
+                                 d, self.f)
+        self.cpu_items += len(tt)
+        self.cpu_experts += int(cpu_set.sum())
+        with torch.cuda.stream(st):
+            self.cpu_out[:T].copy_(self.h_cpu_out[:T], non_blocking=True)
+        B.moe_combine(self.cpu_out[:T], self.row_dest[:T], self.row_gate[:T], None, out, out, stream)
 
     def forward(self, x: torch.Tensor, keep=(), copy_only=False, compute_only_tables=None, ids_out=None):
         """Run all layers on x ([T, d] fp32).  Returns (h_L, {l: (h_l, norm(h_l)) for l in keep}).
@@ -215,6 +311,9 @@ class ExpertStack:
 
     def close(self):
         self.cache.close()
+        if self.cpu_pool is not None:
+            self.cpu_pool.close()
+            self.cpu_pool = None
 
 
 class AdaptiveResidency:

@@ -230,6 +230,33 @@ def test_small_decode_stack_host_misses_teacher_forced(T, by_slot):
     G.close()
 
 
+@pytest.mark.parametrize("T,frac", [(4, 0.0), (4, 0.5), (1, 0.0)])
+def test_small_decode_stack_host_core_misses_teacher_forced(T, frac):
+    """Decode with a share (1 - pcie_frac) of each layer's missed experts
+    computed on host cores (moe_host_expert_ffn) and added on the GPU: every
+    layer teacher-forced against the oracle (ids bit-exact, outputs within the
+    float tolerance), and host items were computed."""
+    S = synth.make_stack(name="decode_stack", overrides=DSMALL, T=T)
+    c = S.cfg
+    store = build_host_store(S.pool, c.wfmt, c.d, c.f)
+    G = ExpertStack(S.routers, S.shared_blobs() if c.has_shared else None, store, S.index, S.resident,
+                    d=c.d, f=c.f, k=c.k, wfmt=c.wfmt, act_mode=B.MOE_ACT_FLOAT, max_T=c.T, biases=S.biases,
+                    miss_mode="host", by_slot=True, cpu_blobs=S.pool, pcie_frac=frac, cpu_threads=4)
+    x = _x0(S)
+    ids_l = []
+    hL, kept = G.forward(x, keep=range(c.n_layers), ids_out=ids_l)
+    torch.cuda.synchronize()
+    hs = [kept[l][0].cpu().numpy() for l in range(c.n_layers)] + [hL.cpu().numpy()]
+    for l in range(c.n_layers):
+        o = _check_decode_layer(S, l, hs[l], kept[l][1].cpu().numpy())
+        assert np.array_equal(ids_l[l].cpu().numpy(), o["ids"]), "layer %d ids" % l
+        ok, rel, mx = R.within_tolerance(hs[l + 1], o["out"])
+        print("[split] T=%d frac=%.2f layer %d: rel-L2 %.3e max-abs/RMS %.3e" % (T, frac, l, rel, mx), flush=True)
+        assert ok, "layer %d: rel %.3e max %.3e" % (l, rel, mx)
+    assert G.cpu_items > 0
+    G.close()
+
+
 def test_small_decode_stack_by_slot_equals_grouped_bitexact():
     """The 4-layer decode stack by slot (no grouping) gives every layer's output
     bit for bit as the grouped path."""
