@@ -396,6 +396,22 @@ int moe_cache_lookup(const moe_cache* cache, int layer, int32_t* hit_ids, int* n
                      int* n_miss);
 
 /*
+ * How moe_cache_stage copies a layer's missed experts into its staging slots
+ * ("Strata benchmarks", prefill optimisation table: the next layer's experts
+ * are streamed over PCIe while the current layer computes):
+ *   MOE_STAGE_MEMCPY (default): one hipMemcpyAsync per missed expert;
+ *   MOE_STAGE_KERNEL: one copy kernel of n_workgroups workgroups (1..1024)
+ *     that reads the missed blobs from mapped pinned host memory, so the host
+ *     enqueues one launch per layer instead of one copy per expert.  The
+ *     (source, destination) list lives in pinned memory the handle owns.
+ *     Needs expert_bytes % 16 == 0.
+ * Errors: MOE_ERR_INVALID_ARG.
+ */
+#define MOE_STAGE_MEMCPY 0
+#define MOE_STAGE_KERNEL 1
+int moe_cache_set_stage_mode(moe_cache* cache, int mode, int n_workgroups);
+
+/*
  * Stage one layer: copy each missing expert of `layer` (ascending id) from its
  * host blob host_src[e] (host array [E] of pinned host pointers; only the
  * misses are read) into consecutive slots of staging buffer `buf`, then write

@@ -33,9 +33,12 @@ EXPORTED = [
     "moe_route_ffn_combine_slots_noalloc", "moe_host_pool_create", "moe_host_pool_destroy", "moe_host_expert_ffn",
     "moe_rmsnorm",
     "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
-    "moe_cache_stage", "moe_cache_map_host", "moe_usage_accumulate", "moe_cache_plan", "moe_cache_replace",
+    "moe_cache_stage", "moe_cache_set_stage_mode", "moe_cache_map_host", "moe_usage_accumulate", "moe_cache_plan", "moe_cache_replace",
 ]
 
+
+MOE_STAGE_MEMCPY = 0
+MOE_STAGE_KERNEL = 1
 
 # device scratch of moe_route_ffn_combine_slots_noalloc (include/moe.h)
 MOE_NOALLOC_SCRATCH_BYTES = 2 << 20
@@ -99,6 +102,7 @@ def lib():
             "moe_cache_set_resident": ([P, P, I, P, P], I),
             "moe_cache_lookup": ([P, I, P, C.POINTER(I), P, C.POINTER(I)], I),
             "moe_cache_stage": ([P, I, I, P, P, P, P], I),
+            "moe_cache_set_stage_mode": ([P, I, I], I),
             "moe_cache_map_host": ([P, I, P, P, P, P], I),
             "moe_usage_accumulate": ([P, P, I, P], I),
             "moe_cache_plan": ([I, P, P, I, C.c_float, P, P, C.POINTER(I)], I),
@@ -316,6 +320,9 @@ class SlotCache:
         nh, nm = C.c_int(), C.c_int()
         _check("moe_cache_lookup", lib().moe_cache_lookup(self.h, layer, hit, C.byref(nh), miss, C.byref(nm)))
         return list(hit[:nh.value]), list(miss[:nm.value])
+
+    def set_stage_mode(self, mode, n_workgroups=32):
+        _check("moe_cache_set_stage_mode", lib().moe_cache_set_stage_mode(self.h, int(mode), int(n_workgroups)))
 
     def stage(self, layer, buf, host_ptrs, dev_table, stream=None, done_event=None):
         """Stage one layer on `stream`; done_event (a torch.cuda.Event) is recorded after it.

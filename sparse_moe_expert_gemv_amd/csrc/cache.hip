@@ -23,6 +23,9 @@ struct moe_cache {
     std::vector<hipEvent_t> table_done;  // per layer: last upload of its table
     std::vector<bool> table_pending;
     std::vector<bool> table_written;     // the pinned table of the layer holds a full mapping
+    int stage_mode = MOE_STAGE_MEMCPY;   // how moe_cache_stage copies the misses
+    int copy_workgroups = 32;            // MOE_STAGE_KERNEL: workgroups of the copy kernel
+    uint64_t* copy_list = nullptr;       // pinned host [n_layers][2 * E] (source, destination) device addresses
 };
 
 using namespace moe;
@@ -32,6 +35,35 @@ __global__ __launch_bounds__(256) static void usage_accumulate(int32_t* __restri
                                                               const int32_t* __restrict__ counts, int E) {
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e < E) usage[e] = (int32_t)((uint32_t)usage[e] + (uint32_t)counts[e]);
+}
+
+// Copies the n missed experts of a layer (eb = 16 n16 bytes each) from mapped
+// pinned host memory into the staging slots: list holds their (source,
+// destination) device addresses and is read once into LDS; every workgroup
+// copies its slice of every expert with 16-byte non-temporal loads, four in
+// flight per thread.  One launch per layer instead of one copy call per expert.
+__global__ __launch_bounds__(256) static void stage_copy(const uint64_t* __restrict__ list, int n, uint32_t n16) {
+    __shared__ uint64_t s_list[2 * 1024];
+    for (int i = threadIdx.x; i < 2 * n; i += 256) s_list[i] = list[i];
+    __syncthreads();
+    const uint32_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const uint32_t c0 = blockIdx.x * per, c1 = min(n16, c0 + per);
+    for (int i = 0; i < n; ++i) {
+        const uint4v* __restrict__ src = reinterpret_cast<const uint4v*>(s_list[2 * i]);
+        uint4v* __restrict__ dst = reinterpret_cast<uint4v*>(s_list[2 * i + 1]);
+        uint32_t c = c0 + threadIdx.x;
+        for (; c + 3 * 256 < c1; c += 4 * 256) {
+            const uint4v v0 = __builtin_nontemporal_load(src + c);
+            const uint4v v1 = __builtin_nontemporal_load(src + c + 256);
+            const uint4v v2 = __builtin_nontemporal_load(src + c + 512);
+            const uint4v v3 = __builtin_nontemporal_load(src + c + 768);
+            dst[c] = v0;
+            dst[c + 256] = v1;
+            dst[c + 512] = v2;
+            dst[c + 768] = v3;
+        }
+        for (; c < c1; c += 256) dst[c] = __builtin_nontemporal_load(src + c);
+    }
 }
 
 static int hip_fail(hipError_t e) {
@@ -56,6 +88,10 @@ int moe_cache_create(moe_cache** cache, int n_layers, int E, int n_slots, size_t
     c->tables = nullptr;
     hipError_t e = hipHostMalloc((void**)&c->tables, sizeof(void*) * (size_t)n_layers * E, hipHostMallocDefault);
     if (e != hipSuccess) { delete c; return hip_fail(e); }
+    if (staging_slots > 0) {
+        e = hipHostMalloc((void**)&c->copy_list, sizeof(uint64_t) * 2 * (size_t)n_layers * E, hipHostMallocDefault);
+        if (e != hipSuccess) { (void)hipHostFree(c->tables); delete c; return hip_fail(e); }
+    }
     c->table_done.assign(n_layers, nullptr);
     c->table_pending.assign(n_layers, false);
     c->table_written.assign(n_layers, false);
@@ -75,7 +111,17 @@ int moe_cache_destroy(moe_cache* c) {
             (void)hipEventDestroy(ev);
         }
     if (c->tables) (void)hipHostFree(c->tables);
+    if (c->copy_list) (void)hipHostFree(c->copy_list);
     delete c;
+    return MOE_OK;
+}
+
+int moe_cache_set_stage_mode(moe_cache* c, int mode, int n_workgroups) {
+    if (!c || (mode != MOE_STAGE_MEMCPY && mode != MOE_STAGE_KERNEL)) return MOE_ERR_INVALID_ARG;
+    if (mode == MOE_STAGE_KERNEL && (n_workgroups < 1 || n_workgroups > 1024 || c->eb % 16 || c->eb / 16 > 0xFFFFFFFFu))
+        return MOE_ERR_INVALID_ARG;
+    c->stage_mode = mode;
+    if (mode == MOE_STAGE_KERNEL) c->copy_workgroups = n_workgroups;
     return MOE_OK;
 }
 
@@ -134,6 +180,8 @@ int moe_cache_stage(moe_cache* c, int layer, int buf, const void* const* host_sr
     void** table = c->tables + (size_t)layer * c->E;
     char* stage = c->staging + (size_t)buf * c->staging_slots * c->eb;
     const hipStream_t st = as_stream(s);
+    const bool kernel = c->stage_mode == MOE_STAGE_KERNEL;
+    uint64_t* list = kernel ? c->copy_list + 2 * (size_t)layer * c->E : nullptr;  // guarded by table_done too
     int i = 0;
     for (int e = 0; e < c->E; ++e) {
         const int slot = c->slot_of[(size_t)layer * c->E + e];
@@ -141,13 +189,30 @@ int moe_cache_stage(moe_cache* c, int layer, int buf, const void* const* host_sr
             table[e] = c->pool + (size_t)slot * c->eb;
         } else {
             char* dst = stage + (size_t)i * c->eb;
-            const hipError_t err = hipMemcpyAsync(dst, host_src[e], c->eb, hipMemcpyHostToDevice, st);
-            if (err != hipSuccess) return hip_fail(err);
+            if (kernel) {
+                void* src = nullptr;
+                const hipError_t err = hipHostGetDevicePointer(&src, const_cast<void*>(host_src[e]), 0);
+                if (err != hipSuccess) return hip_fail(err);
+                list[2 * i] = (uint64_t)(uintptr_t)src;
+                list[2 * i + 1] = (uint64_t)(uintptr_t)dst;
+            } else {
+                const hipError_t err = hipMemcpyAsync(dst, host_src[e], c->eb, hipMemcpyHostToDevice, st);
+                if (err != hipSuccess) return hip_fail(err);
+            }
             table[e] = dst;
             ++i;
         }
     }
-    hipError_t err = hipMemcpyAsync(dev_table, table, sizeof(void*) * (size_t)c->E, hipMemcpyHostToDevice, st);
+    hipError_t err;
+    if (kernel && i > 0) {
+        void* dlist = nullptr;
+        err = hipHostGetDevicePointer(&dlist, list, 0);
+        if (err != hipSuccess) return hip_fail(err);
+        stage_copy<<<c->copy_workgroups, 256, 0, st>>>(static_cast<const uint64_t*>(dlist), i, (uint32_t)(c->eb / 16));
+        const int rc = check_launch();
+        if (rc) return rc;
+    }
+    err = hipMemcpyAsync(dev_table, table, sizeof(void*) * (size_t)c->E, hipMemcpyHostToDevice, st);
     if (err != hipSuccess) return hip_fail(err);
     err = hipEventRecord(c->table_done[layer], st);
     if (err != hipSuccess) return hip_fail(err);

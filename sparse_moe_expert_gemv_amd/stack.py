@@ -53,7 +53,8 @@ from .layer import pack_blobs
 class ExpertStack:
     def __init__(self, routers, shared_blobs, host_store: torch.Tensor, host_index: np.ndarray, resident_ids,
                  *, d, f, k, wfmt, act_mode, max_T, staging_slots=None, device="cuda", eps=1e-6,
-                 biases=None, miss_mode="stage", by_slot=False, cpu_blobs=None, pcie_frac=1.0, cpu_threads=None):
+                 biases=None, miss_mode="stage", by_slot=False, cpu_blobs=None, pcie_frac=1.0, cpu_threads=None,
+                 stage_mode="kernel", stage_workgroups=32):
         """
         routers      list of L fp32 arrays [E, d]
         shared_blobs [L, bytes] canonical uint8 (numpy) or None
@@ -72,6 +73,9 @@ class ExpertStack:
                      layer's missed experts the GPU reads over the host link;
                      the others are computed on host cores (1.0: all on the GPU)
         cpu_threads  host threads for that share (default: up to 16)
+        stage_mode   "kernel": one copy kernel per staged layer reading the
+                     pinned host blobs (stage_workgroups workgroups);
+                     "memcpy": one hipMemcpyAsync per missed expert
         """
         self.by_slot = by_slot
         assert miss_mode in ("stage", "host")
@@ -107,6 +111,10 @@ class ExpertStack:
         self.cache = B.SlotCache(self.L, self.E, self.n_slots, self.eb, self.pool, self.staging, 2,
                                  self.staging_slots)
         self.cache.set_resident(resident_ids, [self.host_ptrs[g // self.E][g % self.E] for g in resident_ids])
+        assert stage_mode in ("kernel", "memcpy")
+        self.stage_mode = stage_mode
+        if stage_mode == "kernel":
+            self.cache.set_stage_mode(B.MOE_STAGE_KERNEL, stage_workgroups)
         if miss_mode == "host":
             for l in range(self.L):
                 self.cache.map_host(l, self.host_ptrs[l], self.tables[l])
