@@ -25,6 +25,15 @@
 
 #include "moe.h"
 
+// Per-CPU clones of the row kernels (dispatched through ifunc resolvers).  A
+// ThreadSanitizer build has none: its runtime is not initialised yet when the
+// resolvers run.
+#if defined(__SANITIZE_THREAD__)
+#define MOE_HOST_ISA_CLONES
+#else
+#define MOE_HOST_ISA_CLONES __attribute__((target_clones("avx512f", "avx2", "default")))
+#endif
+
 namespace {
 
 // ---- thread pool -------------------------------------------------------------
@@ -153,7 +162,7 @@ const float* half_table() {
 // 8 sum x.  Sixteen (int4) or thirty-two (int8) lane accumulators over the
 // row, added in a fixed tree at the end (so the compiler may vectorise the
 // lanes without reordering any sum).
-__attribute__((target_clones("avx512f", "avx2", "default")))
+MOE_HOST_ISA_CLONES
 float row_dot_i4(const uint8_t* __restrict q, const uint16_t* __restrict sc, const float* __restrict xe,
                  const float* __restrict xo, const float* __restrict xsum, const float* __restrict lut, int K) {
     float acc[16] = {};
@@ -171,7 +180,7 @@ float row_dot_i4(const uint8_t* __restrict q, const uint16_t* __restrict sc, con
     return acc[0] - 8.f * corr;
 }
 
-__attribute__((target_clones("avx512f", "avx2", "default")))
+MOE_HOST_ISA_CLONES
 float row_dot_i8(const int8_t* __restrict q, const uint16_t* __restrict sc, const float* __restrict x,
                  const float* __restrict lut, int K) {
     float acc[32] = {};
