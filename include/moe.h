@@ -412,6 +412,22 @@ int moe_cache_lookup(const moe_cache* cache, int layer, int32_t* hit_ids, int* n
 int moe_cache_set_stage_mode(moe_cache* cache, int mode, int n_workgroups);
 
 /*
+ * Fault injection into staging, for tests of a caller's error handling (no
+ * passage defines it; production code installs no hook).  With a hook set,
+ * moe_cache_stage calls hook(user, layer, index, expert) on the host before
+ * it enqueues the copy of the index-th missed expert (local id `expert`) of
+ * `layer`.  A nonzero return value v stops that call: it returns MOE_ERR_HIP
+ * and moe_last_hip_error() reports v.  Copies enqueued before the failure may
+ * still land in staging buffer `buf`, and the device table of the layer is
+ * not uploaded, so until a later moe_cache_stage of the same layer into the
+ * same buffer succeeds, neither that table nor that buffer may be read.
+ * Residency and the other layers' tables are unaffected.  hook NULL removes
+ * the hook.  Errors: MOE_ERR_INVALID_ARG (cache NULL).
+ */
+typedef int (*moe_stage_fault_fn)(void* user, int layer, int index, int expert);
+int moe_cache_set_stage_fault_hook(moe_cache* cache, moe_stage_fault_fn hook, void* user);
+
+/*
  * Stage one layer: copy each missing expert of `layer` (ascending id) from its
  * host blob host_src[e] (host array [E] of pinned host pointers; only the
  * misses are read) into consecutive slots of staging buffer `buf`, then write

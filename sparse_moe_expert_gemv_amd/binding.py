@@ -33,12 +33,15 @@ EXPORTED = [
     "moe_route_ffn_combine_slots_noalloc", "moe_host_pool_create", "moe_host_pool_destroy", "moe_host_expert_ffn",
     "moe_rmsnorm",
     "moe_combine", "moe_cache_create", "moe_cache_destroy", "moe_cache_set_resident", "moe_cache_lookup",
-    "moe_cache_stage", "moe_cache_set_stage_mode", "moe_cache_map_host", "moe_usage_accumulate", "moe_cache_plan", "moe_cache_replace",
+    "moe_cache_stage", "moe_cache_set_stage_mode", "moe_cache_set_stage_fault_hook", "moe_cache_map_host", "moe_usage_accumulate", "moe_cache_plan", "moe_cache_replace",
 ]
 
 
 MOE_STAGE_MEMCPY = 0
 MOE_STAGE_KERNEL = 1
+
+# int hook(void* user, int layer, int index, int expert): nonzero fails the staging call
+STAGE_FAULT_FN = C.CFUNCTYPE(C.c_int, C.c_void_p, C.c_int, C.c_int, C.c_int)
 
 # device scratch of moe_route_ffn_combine_slots_noalloc (include/moe.h)
 MOE_NOALLOC_SCRATCH_BYTES = 2 << 20
@@ -103,6 +106,7 @@ def lib():
             "moe_cache_lookup": ([P, I, P, C.POINTER(I), P, C.POINTER(I)], I),
             "moe_cache_stage": ([P, I, I, P, P, P, P], I),
             "moe_cache_set_stage_mode": ([P, I, I], I),
+            "moe_cache_set_stage_fault_hook": ([P, STAGE_FAULT_FN, P], I),
             "moe_cache_map_host": ([P, I, P, P, P, P], I),
             "moe_usage_accumulate": ([P, P, I, P], I),
             "moe_cache_plan": ([I, P, P, I, C.c_float, P, P, C.POINTER(I)], I),
@@ -323,6 +327,16 @@ class SlotCache:
 
     def set_stage_mode(self, mode, n_workgroups=32):
         _check("moe_cache_set_stage_mode", lib().moe_cache_set_stage_mode(self.h, int(mode), int(n_workgroups)))
+
+    def set_stage_fault_hook(self, fn):
+        """Install fn(layer, index, expert) -> int, called before each staging copy
+        (a nonzero result fails that stage call with that value); None removes it."""
+        if fn is None:
+            cb = STAGE_FAULT_FN()
+        else:
+            cb = STAGE_FAULT_FN(lambda _user, layer, index, expert: int(fn(layer, index, expert)))
+        _check("moe_cache_set_stage_fault_hook", lib().moe_cache_set_stage_fault_hook(self.h, cb, None))
+        self._fault_cb = cb  # the library keeps the pointer: keep the thunk alive
 
     def stage(self, layer, buf, host_ptrs, dev_table, stream=None, done_event=None):
         """Stage one layer on `stream`; done_event (a torch.cuda.Event) is recorded after it.

@@ -26,6 +26,8 @@ struct moe_cache {
     int stage_mode = MOE_STAGE_MEMCPY;   // how moe_cache_stage copies the misses
     int copy_workgroups = 32;            // MOE_STAGE_KERNEL: workgroups of the copy kernel
     uint64_t* copy_list = nullptr;       // pinned host [n_layers][2 * E] (source, destination) device addresses
+    moe_stage_fault_fn fault = nullptr;  // test hook consulted before each staging copy
+    void* fault_user = nullptr;
 };
 
 using namespace moe;
@@ -125,6 +127,13 @@ int moe_cache_set_stage_mode(moe_cache* c, int mode, int n_workgroups) {
     return MOE_OK;
 }
 
+int moe_cache_set_stage_fault_hook(moe_cache* c, moe_stage_fault_fn hook, void* user) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    c->fault = hook;
+    c->fault_user = hook ? user : nullptr;
+    return MOE_OK;
+}
+
 int moe_cache_set_resident(moe_cache* c, const int32_t* ids, int n, const void* const* host_src, moe_stream_t s) {
     if (!c || n < 0 || n > c->n_slots || (n > 0 && (!ids || !host_src))) return MOE_ERR_INVALID_ARG;
     const long total = (long)c->n_layers * c->E;
@@ -182,6 +191,12 @@ int moe_cache_stage(moe_cache* c, int layer, int buf, const void* const* host_sr
     const hipStream_t st = as_stream(s);
     const bool kernel = c->stage_mode == MOE_STAGE_KERNEL;
     uint64_t* list = kernel ? c->copy_list + 2 * (size_t)layer * c->E : nullptr;  // guarded by table_done too
+    // from here on the pinned table is being rewritten: a failure leaves it
+    // holding a partial mapping that moe_cache_replace must not upload
+    auto fail = [&](hipError_t e) {
+        c->table_written[layer] = false;
+        return hip_fail(e);
+    };
     int i = 0;
     for (int e = 0; e < c->E; ++e) {
         const int slot = c->slot_of[(size_t)layer * c->E + e];
@@ -189,15 +204,19 @@ int moe_cache_stage(moe_cache* c, int layer, int buf, const void* const* host_sr
             table[e] = c->pool + (size_t)slot * c->eb;
         } else {
             char* dst = stage + (size_t)i * c->eb;
+            if (c->fault) {
+                const int injected = c->fault(c->fault_user, layer, i, e);
+                if (injected != 0) return fail(static_cast<hipError_t>(injected));
+            }
             if (kernel) {
                 void* src = nullptr;
                 const hipError_t err = hipHostGetDevicePointer(&src, const_cast<void*>(host_src[e]), 0);
-                if (err != hipSuccess) return hip_fail(err);
+                if (err != hipSuccess) return fail(err);
                 list[2 * i] = (uint64_t)(uintptr_t)src;
                 list[2 * i + 1] = (uint64_t)(uintptr_t)dst;
             } else {
                 const hipError_t err = hipMemcpyAsync(dst, host_src[e], c->eb, hipMemcpyHostToDevice, st);
-                if (err != hipSuccess) return hip_fail(err);
+                if (err != hipSuccess) return fail(err);
             }
             table[e] = dst;
             ++i;
@@ -207,15 +226,18 @@ int moe_cache_stage(moe_cache* c, int layer, int buf, const void* const* host_sr
     if (kernel && i > 0) {
         void* dlist = nullptr;
         err = hipHostGetDevicePointer(&dlist, list, 0);
-        if (err != hipSuccess) return hip_fail(err);
+        if (err != hipSuccess) return fail(err);
         stage_copy<<<c->copy_workgroups, 256, 0, st>>>(static_cast<const uint64_t*>(dlist), i, (uint32_t)(c->eb / 16));
         const int rc = check_launch();
-        if (rc) return rc;
+        if (rc) {
+            c->table_written[layer] = false;
+            return rc;
+        }
     }
     err = hipMemcpyAsync(dev_table, table, sizeof(void*) * (size_t)c->E, hipMemcpyHostToDevice, st);
-    if (err != hipSuccess) return hip_fail(err);
+    if (err != hipSuccess) return fail(err);
     err = hipEventRecord(c->table_done[layer], st);
-    if (err != hipSuccess) return hip_fail(err);
+    if (err != hipSuccess) return fail(err);
     c->table_pending[layer] = true;
     c->table_written[layer] = true;
     if (done) {

@@ -128,6 +128,55 @@ def test_cache_capacity_error_when_staging_too_small():
     G.close()
 
 
+@pytest.mark.parametrize("stage_mode", ["memcpy", "kernel"])
+def test_injected_staging_failure_then_retry_bitexact(stage_mode):
+    """A staging copy forced to fail from the host (the cache's fault hook)
+    makes moe_cache_stage report MOE_ERR_HIP with the injected code; residency
+    and the other buffer's layer stay intact, and staging the layer again gives
+    the same output, bit for bit, as a run that never failed."""
+    S = synth.make_stack(overrides=SMALL)
+    c = S.cfg
+    store = build_host_store(S.pool, c.wfmt, c.d, c.f)
+    G = ExpertStack(S.routers, S.shared_blobs(), store, S.index, S.resident, d=c.d, f=c.f, k=c.k, wfmt=c.wfmt,
+                    act_mode=B.MOE_ACT_Q8, max_T=c.T, stage_mode=stage_mode)
+    x = _x0(S)
+    ref = [torch.empty_like(x) for _ in range(2)]
+    for l in range(2):
+        G.stage(l)
+        torch.cuda.current_stream().wait_event(G.staged[l])
+        G.layer(l, x, ref[l])
+    torch.cuda.synchronize()
+    hits_before = [G.cache.lookup(l)[0] for l in range(c.n_layers)]
+    miss1 = G.misses(1)
+    assert len(miss1) > 6
+    fail_at, injected = 5, 2  # hipErrorOutOfMemory
+    calls = []
+
+    def hook(layer, index, expert):
+        calls.append((layer, index, expert))
+        return injected if (layer == 1 and index == fail_at) else 0
+
+    G.cache.set_stage_fault_hook(hook)
+    with pytest.raises(B.MoeError) as ei:
+        G.stage(1)
+    assert ei.value.status == B.MOE_ERR_HIP and ei.value.hip_error == injected
+    assert calls == [(1, i, miss1[i]) for i in range(fail_at + 1)]
+    G.cache.set_stage_fault_hook(None)
+    torch.cuda.synchronize()
+    assert [G.cache.lookup(l)[0] for l in range(c.n_layers)] == hits_before
+    out = torch.empty_like(x)
+    # layer 0 lives in the other staging buffer: untouched by the failed call
+    G.layer(0, x, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref[0])
+    G.stage(1)
+    torch.cuda.current_stream().wait_event(G.staged[1])
+    G.layer(1, x, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref[1])
+    G.close()
+
+
 def test_full_stack_48_layers_sampled():
     """The 48-layer, 24,576-expert stack at T=8192 with 4,500 resident slots:
     on every layer, teacher-forced, the routing of all tokens (ids, counts,

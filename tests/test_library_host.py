@@ -198,3 +198,11 @@ def test_decode_stack_inputs_follow_the_profile():
         order = np.argsort(r)
         assert np.all(np.diff(b[order]) < 0)
         assert abs(float(b[order[0]]) - (-0.38 * 1.1 * np.log(r[order[0]] + 1.0))) < 1e-5
+
+
+def test_stage_fault_hook_rejects_null_cache():
+    """The staging fault hook is host bookkeeping only: a NULL cache is an
+    argument error, with or without a hook."""
+    L = B.lib()
+    assert L.moe_cache_set_stage_fault_hook(None, B.STAGE_FAULT_FN(lambda *a: 0), None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_cache_set_stage_fault_hook(None, B.STAGE_FAULT_FN(), None) == B.MOE_ERR_INVALID_ARG
