@@ -696,7 +696,8 @@ def bench_peak(a):
     rate of each matrix-core instruction the FFN kernels use, the plain fp32
     FMA rate of the vector unit, the rate of one int8 32x32x32 MFMA per block
     followed by the exact two-operation block-scale epilogue (and by a
-    one-operation one), and a non-temporal HBM read stream over 4 GiB.
+    one-operation one), a non-temporal HBM read stream over 4 GiB, and single
+    launches that read 10-70 MiB (the per-launch reads of the decode kernels).
     Workgroups of 256 threads; ``waves/SIMD`` = grid / 256 (one wavefront of
     each workgroup per SIMD).  Best rate over the grid sizes tried."""
     import ctypes
@@ -766,6 +767,39 @@ def bench_peak(a):
             best = (gbs, w, t)
     res["hbm_stream_read"] = {"rate": round(best[0], 1), "unit": "GB/s", "workgroups_per_cu": best[1],
                               "bytes": nbytes, "ms": round(best[2] * 1e3, 3)}
+    # short reads: one launch reads `size` bytes, the sizes the decode kernels
+    # read per launch; consecutive launches take consecutive windows of the
+    # 4 GiB buffer, so every launch reads cold data (not held in the 256 MB
+    # last-level cache); best over kernel shape and grid
+    short = {}
+    for size in (10 << 20, 20 << 20, 35 << 20, 70 << 20):
+        n_win = nbytes // size
+        best = None
+        for kind in (6, 8):
+            for w in (1, 2, 4, 8):
+                grid = n_cu * w
+                reps = 40
+
+                def launch(r):
+                    rc = lib.moe_probe_run(kind, grid, 0, 1, out.data_ptr(), buf.data_ptr() + (r % n_win) * size,
+                                           size, stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError("moe_probe_run(kind=%d) returned %d" % (kind, rc))
+                for r in range(reps):
+                    launch(r)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for r in range(reps):
+                    launch(reps + r)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1) / reps * 1e-3
+                if best is None or size / t > best[0]:
+                    best = (size / t / 1e9, "burst" if kind == 8 else "single", w, t)
+        short["%d_MiB" % (size >> 20)] = {"rate": round(best[0], 1), "unit": "GB/s", "us_per_launch":
+                                          round(best[3] * 1e6, 2), "kernel": best[1], "workgroups_per_cu": best[2]}
+    res["short_read_one_launch"] = short
     del buf
     print(json.dumps({"workload": "peak", "compute_units": n_cu, "datasheet": {
         "int8_mfma_TOPS": INT8_PEAK_TOPS, "f16_mfma_TFLOPS": 2500.0, "fp32_vector_TFLOPS": 157.3,

@@ -48,6 +48,8 @@ void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* bas
         w->h = take(float_h_bytes(T, f, k));
         w->hs = nullptr;
     }
+    w->slot_blob = act_mode == MOE_ACT_Q8 ? nullptr
+                                          : reinterpret_cast<const uint8_t**>(take(sizeof(void*) * (size_t)T * k));
     w->bytes = off;
 }
 

@@ -115,6 +115,8 @@ struct Workspace {
     int32_t* tiles;     // q8 tile list (int2) + count    ffn
     void* h;            // SwiGLU intermediate [T*k + T, f]: fp16 (float mode, q8 with int4 weights) or int8 (q8, int8 weights)
     float* hs;          // q8: [T*k + T, f/32] block scales of h
+    const uint8_t** slot_blob;  // float mode: [T*k] expert blob of each routed slot (by-slot decode;
+                                // written by the gate/up launch, read by the down + combine launch)
     size_t route_bytes, permute_bytes, bytes;
 };
 constexpr int kPermChunk = 1024;
@@ -145,8 +147,11 @@ int launch_quant_act(const void* x, int x_dtype, int T, int d, int8_t* xq, float
 // tokens): out = residual + shared + sum_j g_j y_j without y_perm
 constexpr int kDownCombineMax = 8;
 bool down_combine_ok(const moe_ffn_args* a);
+// slot_blob (by-slot batches, dest NULL): the routed slots' expert blobs as the
+// gate/up launch wrote them, read instead of expert_ptrs[ids]
 int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t* ids, const int32_t* dest,
-                        const float* gates, const float* residual, float* out, hipStream_t s);
+                        const float* gates, const float* residual, float* out, hipStream_t s,
+                        const uint8_t* const* slot_blob = nullptr);
 // decode without the grouping: gate/up per routed slot, then the fused down +
 // combine (h row of slot (t, j) = t k + j)
 bool ffn_combine_slots_ok(const moe_ffn_args* a);

@@ -466,7 +466,8 @@ template <> struct XChunk<_Float16> {
 // slot_ids[a], its one row written to h row a), slot T k the shared expert.
 // TOPK > 0 (with BY_SLOT): the slot's expert is selected here instead, by the
 // router's top-k of token a / k over the logits (TOPK values per lane); the
-// first wavefront ranks the token's logits and also writes its ids and gates.
+// first wavefront ranks the token's logits, and one workgroup per token
+// writes its ids and gates at the end.
 template <int NT, int S, typename XT, int NTH = 256, bool BY_SLOT = false, int TOPK = 0>
 __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x, int T, int d, int f, int k, int E,
                                                         const void* const* __restrict__ expert_ptrs,
@@ -477,8 +478,11 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
                                                         const int32_t* __restrict__ active, _Float16* __restrict__ h,
                                                         const int32_t* __restrict__ slot_ids,
                                                         const double* __restrict__ logits, int planes,
-                                                        int32_t* __restrict__ ids_out, float* __restrict__ gates_out) {
+                                                        int32_t* __restrict__ ids_out, float* __restrict__ gates_out,
+                                                        const uint8_t** __restrict__ slot_blob_out) {
     extern __shared__ __align__(16) uint4 xs4[];  // [T][d / 8] fp16, chunk c of row r at (c ^ r); later [4][2][4][64] f32
+    __shared__ RankScratch rs;       // TOPK: the selection of this workgroup's token
+    __shared__ int32_t s_sel[64];
     const int XC = d / 8;           // a power of two (checked by the launcher)
     const int lxc = __builtin_ctz(XC);
     const int lane = threadIdx.x & 63;
@@ -490,7 +494,10 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
     const int nx = T * XC;
     XChunk<XT> xr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xr[j].load(x + (size_t)min((int)threadIdx.x + j * NTH, nx - 1) * 8);
+    for (int j = 0; j < 4; ++j) {  // chunks past the end are not requested (no repeated address)
+        const int idx = (int)threadIdx.x + j * NTH;
+        if (idx < nx) xr[j].load(x + (size_t)idx * 8);
+    }
     const uint8_t* blob;
     int e, c, p0, slot_of;
     if constexpr (BY_SLOT) {
@@ -498,12 +505,8 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
         const bool routed = a < n_slots;
         int e_raw;
         if constexpr (TOPK > 0) {
-            __shared__ RankScratch rs;
-            __shared__ int32_t s_sel[64];
             const int ts = min(a, n_slots - 1) / k;
-            if (wave == 0)
-                topk_rank<TOPK>(logits + (size_t)ts * E, E, k, ids_out + (size_t)ts * k, gates_out + (size_t)ts * k,
-                                s_sel, rs, planes, (size_t)T * E);
+            if (wave == 0) topk_select<TOPK>(logits + (size_t)ts * E, E, k, s_sel, rs, planes, (size_t)T * E);
             __syncthreads();
             e_raw = s_sel[min(a, n_slots - 1) - ts * k];
         } else {
@@ -516,6 +519,9 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
         c = routed ? 1 : T;
         p0 = routed ? a : n_slots;
         slot_of = a;  // the slot's single row belongs to token a / k
+        // the slot's blob for the down projection, which then needs no lookup of
+        // its own (one vector store per slot)
+        if (slot_blob_out && routed && strip == 0 && part == 0 && lane == 0) slot_blob_out[a] = blob;
     } else {
         const int n_active = active[0];
         const int e_raw = active[1 + min(a, E - 1)];
@@ -562,7 +568,10 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
     for (int base = 4 * NTH; base < nx; base += 4 * NTH) {
         XChunk<XT> xq[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xq[j].load(x + (size_t)min(base + (int)threadIdx.x + j * NTH, nx - 1) * 8);
+        for (int j = 0; j < 4; ++j) {
+            const int idx = base + (int)threadIdx.x + j * NTH;
+            if (idx < nx) xq[j].load(x + (size_t)idx * 8);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int idx = base + (int)threadIdx.x + j * NTH;
@@ -619,6 +628,15 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
         red[wave][1][r][lane] = accu[r];
     }
     __syncthreads();
+    if constexpr (TOPK > 0) {
+        // ids and gates of the token (the softmax over the selected logits),
+        // written once, by the workgroup of its first slot's first strip, and
+        // only after every load of this workgroup: the selection alone gates
+        // the weight loads
+        const int n_slots = T * k;
+        if (wave == 0 && a < n_slots && a % k == 0 && strip == 0)
+            topk_gates(rs, k, ids_out + (size_t)(a / k) * k, gates_out + (size_t)(a / k) * k);
+    }
     if (!work) return;
     const int w0 = wave - part;
     const int col = strip * 16 + (lane & 15);
@@ -652,7 +670,8 @@ __global__ __launch_bounds__(NTH) void ffn_gateup_tok16(const XT* __restrict__ x
 template <typename XT, bool BY_SLOT = false, int TOPK = 0>
 static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, hipStream_t s,
                                 const int32_t* slot_ids = nullptr, const double* logits = nullptr, int planes = 1,
-                                int32_t* ids_out = nullptr, float* gates_out = nullptr) {
+                                int32_t* ids_out = nullptr, float* gates_out = nullptr,
+                                const uint8_t** slot_blob = nullptr) {
     const int nkt = a->d / 128;
     const int items = slots * (a->f / 16);
     // few items (a single token routes to k + 1 slots): four wavefronts per
@@ -663,7 +682,7 @@ static bool launch_gateup_tok16(const moe_ffn_args* a, _Float16* h, int slots, h
 #define MOE_GU16(NT, S)                                                                                         \
     ffn_gateup_tok16<NT, S, XT, S == 2 ? 512 : 256, BY_SLOT, TOPK><<<grid, S == 2 ? 512 : 256, lds, s>>>(        \
         (const XT*)a->x, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->counts, \
-        a->offsets, a->sorted_idx, a->active, h, slot_ids, logits, planes, ids_out, gates_out)
+        a->offsets, a->sorted_idx, a->active, h, slot_ids, logits, planes, ids_out, gates_out, slot_blob)
     if (four) {
         switch (nkt) {
         case 8: MOE_GU16(2, 4); return true;
@@ -846,7 +865,7 @@ __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __re
                                                             const int32_t* __restrict__ ids,
                                                             const int32_t* __restrict__ dest,
                                                             const float* __restrict__ gates, const float* residual,
-                                                            float* out) {
+                                                            float* out, const uint8_t* const* __restrict__ slot_blob) {
     extern __shared__ __align__(16) uint4 hrow[];  // [nj][f / 8]
     __shared__ const uint8_t* s_blob[kDcMaxSlots];  // nullptr: the slot is ignored
     __shared__ int32_t s_p[kDcMaxSlots];
@@ -858,7 +877,11 @@ __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __re
     const int nj = k + (shared_blob ? 1 : 0);
     const int HC = f / 8;
     for (int j = threadIdx.x; j < nj; j += 64 * NW) {
-        if (j < k) {
+        if (j < k && slot_blob) {  // by slot: the blob the gate/up launch used (nullptr: ignored)
+            s_blob[j] = slot_blob[(size_t)t * k + j];
+            s_p[j] = t * k + j;
+            s_g[j] = gates[(size_t)t * k + j];
+        } else if (j < k) {
             const int e = ids[(size_t)t * k + j];
             const bool ok = (unsigned)e < (unsigned)E;  // ids outside [0, E) are ignored, as in the grouping
             s_blob[j] = ok ? (const uint8_t*)expert_ptrs[e] : nullptr;
@@ -890,13 +913,17 @@ __global__ __launch_bounds__(64 * NW) void ffn_down_combine(const _Float16* __re
     };
     // the slots' h rows (at most kDcChunks 16-byte chunks per thread) and the
     // first slot's quant tiles are all in flight before any LDS store
+    // (straight-line buffer loads: a chunk past the end gets an offset outside
+    // the resource, which reads nothing, so no address is requested twice)
     const int nh = nj * HC;
+    const __amdgpu_buffer_rsrc_t hres = buf_rsrc(h, (uint32_t)(((size_t)T * k + T) * f * 2));
     uint4v v[kDcChunks];
 #pragma unroll
-    for (int u = 0; u < kDcChunks; ++u) {  // past the end: the last chunk again (not stored)
-        const int idx = min((int)threadIdx.x + u * 64 * NW, nh - 1);
-        const int j = idx / HC;
-        v[u] = gload(reinterpret_cast<const uint4v*>(h + (size_t)s_p[j] * f) + (idx - j * HC));
+    for (int u = 0; u < kDcChunks; ++u) {
+        const int idx = (int)threadIdx.x + u * 64 * NW;
+        const int ic = min(idx, nh - 1), j = ic / HC;
+        const uint32_t off = idx < nh ? ((uint32_t)s_p[j] * f + (uint32_t)(ic - j * HC) * 8) * 2 : 0x80000000u;
+        v[u] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(hres, off, 0, 0));
     }
     if (wave < nj) issue(wave, q, sc);
 #pragma unroll
@@ -966,7 +993,8 @@ bool down_combine_ok(const moe_ffn_args* a) {
 }
 
 int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t* ids, const int32_t* dest,
-                        const float* gates, const float* residual, float* out, hipStream_t s) {
+                        const float* gates, const float* residual, float* out, hipStream_t s,
+                        const uint8_t* const* slot_blob) {
     if (!down_combine_ok(a)) return MOE_ERR_UNSUPPORTED;
     const _Float16* h = reinterpret_cast<const _Float16*>(w.h);
     const dim3 grid(a->T * (a->d / (16 * kDcStrips)));
@@ -974,7 +1002,7 @@ int launch_down_combine(const moe_ffn_args* a, const Workspace& w, const int32_t
     const size_t lds = (size_t)(a->k + (sb ? 1 : 0)) * a->f * sizeof(_Float16);
 #define MOE_DC(NKT, NW)                                                                                          \
     ffn_down_combine<NKT, NW><<<grid, 64 * NW, lds, s>>>(h, a->T, a->d, a->f, a->k, a->E, a->expert_ptrs, sb, ids, \
-                                                        dest, gates, residual, out)
+                                                        dest, gates, residual, out, slot_blob)
 #define MOE_DC_NW(NKT)                          \
     if (a->T <= 2) MOE_DC(NKT, kDcWavesFew);    \
     else MOE_DC(NKT, kDcWaves)
@@ -1004,12 +1032,14 @@ int launch_ffn_combine_slots(const moe_ffn_args* a, const Workspace& w, const in
     if (!ffn_combine_slots_ok(a)) return MOE_ERR_UNSUPPORTED;
     const int slots = a->T * a->k + (a->shared_blob ? 1 : 0);
     _Float16* h = reinterpret_cast<_Float16*>(w.h);
-    const bool ok = a->x_dtype == MOE_DT_F32 ? launch_gateup_tok16<float, true>(a, h, slots, s, ids)
-                                             : launch_gateup_tok16<uint16_t, true>(a, h, slots, s, ids);
+    const bool ok =
+        a->x_dtype == MOE_DT_F32
+            ? launch_gateup_tok16<float, true>(a, h, slots, s, ids, nullptr, 1, nullptr, nullptr, w.slot_blob)
+            : launch_gateup_tok16<uint16_t, true>(a, h, slots, s, ids, nullptr, 1, nullptr, nullptr, w.slot_blob);
     if (!ok) return MOE_ERR_UNSUPPORTED;
     const int rc = check_launch();
     if (rc || a->phase == 1) return rc;
-    return launch_down_combine(a, w, ids, nullptr, gates, residual, out, s);
+    return launch_down_combine(a, w, ids, nullptr, gates, residual, out, s, w.slot_blob);
 }
 
 // routing + by-slot FFN + combine for decode batches: the router logits are
@@ -1023,16 +1053,20 @@ int launch_ffn_combine_slots_topk(const moe_ffn_args* a, const Workspace& w, int
     bool ok;
     if (a->E <= 512)
         ok = a->x_dtype == MOE_DT_F32
-                 ? launch_gateup_tok16<float, true, 8>(a, h, slots, s, nullptr, w.logits, planes, ids, gates)
-                 : launch_gateup_tok16<uint16_t, true, 8>(a, h, slots, s, nullptr, w.logits, planes, ids, gates);
+                 ? launch_gateup_tok16<float, true, 8>(a, h, slots, s, nullptr, w.logits, planes, ids, gates,
+                                                       w.slot_blob)
+                 : launch_gateup_tok16<uint16_t, true, 8>(a, h, slots, s, nullptr, w.logits, planes, ids, gates,
+                                                          w.slot_blob);
     else
         ok = a->x_dtype == MOE_DT_F32
-                 ? launch_gateup_tok16<float, true, 16>(a, h, slots, s, nullptr, w.logits, planes, ids, gates)
-                 : launch_gateup_tok16<uint16_t, true, 16>(a, h, slots, s, nullptr, w.logits, planes, ids, gates);
+                 ? launch_gateup_tok16<float, true, 16>(a, h, slots, s, nullptr, w.logits, planes, ids, gates,
+                                                        w.slot_blob)
+                 : launch_gateup_tok16<uint16_t, true, 16>(a, h, slots, s, nullptr, w.logits, planes, ids, gates,
+                                                           w.slot_blob);
     if (!ok) return MOE_ERR_UNSUPPORTED;
     const int rc = check_launch();
     if (rc || a->phase == 1) return rc;
-    return launch_down_combine(a, w, ids, nullptr, gates, residual, out, s);
+    return launch_down_combine(a, w, ids, nullptr, gates, residual, out, s, w.slot_blob);
 }
 
 size_t float_h_bytes(int T, int f, int k) { return ((size_t)T * k + T) * (size_t)f * sizeof(_Float16); }

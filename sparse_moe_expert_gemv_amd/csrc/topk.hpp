@@ -78,10 +78,13 @@ struct RankScratch {
 //  3. each candidate counts the candidates ranking before it, which is its rank;
 //     lane r then holds the entry of rank r.
 // More than 64 candidates (heavy ties) fall back to k rounds of wave argmax.
+// topk_select leaves rank r's value and index in S.v[r], S.i[r] (r < k) and,
+// if s_ids is given, the index in s_ids[r]; topk_gates then forms the softmax
+// from S and writes ids and gates, so that a caller can take the selection
+// alone first and the gates later.
 template <int NPL>
-__device__ __forceinline__ void topk_rank(const double* __restrict__ z, int E, int k, int32_t* __restrict__ ids,
-                          float* __restrict__ gates, int32_t* s_ids, RankScratch& S, int planes = 1,
-                          size_t plane_stride = 0) {
+__device__ __forceinline__ void topk_select(const double* __restrict__ z, int E, int k, int32_t* s_ids,
+                                            RankScratch& S, int planes = 1, size_t plane_stride = 0) {
     const int lane = threadIdx.x & 63;
     double v[NPL];
 #pragma unroll
@@ -154,8 +157,6 @@ __device__ __forceinline__ void topk_rank(const double* __restrict__ z, int E, i
         base += __popcll(b);
     }
     wave_lds_sync();
-    double sv;
-    int si;
     if (base <= 64) {
         const uint64_t ck = lane < base ? S.k[lane] : 0;
         const int ci = lane < base ? S.i[lane] : 0x40000000 + lane;
@@ -168,15 +169,19 @@ __device__ __forceinline__ void topk_rank(const double* __restrict__ z, int E, i
         }
         wave_lds_sync();
         if (lane < base && cr < 64) { S.v[cr] = key_value(ck); S.i[cr] = ci; }
-        wave_lds_sync();
-        sv = lane < k ? S.v[lane] : -DBL_MAX;
-        si = lane < k ? S.i[lane] : 0;
     } else {
         topk_iterative<NPL>(v, E, k, S.i, S.v);
-        wave_lds_sync();
-        sv = lane < k ? S.v[lane] : -DBL_MAX;
-        si = lane < k ? S.i[lane] : 0;
     }
+    wave_lds_sync();
+    if (s_ids && lane < k) s_ids[lane] = S.i[lane];
+}
+
+// softmax over the k selected values of S (rank order) and the global writes
+__device__ __forceinline__ void topk_gates(const RankScratch& S, int k, int32_t* __restrict__ ids,
+                                           float* __restrict__ gates) {
+    const int lane = threadIdx.x & 63;
+    const double sv = lane < k ? S.v[lane] : -DBL_MAX;
+    const int si = lane < k ? S.i[lane] : 0;
     // lane r holds rank r: the softmax terms are summed in rank order
     const double z0 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(sv), 0),
                                        __builtin_amdgcn_readlane(__double2loint(sv), 0));
@@ -185,8 +190,15 @@ __device__ __forceinline__ void topk_rank(const double* __restrict__ z, int E, i
     if (lane < k) {
         ids[lane] = si;
         gates[lane] = (float)(p / ssum);
-        if (s_ids) s_ids[lane] = si;
     }
+}
+
+template <int NPL>
+__device__ __forceinline__ void topk_rank(const double* __restrict__ z, int E, int k, int32_t* __restrict__ ids,
+                                          float* __restrict__ gates, int32_t* s_ids, RankScratch& S, int planes = 1,
+                                          size_t plane_stride = 0) {
+    topk_select<NPL>(z, E, k, s_ids, S, planes, plane_stride);
+    topk_gates(S, k, ids, gates);
 }
 
 // values per lane for E experts (E <= 1024)

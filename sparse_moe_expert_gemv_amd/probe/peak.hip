@@ -27,6 +27,7 @@ enum {
     PROBE_I8_MFMA_TWO_OP_EPILOGUE = 5,   // one 32x32x32 int8 MFMA + 2 fp32 FMAs per output
     PROBE_STREAM_READ = 6,
     PROBE_I8_MFMA_ONE_OP_EPILOGUE = 7,   // one 32x32x32 int8 MFMA + 1 fp32 FMA per output
+    PROBE_STREAM_READ_BURST = 8,         // the read with eight loads in flight per thread
 };
 
 __global__ __launch_bounds__(256) void k_mfma_i8_32(int iters, int seed, float* out) {
@@ -162,17 +163,38 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4v* __restrict__ 
     out[blockIdx.x * blockDim.x + threadIdx.x] = (float)s;
 }
 
+// The same read with eight loads in flight per thread and iteration, the
+// shape of a short read (a few MB in one launch) at its best: no load waits
+// on the previous one.
+__global__ __launch_bounds__(256) void k_stream_read_burst(const uint4v* __restrict__ in, size_t n16, float* out) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    uint32_t s = 0;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        uint4v v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(in + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < n16; i += stride) {
+        const uint4v v = __builtin_nontemporal_load(in + i);
+        s += v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    out[blockIdx.x * blockDim.x + threadIdx.x] = (float)s;
+}
+
 extern "C" {
 
 // Launches one calibration kernel on `stream` (a hipStream_t, or null for the
 // default stream).  grid workgroups of 256 threads; out must hold grid * 256
-// floats.  For PROBE_STREAM_READ, in points to in_bytes (a multiple of 16) of
-// device memory; the other kinds ignore it.  Returns 0, -1 for a bad argument
+// floats.  For PROBE_STREAM_READ and PROBE_STREAM_READ_BURST, in points to
+// in_bytes (a multiple of 16) of device memory; the other kinds ignore it.  Returns 0, -1 for a bad argument
 // (checked before any launch), or the hipError_t of the launch.
 int moe_probe_run(int kind, int grid, int iters, int seed, float* out, const void* in, size_t in_bytes,
                   void* stream) {
     if (grid <= 0 || iters < 0 || !out) return -1;
-    if (kind == PROBE_STREAM_READ && (!in || in_bytes % 16)) return -1;
+    if ((kind == PROBE_STREAM_READ || kind == PROBE_STREAM_READ_BURST) && (!in || in_bytes % 16)) return -1;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (kind) {
         case PROBE_MFMA_I8_32X32X32: k_mfma_i8_32<<<grid, 256, 0, s>>>(iters, seed, out); break;
@@ -184,6 +206,9 @@ int moe_probe_run(int kind, int grid, int iters, int seed, float* out, const voi
         case PROBE_I8_MFMA_ONE_OP_EPILOGUE: k_i8_epilogue<false><<<grid, 256, 0, s>>>(iters, seed, out); break;
         case PROBE_STREAM_READ:
             k_stream_read<<<grid, 256, 0, s>>>(reinterpret_cast<const uint4v*>(in), in_bytes / 16, out);
+            break;
+        case PROBE_STREAM_READ_BURST:
+            k_stream_read_burst<<<grid, 256, 0, s>>>(reinterpret_cast<const uint4v*>(in), in_bytes / 16, out);
             break;
         default: return -1;
     }
