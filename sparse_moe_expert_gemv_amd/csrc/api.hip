@@ -35,7 +35,10 @@ void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* bas
     // T also serves every smaller batch): P T' <= kMaxLogitPlanes T' with P = 1
     // beyond 256 tokens
     const size_t logit_rows = (size_t)T + (size_t)(kMaxLogitPlanes - 1) * std::min(T, 256);
-    w->logits = reinterpret_cast<double*>(take(sizeof(double) * logit_rows * E));
+    // large batches: also room for the filtered router's scratch (route_filter.hip)
+    size_t logit_bytes = sizeof(double) * logit_rows * E;
+    if (T > 256) logit_bytes = std::max(logit_bytes, route_filter_bytes(T, E, d));
+    w->logits = reinterpret_cast<double*>(take(logit_bytes));
     w->route_bytes = off;
     w->hist = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * std::max<size_t>(nch, 1) * E));
     w->permute_bytes = off;

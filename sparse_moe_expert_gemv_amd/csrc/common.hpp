@@ -132,6 +132,12 @@ constexpr int kMaxLogitPlanes = 4;
 int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
                  int32_t* ids, float* gates, double* logits, hipStream_t s);
 bool route_small_ok(int T, int d, int k);
+// large bf16 batches: certified bf16 filter + exact refine of the candidates
+// (route_filter.hip); its scratch (route_filter_bytes) lives in the logits region
+bool route_filter_ok(int T, int d, int E, int k, int x_dtype);
+size_t route_filter_bytes(int T, int E, int d);
+int launch_route_filtered(const void* x, int T, int d, const float* Wr, const float* bias, int E, int k,
+                          int32_t* ids, float* gates, void* scratch, hipStream_t s);
 int launch_route_small(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
                        int32_t* ids, float* gates, double* logits, bool do_permute, int32_t* counts,
                        int32_t* offsets, int32_t* sorted_idx, int32_t* dest, int32_t* active, hipStream_t s);

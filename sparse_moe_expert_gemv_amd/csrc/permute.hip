@@ -23,7 +23,10 @@ __global__ __launch_bounds__(256) void perm_hist(const int32_t* __restrict__ ids
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One workgroup of 1024 threads (E <= 1024).
+// One workgroup of 1024 threads (E <= 1024).  Thread e turns its expert's
+// chunk counts into exclusive positions within the expert, reading them 16 at
+// a time so that the loads overlap (one dependent round trip per 16 chunks);
+// the expert base (offsets[e]) is added by the scatter.
 __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ hist, int nch, int E,
                                                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ active) {
@@ -32,10 +35,16 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ hist, in
     const int e = threadIdx.x;
     int total = 0;
     if (e < E) {
-        for (int c = 0; c < nch; ++c) {
-            const int v = hist[(size_t)c * E + e];
-            hist[(size_t)c * E + e] = total;  // exclusive within the expert, before the expert base is added
-            total += v;
+        constexpr int G = 16;
+        for (int c0 = 0; c0 < nch; c0 += G) {
+            int v[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) v[g] = c0 + g < nch ? hist[(size_t)(c0 + g) * E + e] : 0;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (c0 + g < nch) hist[(size_t)(c0 + g) * E + e] = total;
+                total += v[g];
+            }
         }
         counts[e] = total;
     }
@@ -55,7 +64,6 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ hist, in
     if (e < E) {
         offsets[e] = excl;
         if (total > 0) active[1 + sf[e] - 1] = e;
-        for (int c = 0; c < nch; ++c) hist[(size_t)c * E + e] += excl;
     }
     if (e == E - 1) {
         offsets[E] = sc[e];
@@ -66,10 +74,11 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ hist, in
 // One wavefront per chunk, slots visited in ascending order.
 __global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ ids, int n, int E,
                                                    const int32_t* __restrict__ hist,
+                                                   const int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ sorted_idx, int32_t* __restrict__ dest) {
     extern __shared__ int32_t pos[];
     const int lane = threadIdx.x;
-    for (int e = lane; e < E; e += 64) pos[e] = hist[(size_t)blockIdx.x * E + e];
+    for (int e = lane; e < E; e += 64) pos[e] = offsets[e] + hist[(size_t)blockIdx.x * E + e];
     __syncthreads();
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
@@ -112,7 +121,7 @@ int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int
     perm_scan<<<1, 1024, 0, s>>>(hist, nch, E, counts, offsets, active);
     rc = check_launch();
     if (rc) return rc;
-    perm_scatter<<<nch, 64, E * sizeof(int32_t), s>>>(ids, n, E, hist, sorted_idx, dest);
+    perm_scatter<<<nch, 64, E * sizeof(int32_t), s>>>(ids, n, E, hist, offsets, sorted_idx, dest);
     return check_launch();
 }
 

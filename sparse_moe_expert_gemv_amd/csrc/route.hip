@@ -708,6 +708,9 @@ int launch_route(const void* x, int x_dtype, int T, int d, const float* Wr, cons
     if (route_small_ok(T, d, k))
         return launch_route_small(x, x_dtype, T, d, Wr, bias, E, k, ids, gates, logits, false, nullptr, nullptr,
                                   nullptr, nullptr, nullptr, s);
+    // the workspace layout sizes the logits region for the filter's scratch too
+    if (route_filter_ok(T, d, E, k, x_dtype))
+        return launch_route_filtered(x, T, d, Wr, bias, E, k, ids, gates, logits, s);
     int rc = launch_logits(x, x_dtype, T, d, Wr, bias, E, logits, s);
     if (rc) return rc;
     const int planes = logit_planes(T, d, E);

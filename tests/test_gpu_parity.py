@@ -107,6 +107,62 @@ def test_route_and_permute_bitexact(name):
                                             sorted_idx=sorted_idx, dest=dest), E)
 
 
+def _route_filter_scratch_overflow(ws, T, E):
+    """Overflow count of the large-batch router, read from the library's
+    internal scratch layout (256-byte aligned: T E fp32 filter logits, E
+    doubles, then the count) to show which pass handled the tokens."""
+    up = lambda v: (v + 255) // 256 * 256
+    off = up(T * E * 4) + up(E * 8)
+    return int(ws[off:off + 4].cpu().numpy().view(np.int32)[0])
+
+
+@pytest.mark.parametrize("case", ["near_ties", "overflow"])
+def test_route_filter_near_ties_and_overflow(case):
+    """Large bf16 batches route through the certified bf16 filter and the exact
+    refine of the candidates.  Router rows built to defeat the filter: a row
+    scaled by (1 + 2^-18) (logits ~1e-6 apart, far inside the filter's error
+    bound), an exact duplicate (an exact tie: the lower index wins), a nudged
+    copy; and, for the overflow case, 100 identical dominant rows (more than
+    64 candidates: the exact full-row pass).  Ids bit-exact, gates within 1e-6."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    T, d, E, k = 600, 256, 128 if case == "near_ties" else 256, 8
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    Wr = (0.02 * rng.standard_normal((E, d))).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(E)).astype(np.float32)
+    if case == "near_ties":
+        Wr[2] *= 3.0
+        Wr[5] = Wr[2] * np.float32(1 + 2.0 ** -18)
+        Wr[9] = Wr[2]
+        Wr[40] = Wr[2]
+        Wr[40, 7] = np.nextafter(Wr[2, 7], np.float32(1.0))
+        bias[[5, 9, 40]] = bias[2]
+    else:
+        Wr[:100] = 4.0 * Wr[0]
+        bias[:100] = bias[0]
+    xt = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    Wt = torch.from_numpy(Wr).to(DEV)
+    bt = torch.from_numpy(bias).to(DEV)
+    ws = torch.zeros(B.moe_workspace_size(T, d, 128, E, k, B.MOE_ACT_FLOAT), dtype=torch.uint8, device=DEV)
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gates = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    B.moe_route(xt, Wt, bt, k, ids, gates, ws)
+    torch.cuda.synchronize()
+    n_ovf = _route_filter_scratch_overflow(ws, T, E)
+    ref_ids, ref_gates = oracle.route(synth.bf16_bits_to_f32(x), Wr, bias, k)
+    got = host(ids)
+    assert np.array_equal(got, ref_ids), "ids differ in %d tokens" % int((got != ref_ids).any(axis=1).sum())
+    assert np.max(np.abs(host(gates) - ref_gates)) <= 1e-6
+    if case == "near_ties":
+        tie = np.isin(ref_ids, [2, 5, 9, 40]).sum(axis=1)
+        assert (tie == 4).sum() > 50  # the tied group is selected whole, in order, for many tokens
+        assert n_ovf == 0
+    else:
+        # the tied rows lead for about a third of the tokens; every such token
+        # has all 100 of them as candidates and takes the full-row pass
+        assert (ref_ids[:, 0] == 0).sum() > 100
+        assert n_ovf >= (ref_ids[:, 0] == 0).sum()
+
+
 _LAYERS = {}
 
 
