@@ -102,7 +102,10 @@ int moe_unpack_experts(const void* src, void* dst, int n, int wfmt, int d, int f
  * Workspace bytes needed by route, permute and expert_ffn for a layer with
  * these shapes (the same workspace may be passed to all three calls of one
  * layer; calls on one stream are ordered).  Writes *bytes.  The workspace is
- * scratch: its contents need no initialisation and are not preserved.
+ * scratch: its contents need no initialisation and are not preserved.  No
+ * passage defines this; it is the library's sizing convention (a workspace
+ * sized for T tokens serves every smaller batch of the same layer).
+ * Errors: MOE_ERR_INVALID_ARG for shapes outside the limits above.
  */
 int moe_workspace_size(int T, int d, int f, int E, int k, int act_mode, size_t* bytes);
 
@@ -119,6 +122,9 @@ int moe_workspace_size(int T, int d, int f, int E, int k, int act_mode, size_t* 
  *                  inputs are exact in double; sums are double).
  *   gates [T, k]   fp32 out: softmax over the k selected logits (equal to the
  *                  full softmax renormalised over the top k).
+ * Batches of more than 256 bf16 tokens (k <= 32, d <= 4096) first bound every
+ * logit with a bf16 matrix-core filter and take exact double logits only for
+ * the experts that can still rank in the top k; the outputs are the same.
  */
 int moe_route(const void* x, int x_dtype, int T, int d, const float* Wr, const float* bias, int E, int k,
               int32_t* ids, float* gates, void* ws, size_t ws_bytes, moe_stream_t stream);
@@ -136,6 +142,10 @@ int moe_route_permute(const void* x, int x_dtype, int T, int d, const float* Wr,
 
 /*
  * Stable grouping of the T*k routing slots by expert (flat slot f = t*k + j).
+ * No passage defines this step; it is the dispatch that on-demand expert
+ * scheduling implies ("single RTX 5090 runs a 125B model": only the picked
+ * experts compute), grouping each picked expert's rows so that its weights
+ * are read once per call.
  *   counts     [E]      number of slots routed to each expert
  *   offsets    [E+1]    exclusive prefix sum of counts (offsets[E] = T*k)
  *   sorted_idx [T*k]    slots in (expert, slot) order: expert-major, ascending
@@ -150,7 +160,10 @@ int moe_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_
                 int32_t* dest, int32_t* active, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /*
- * int8 activation quantisation (MOE_ACT_Q8 input): per token, per 32
+ * int8 activation quantisation (MOE_ACT_Q8 input), for the int8 matrix-core
+ * prefill that "Strata benchmarks" names (bottleneck analysis 1, prefill
+ * optimisation table: int8 tensor-core products without dequantisation; the
+ * block of 32 and the scale rule are this library's reading): per token, per 32
  * consecutive features, s = amax / 127 (fp32, IEEE division),
  * q = clamp(rint(x / s), -127, 127) with ties to even; an all-zero block gives
  * s = 0 and q = 0.  x [T, d] (F32 or BF16) -> xq [T, d] int8, sx [T, d/32] fp32.
@@ -346,7 +359,10 @@ int moe_host_expert_ffn(moe_host_pool* pool, int n_items, const int32_t* item_to
 
 /*
  * Combine: out[t] = residual[t] + y_shared[t] + sum_{j<k} gates[t,j] * y_perm[dest[t*k+j]],
- * summed in j order (deterministic).
+ * summed in j order (deterministic): the picked experts' outputs weighted by
+ * the gating network's weights ("single RTX 5090 runs a 125B model",
+ * on-demand expert scheduling) plus the always-resident shared expert ("How
+ * Strata works", three-tier division), ungated.
  *   y_perm [T*k, d] (y_dtype F32 or F16), dest [T*k], gates [T, k],
  *   y_shared [T, d] fp32 or NULL, residual [T, d] fp32 or NULL, out [T, d] fp32.
  * out may alias residual.
