@@ -163,6 +163,31 @@ def test_route_filter_near_ties_and_overflow(case):
         assert n_ovf >= (ref_ids[:, 0] == 0).sum()
 
 
+@pytest.mark.parametrize("T,d,E,k", [(300, 4096, 200, 32), (257, 128, 1024, 1), (1000, 384, 96, 7),
+                                     (513, 2048, 1024, 10), (300, 256, 64, 32)])
+def test_route_filter_shapes(T, d, E, k):
+    """The large-batch router (bf16 filter + exact refine) at shapes that
+    exercise its other instances and edges: router rows not a multiple of the
+    128-row filter tile, E = 1024 (16 logits per lane), d = 4096 (the wider token
+    layout of the refine), k = 32 (the filter's limit) and k = 1, d = 128, a
+    token count not a multiple of the 64-token tile.  Ids bit-exact against the
+    oracle, gates within 1e-6."""
+    rng = np.random.Generator(np.random.PCG64(1000 + T + d + E + k))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    Wr = (0.02 * rng.standard_normal((E, d))).astype(np.float32)
+    bias = (0.01 * rng.standard_normal(E)).astype(np.float32)
+    xt = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    ws = torch.empty(B.moe_workspace_size(T, d, 128, E, k, B.MOE_ACT_FLOAT), dtype=torch.uint8, device=DEV)
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gates = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    B.moe_route(xt, torch.from_numpy(Wr).to(DEV), torch.from_numpy(bias).to(DEV), k, ids, gates, ws)
+    torch.cuda.synchronize()
+    ref_ids, ref_gates = oracle.route(synth.bf16_bits_to_f32(x), Wr, bias, k)
+    got = host(ids)
+    assert np.array_equal(got, ref_ids), "ids differ in %d tokens" % int((got != ref_ids).any(axis=1).sum())
+    assert np.max(np.abs(host(gates) - ref_gates)) <= 1e-6
+
+
 _LAYERS = {}
 
 
