@@ -12,6 +12,8 @@
 // a persistent thread pool by output rows (gate/up rows, then down rows);
 // every output is produced by one thread in a fixed order, so the result does
 // not depend on the thread count.  Host code only: no HIP call.
+#include <immintrin.h>
+
 #include <atomic>
 #include <cmath>
 #include <condition_variable>
@@ -195,6 +197,71 @@ float row_dot_i8(const int8_t* __restrict q, const uint16_t* __restrict sc, cons
     return acc[0];
 }
 
+// AVX-512 forms of the two row kernels (chosen at run time where the CPU has
+// AVX-512F/BW): per 32-block, the 32 quants are widened to int32 and converted
+// to fp32 (int4: the low and high nibbles of 16 bytes, against the even and odd
+// elements of x), multiplied with x and summed into a 16-lane block sum by one
+// multiply and one fused multiply-add, then scaled by the block's fp16 scale
+// into a 16-lane accumulator (two accumulators over alternate blocks, added at
+// the end); the lanes are then added in the fixed order of the reduction
+// instruction sequence.  Deterministic for a given CPU; the order of the sums
+// differs from the portable loops above (same tolerance against the oracle).
+#define MOE_AVX512 __attribute__((target("avx512f,avx512bw,f16c")))
+
+MOE_AVX512 static inline void i4_block(const uint8_t* __restrict q, const uint16_t* __restrict sc,
+                                       const float* __restrict xe, const float* __restrict xo,
+                                       const float* __restrict xsum, int b, __m512& acc, float& corr) {
+    const __m512i w = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(q + b * 16)));
+    const __m512 lo = _mm512_cvtepi32_ps(_mm512_and_si512(w, _mm512_set1_epi32(15)));
+    const __m512 hi = _mm512_cvtepi32_ps(_mm512_srli_epi32(w, 4));
+    const __m512 t = _mm512_fmadd_ps(_mm512_loadu_ps(xo + b * 16), hi, _mm512_mul_ps(_mm512_loadu_ps(xe + b * 16), lo));
+    const float s = _cvtsh_ss(sc[b]);
+    acc = _mm512_fmadd_ps(_mm512_set1_ps(s), t, acc);
+    corr += s * xsum[b];
+}
+
+MOE_AVX512 float row_dot_i4_avx512(const uint8_t* __restrict q, const uint16_t* __restrict sc,
+                                   const float* __restrict xe, const float* __restrict xo,
+                                   const float* __restrict xsum, int K) {
+    __m512 acc0 = _mm512_setzero_ps(), acc1 = _mm512_setzero_ps();
+    float corr0 = 0.f, corr1 = 0.f;
+    const int nb = K / 32;
+    int b = 0;
+    for (; b + 1 < nb; b += 2) {
+        i4_block(q, sc, xe, xo, xsum, b, acc0, corr0);
+        i4_block(q, sc, xe, xo, xsum, b + 1, acc1, corr1);
+    }
+    if (b < nb) i4_block(q, sc, xe, xo, xsum, b, acc0, corr0);
+    return _mm512_reduce_add_ps(_mm512_add_ps(acc0, acc1)) - 8.f * (corr0 + corr1);
+}
+
+MOE_AVX512 static inline void i8_block(const int8_t* __restrict q, const uint16_t* __restrict sc,
+                                       const float* __restrict x, int b, __m512& acc) {
+    const __m512 a = _mm512_cvtepi32_ps(_mm512_cvtepi8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(q + b * 32))));
+    const __m512 c = _mm512_cvtepi32_ps(_mm512_cvtepi8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(q + b * 32 + 16))));
+    const __m512 t = _mm512_fmadd_ps(_mm512_loadu_ps(x + b * 32 + 16), c, _mm512_mul_ps(_mm512_loadu_ps(x + b * 32), a));
+    acc = _mm512_fmadd_ps(_mm512_set1_ps(_cvtsh_ss(sc[b])), t, acc);
+}
+
+MOE_AVX512 float row_dot_i8_avx512(const int8_t* __restrict q, const uint16_t* __restrict sc,
+                                   const float* __restrict x, int K) {
+    __m512 acc0 = _mm512_setzero_ps(), acc1 = _mm512_setzero_ps();
+    const int nb = K / 32;
+    int b = 0;
+    for (; b + 1 < nb; b += 2) {
+        i8_block(q, sc, x, b, acc0);
+        i8_block(q, sc, x, b + 1, acc1);
+    }
+    if (b < nb) i8_block(q, sc, x, b, acc0);
+    return _mm512_reduce_add_ps(_mm512_add_ps(acc0, acc1));
+}
+
+bool have_avx512() {
+    static const bool v = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                          __builtin_cpu_supports("f16c");
+    return v;
+}
+
 struct Canon {
     size_t qg, qu, qd, sg, su, sd;
 };
@@ -226,9 +293,14 @@ struct RowInput {
     }
     float dot(const uint8_t* blob, size_t qoff, size_t soff, int row, int K, int wfmt, const float* lut) const {
         const uint16_t* sc = reinterpret_cast<const uint16_t*>(blob + soff) + (size_t)row * (K / 32);
-        if (wfmt == MOE_WFMT_I4B32)
-            return row_dot_i4(blob + qoff + (size_t)row * (K / 2), sc, xe.data(), xo.data(), xsum.data(), lut, K);
-        return row_dot_i8(reinterpret_cast<const int8_t*>(blob + qoff) + (size_t)row * K, sc, x.data(), lut, K);
+        if (wfmt == MOE_WFMT_I4B32) {
+            const uint8_t* q = blob + qoff + (size_t)row * (K / 2);
+            if (have_avx512()) return row_dot_i4_avx512(q, sc, xe.data(), xo.data(), xsum.data(), K);
+            return row_dot_i4(q, sc, xe.data(), xo.data(), xsum.data(), lut, K);
+        }
+        const int8_t* q = reinterpret_cast<const int8_t*>(blob + qoff) + (size_t)row * K;
+        if (have_avx512()) return row_dot_i8_avx512(q, sc, x.data(), K);
+        return row_dot_i8(q, sc, x.data(), lut, K);
     }
 };
 
