@@ -498,9 +498,12 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_gateup(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_idx, const int32_t* __restrict__ active,
     const int4* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, _Float16* __restrict__ h_out) {
     // two LDS stages as separate variables: the compiler then knows that the
-    // loads filling one do not alias the reads of the other
+    // loads filling one do not alias the reads of the other.  The token scales,
+    // read 12 times per block and wavefront, are over-aligned so that they are
+    // placed first, within the 64 KiB reach of the LDS instructions' immediate
+    // offsets (no address arithmetic per read)
     __shared__ GUStage S0, S1;
-    __shared__ GUScales SA0, SA1;
+    __shared__ __align__(1024) GUScales SA0, SA1;
     __shared__ int32_t s_row[kTR];  // token of each tile row
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
