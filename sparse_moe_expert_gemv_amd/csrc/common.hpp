@@ -67,6 +67,7 @@ __host__ __device__ inline CanonLayout canon_layout(int wfmt, int d, int f) {
 
 // ---- vector types -----------------------------------------------------------
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float16v __attribute__((ext_vector_type(16)));

@@ -127,6 +127,79 @@ __global__ __launch_bounds__(256) void combine(const YT* __restrict__ y, const i
     }
 }
 
+// The same sum with every gather of a chunk requested before any is waited
+// for: the slots' rows and gates are read for all U positions of the chunk (the
+// index clamped to the last slot), and each row piece is a buffer load whose
+// offset for a position past k lies outside the resource (it reads nothing
+// and returns zero), so that the loads stay straight-line code; with the
+// loads under branches the compiler waits for each before the next.  Rows
+// must lie in the first 2 GiB of y (the caller checks).  Sum order as combine.
+template <typename YT, int V>
+__global__ __launch_bounds__(256) void combine_gather(const YT* __restrict__ y, uint32_t y_bytes,
+                                                      const int32_t* __restrict__ dest,
+                                                      const float* __restrict__ gates,
+                                                      const float* __restrict__ ysh, const float* residual, int T,
+                                                      int k, int d, float* out) {
+    constexpr int NQ = V / 4;
+    constexpr int U = 16;
+    constexpr int PB = V * (int)sizeof(YT);  // bytes of one thread's piece of a row: 8 or 16
+    const int t = blockIdx.x;
+    const __amdgpu_buffer_rsrc_t yr = buf_rsrc(y, y_bytes);
+    for (int o = (int)threadIdx.x * V; o < d; o += 256 * V) {
+        float4 acc[NQ];
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (residual) acc[u] = *reinterpret_cast<const float4*>(residual + (size_t)t * d + o + 4 * u);
+            if (ysh) {
+                const float4 v = *reinterpret_cast<const float4*>(ysh + (size_t)t * d + o + 4 * u);
+                acc[u].x += v.x; acc[u].y += v.y; acc[u].z += v.z; acc[u].w += v.w;
+            }
+        }
+        for (int j0 = 0; j0 < k; j0 += U) {
+            float g[U];
+            int row[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const int jj = min(j0 + j, k - 1);
+                g[j] = gates[(size_t)t * k + jj];
+                row[j] = dest[(size_t)t * k + jj];
+            }
+            float4 v[U][NQ];
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const uint32_t off =
+                    j0 + j < k ? ((uint32_t)row[j] * (uint32_t)d + (uint32_t)o) * (uint32_t)sizeof(YT) : 0x80000000u;
+                // whole-vector casts only: this compiler narrows a load whose
+                // vector elements are bit-cast one by one, reading element 0 for all
+                if constexpr (PB == 16) {
+                    const auto raw = __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, 0);
+                    if constexpr (sizeof(YT) == 4) {
+                        const float4v f = __builtin_bit_cast(float4v, raw);
+                        v[j][0] = make_float4(f[0], f[1], f[2], f[3]);
+                    } else {
+                        const half8 h = __builtin_bit_cast(half8, raw);
+                        v[j][0] = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+                        v[j][NQ - 1] = make_float4((float)h[4], (float)h[5], (float)h[6], (float)h[7]);
+                    }
+                } else {
+                    const half4v h = __builtin_bit_cast(half4v, __builtin_amdgcn_raw_buffer_load_b64(yr, off, 0, 0));
+                    v[j][0] = make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                if (j0 + j < k) {
+#pragma unroll
+                    for (int u = 0; u < NQ; ++u) fma4(g[j], v[j][u], acc[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) *reinterpret_cast<float4*>(out + (size_t)t * d + o + 4 * u) = acc[u];
+    }
+}
+
 // out[t] = x[t] / sqrt(mean(x[t]^2) + eps): one wavefront per row, sums of
 // squares and the scale in double, result rounded once to fp32.
 __global__ __launch_bounds__(256) void rmsnorm(const float* __restrict__ x, int T, int d, double eps,
@@ -163,6 +236,21 @@ int launch_combine(const void* y_perm, int y_dtype, const int32_t* dest, const f
     const int V = (y_dtype == MOE_DT_F16 && d % 8 == 0) ? 8 : 4;
     if (T == 0) return MOE_OK;
     const int grid = T;
+    // rows of y_perm addressed by dest are < T k
+    const size_t y_bytes = (size_t)T * k * d * (y_dtype == MOE_DT_F32 ? 4 : 2);
+    if (y_bytes < ((size_t)1 << 31)) {
+        const uint32_t yb = (uint32_t)y_bytes;
+        if (y_dtype == MOE_DT_F32)
+            combine_gather<float, 4><<<grid, 256, 0, s>>>((const float*)y_perm, yb, dest, gates, y_shared, residual, T,
+                                                          k, d, out);
+        else if (V == 8)
+            combine_gather<_Float16, 8><<<grid, 256, 0, s>>>((const _Float16*)y_perm, yb, dest, gates, y_shared,
+                                                             residual, T, k, d, out);
+        else
+            combine_gather<_Float16, 4><<<grid, 256, 0, s>>>((const _Float16*)y_perm, yb, dest, gates, y_shared,
+                                                             residual, T, k, d, out);
+        return check_launch();
+    }
     if (y_dtype == MOE_DT_F32)
         combine<float, 4><<<grid, 256, 0, s>>>((const float*)y_perm, dest, gates, y_shared, residual, T, k, d, out);
     else if (V == 8)

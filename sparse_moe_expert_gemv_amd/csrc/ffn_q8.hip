@@ -653,8 +653,13 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_gateup(
         }
         // h = silu(g) * u, requantised per (token, 32 features of this
         // wavefront): the 32 features of a token are the lanes of one
-        // half-wavefront
-        const int feat = grp * kGUFeat + fg * 32 + (lane & 31);
+        // half-wavefront.  h leaves through LDS (the stages are free after the
+        // last barrier): each wavefront writes its [32 tokens][32 features]
+        // tile (rows padded by 16 bytes) element by element and stores it as
+        // 16-byte pieces of rows.
+        constexpr int HRB = 32 * 2 + 16;  // tile row pitch in bytes
+        unsigned char* htile = reinterpret_cast<unsigned char*>(&S0) + wave * (32 * HRB);
+        _Float16* hdst = h_out + (size_t)(p0 + m0) * f + grp * kGUFeat + fg * 32;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
 #pragma unroll
@@ -670,9 +675,22 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_gateup(
                 const float sc = amax / 127.0f;
                 float q = 0.0f;
                 if (sc != 0.0f) q = fminf(fmaxf(rintf(hv * (127.0f * __builtin_amdgcn_rcpf(amax))), -127.0f), 127.0f);
-                const int mrow = (mt0 + m) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (mrow < mc) h_out[(size_t)(p0 + m0 + mrow) * f + feat] = (_Float16)(q * sc);
+                const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                *reinterpret_cast<_Float16*>(htile + row * HRB + (lane & 31) * 2) = (_Float16)(q * sc);
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = 16 * i + (lane >> 2), pc = lane & 3;
+                const uint4 v = *reinterpret_cast<const uint4*>(htile + row * HRB + pc * 16);
+                const int trow = (mt0 + m) * 32 + row;
+                if (trow < mc) *reinterpret_cast<uint4*>(hdst + (size_t)trow * f + pc * 8) = v;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");  // the next tile reuses the buffer
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         }
     };
     switch (min(max(nmt - mt0, 0), 3)) {  // wave-uniform
@@ -725,6 +743,46 @@ __device__ __forceinline__ void dn_chunk(const DNStage& G, int lane, int r0, int
         acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i & 1], B0[st & 1], acc[m][0], 0, 0, 0);
         acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i & 1], B1[st & 1], acc[m][1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Bytes of one wavefront's [32][64] output tile of element type YT in LDS
+// (rows padded by 16 bytes: the element writes of the two half-wavefronts,
+// four rows apart, fall in different banks).
+template <typename YT>
+constexpr int dn_tile_bytes() { return 32 * (64 * (int)sizeof(YT) + 16); }
+
+// Writes a wavefront's NM output tiles (token rows 32 (mt0 + m) .., the
+// wavefront's 64 output columns) to dst[row * d + col] through its LDS tile:
+// rows at or past mc are not written.
+template <int NM, typename YT>
+__device__ __forceinline__ void dn_write_tiles(unsigned char* tile, const float16v (&acc)[3][2], int lane, int mt0,
+                                               int mc, YT* dst, int d) {
+    constexpr int RB = 64 * (int)sizeof(YT) + 16;  // row pitch in bytes
+    constexpr int PER_ROW = 64 * (int)sizeof(YT) / 16;  // 16-byte pieces per row
+    constexpr int ROWS_PER = 64 / PER_ROW;              // rows covered by one wavefront read
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                *reinterpret_cast<YT*>(tile + row * RB + (n * 32 + (lane & 31)) * (int)sizeof(YT)) = (YT)acc[m][n][r];
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+        for (int i = 0; i < 32 / ROWS_PER; ++i) {
+            const int row = i * ROWS_PER + lane / PER_ROW, pc = lane % PER_ROW;
+            const uint4 v = *reinterpret_cast<const uint4*>(tile + row * RB + pc * 16);
+            const int trow = (mt0 + m) * 32 + row;
+            if (trow < mc) *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(dst + (size_t)trow * d) + pc * 16) = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");  // the next tile reuses the buffer
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
     }
 }
 
@@ -844,20 +902,19 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_down(
                 if (c + 4 < nkc) load_chunk(R0, c + 4);
             }
         }
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int o = grp * kDNRows + (n == 0 ? r0 : r1);
-                if (o >= d) continue;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int mrow = (mt0 + m) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (mrow >= mc) continue;
-                    if (routed) y_perm[(size_t)(p0 + m0 + mrow) * d + o] = (YT)acc[m][n][r];
-                    else y_shared[(size_t)(m0 + mrow) * d + o] = acc[m][n][r];
-                }
-            }
+        // The expert outputs leave through LDS: the stages are free after the
+        // last barrier, and each wavefront owns a [32][64] tile of its own
+        // there (its 32 token rows of tile m times its 64 output rows, rows
+        // padded by 16 bytes).  Lane l holds rows 8 (r / 4) + 4 (l / 32) + r % 4
+        // of columns n 32 + l % 32; written as elements, the tile is read back
+        // as 16-byte pieces of rows, so every global store writes whole rows of
+        // 64 consecutive outputs (128-bit stores instead of 2-byte ones).
+        const int o0 = grp * kDNRows + og * 64;  // first output of this wavefront's columns
+        if (o0 < d) {
+            if (routed) dn_write_tiles<NM, YT>(reinterpret_cast<unsigned char*>(&S[0]) + wave * dn_tile_bytes<YT>(),
+                                               acc, lane, mt0, mc, y_perm + (size_t)(p0 + m0) * d + o0, d);
+            else dn_write_tiles<NM, float>(reinterpret_cast<unsigned char*>(&S[0]) + wave * dn_tile_bytes<float>(),
+                                           acc, lane, mt0, mc, y_shared + (size_t)m0 * d + o0, d);
         }
     };
     switch (min(max(nmt - mt0, 0), 3)) {  // wave-uniform
