@@ -652,41 +652,60 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_gateup(
             }
         }
         // h = silu(g) * u, requantised per (token, 32 features of this
-        // wavefront): the 32 features of a token are the lanes of one
-        // half-wavefront.  h leaves through LDS (the stages are free after the
-        // last barrier): each wavefront writes its [32 tokens][32 features]
-        // tile (rows padded by 16 bytes) element by element and stores it as
-        // 16-byte pieces of rows.
-        constexpr int HRB = 32 * 2 + 16;  // tile row pitch in bytes
+        // wavefront).  In the MFMA layout the 32 features of a token are the
+        // lanes of one half-wavefront, so h first goes through LDS (the stages
+        // are free after the last barrier): each wavefront writes its
+        // [32 tokens][32 features] fp32 tile (rows padded by 16 bytes) and
+        // reads it back as half rows, lane l holding features 16 (l & 1) .. +15
+        // of token l / 2.  The block maximum is then 15 local maxima and one
+        // with the neighbouring lane, the scale amax / 127 one division per
+        // lane, and the 16 codes leave as two 16-byte row stores of fp16(q s).
+        constexpr int HRB = 32 * 4 + 16;  // tile row pitch in bytes
+        static_assert(kPThreads / 64 * 32 * HRB <= sizeof(GUStage), "h tiles exceed the stage");
         unsigned char* htile = reinterpret_cast<unsigned char*>(&S0) + wave * (32 * HRB);
-        _Float16* hdst = h_out + (size_t)(p0 + m0) * f + grp * kGUFeat + fg * 32;
+        const int hrow = lane >> 1, hhalf = lane & 1;
+        _Float16* hdst = h_out + (size_t)(p0 + m0) * f + grp * kGUFeat + fg * 32 + 16 * hhalf;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float g = acc[m][0][r];
                 const float hv = g * acc[m][1][r] * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                float amax = fabsf(hv);
-                amax = fmaxf(amax, __uint_as_float(lane_xor<1>(__float_as_uint(amax))));
-                amax = fmaxf(amax, __uint_as_float(lane_xor<2>(__float_as_uint(amax))));
-                amax = fmaxf(amax, __uint_as_float(lane_xor<4>(__float_as_uint(amax))));
-                amax = fmaxf(amax, __uint_as_float(lane_xor<8>(__float_as_uint(amax))));
-                amax = fmaxf(amax, __uint_as_float(lane_xor<16>(__float_as_uint(amax))));
-                const float sc = amax / 127.0f;
-                float q = 0.0f;
-                if (sc != 0.0f) q = fminf(fmaxf(rintf(hv * (127.0f * __builtin_amdgcn_rcpf(amax))), -127.0f), 127.0f);
                 const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                *reinterpret_cast<_Float16*>(htile + row * HRB + (lane & 31) * 2) = (_Float16)(q * sc);
+                *reinterpret_cast<float*>(htile + row * HRB + (lane & 31) * 4) = hv;
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+            float v[16];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = 16 * i + (lane >> 2), pc = lane & 3;
-                const uint4 v = *reinterpret_cast<const uint4*>(htile + row * HRB + pc * 16);
-                const int trow = (mt0 + m) * 32 + row;
-                if (trow < mc) *reinterpret_cast<uint4*>(hdst + (size_t)trow * f + pc * 8) = v;
+            for (int j = 0; j < 4; ++j) {
+                const float4 t = *reinterpret_cast<const float4*>(htile + hrow * HRB + hhalf * 64 + j * 16);
+                v[4 * j + 0] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+            }
+            float amax = fabsf(v[0]);
+#pragma unroll
+            for (int j = 1; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+            amax = fmaxf(amax, __uint_as_float(lane_xor<1>(__float_as_uint(amax))));
+            const float sc = amax / 127.0f;
+            const float inv = 127.0f * __builtin_amdgcn_rcpf(amax);
+            uint32_t pk[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float q0 = 0.0f, q1 = 0.0f;
+                if (sc != 0.0f) {
+                    q0 = fminf(fmaxf(rintf(v[2 * j] * inv), -127.0f), 127.0f);
+                    q1 = fminf(fmaxf(rintf(v[2 * j + 1] * inv), -127.0f), 127.0f);
+                }
+                const _Float16 h0 = (_Float16)(q0 * sc), h1 = (_Float16)(q1 * sc);
+                pk[j] = (uint32_t)__builtin_bit_cast(unsigned short, h0) |
+                        ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
+            }
+            const int trow = (mt0 + m) * 32 + hrow;
+            if (trow < mc) {
+                uint4* dst = reinterpret_cast<uint4*>(hdst + (size_t)trow * f);
+                dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");  // the next tile reuses the buffer
             __builtin_amdgcn_wave_barrier();
