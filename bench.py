@@ -801,6 +801,23 @@ def bench_peak(a):
                                           round(best[3] * 1e6, 2), "kernel": best[1], "workgroups_per_cu": best[2]}
     res["short_read_one_launch"] = short
     del buf
+    # the vendor library's fp16 rate at the prefill expert shapes: torch.bmm
+    # (hipBLASLt) over 512 experts of 176 token rows with dense fp16 weights
+    # (four times the weight bytes of int4), gate/up (2,048 k, 1,536 outputs)
+    # and down (768 k, 2,048 outputs); operands contiguous, fp16 outputs
+    vendor = {}
+    for nm, (G, M, K, N) in (("gateup_512x176x2048x1536", (512, 176, 2048, 1536)),
+                             ("down_512x176x768x2048", (512, 176, 768, 2048))):
+        A = torch.randn(G, M, K, device="cuda", dtype=torch.float16)
+        Bm = torch.randn(G, K, N, device="cuda", dtype=torch.float16).contiguous()
+        Cm = torch.empty(G, M, N, device="cuda", dtype=torch.float16)
+        time_it(lambda: torch.bmm(A, Bm, out=Cm), reps=2)  # warm-up (the library's kernel selection)
+        t = time_it(lambda: torch.bmm(A, Bm, out=Cm), reps=10)
+        fl = 2.0 * G * M * K * N
+        vendor[nm] = {"ms": round(t * 1e3, 3), "rate": round(fl / t / 1e12, 1), "unit": "TFLOPS",
+                      "frac_of_f16_peak": round(fl / t / 1e12 / 2500.0, 4)}
+        del A, Bm, Cm
+    res["vendor_fp16_bmm"] = vendor
     print(json.dumps({"workload": "peak", "compute_units": n_cu, "datasheet": {
         "int8_mfma_TOPS": INT8_PEAK_TOPS, "f16_mfma_TFLOPS": 2500.0, "fp32_vector_TFLOPS": 157.3,
         "hbm_GBps": HBM_PEAK_GBS}, "measured": res}), flush=True)
