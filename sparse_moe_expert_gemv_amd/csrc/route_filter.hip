@@ -12,8 +12,9 @@
 //     c = 2^-16 + 4 * 1.008 * gamma(2 d), gamma(n) = n u / (1 - n u), u = 2^-24
 //     (Cauchy-Schwarz bounds the absolute sum by the norms; the factor 4 is a
 //     margin over round-to-nearest accumulation, whatever order the matrix
-//     cores add in).  The split and ||w_e||^2 (in double) are formed once per
-//     call by route_split; the filter stages bf16 tiles only.
+//     cores add in).  The split and ||w_e|| (the root of a double sum of
+//     squares) are formed once per call by route_split; the filter stages bf16
+//     tiles only.
 //  2. route_refine, one wavefront per token: with lo_e = zf_e - delta_e and
 //     hi_e = zf_e + delta_e (delta_e the bound above, biases added exactly),
 //     L = the k-th largest lo_e is a lower bound on the k-th largest logit, so
@@ -54,11 +55,11 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
 
 // Router split, once per call: one wavefront per router row writes
 // w_hi = bf16(w) and w_lo = bf16(w - w_hi) (the difference is exact in fp32)
-// as bf16 rows [E, d] and ||w_e||^2 in double; the first thread also clears
+// as bf16 rows [E, d] and ||w_e|| (root of a double sum); the first thread also clears
 // the overflow count that the refine and overflow passes read.
 __global__ __launch_bounds__(256) void route_split(const float* __restrict__ Wr, int d, int E,
                                                    uint16_t* __restrict__ wh, uint16_t* __restrict__ wl,
-                                                   double* __restrict__ wnorm2, int32_t* __restrict__ n_overflow) {
+                                                   double* __restrict__ wnorm, int32_t* __restrict__ n_overflow) {
     const int lane = threadIdx.x & 63;
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (blockIdx.x == 0 && threadIdx.x == 0) *n_overflow = 0;
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void route_split(const float* __restrict__ Wr,
             uint4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
     }
     s = wave_sum_xor_d(s);
-    if (lane == 0) wnorm2[e] = s;
+    if (lane == 0) wnorm[e] = sqrt(s);  // once per row rather than once per (token, row) in route_refine
 }
 
 // LDS tile of FT (or FE) rows x FKC bf16: 16-byte chunk c of row r at c ^ (r & 7)
@@ -272,7 +273,7 @@ template <int NPL, int XPL>
 __global__ __launch_bounds__(256) void route_refine(const uint16_t* __restrict__ x, int T, int d,
                                                     const float* __restrict__ Wr, const float* __restrict__ bias,
                                                     int E, int k, double cbound, const float* __restrict__ zf,
-                                                    const double* __restrict__ wnorm2, int32_t* __restrict__ ids,
+                                                    const double* __restrict__ wnorm, int32_t* __restrict__ ids,
                                                     float* __restrict__ gates, int32_t* __restrict__ n_overflow,
                                                     int32_t* __restrict__ overflow) {
     __shared__ RankScratch RS[4];
@@ -282,15 +283,20 @@ __global__ __launch_bounds__(256) void route_refine(const uint16_t* __restrict__
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;  // whole wavefronts only: no workgroup barrier below
     RankScratch& S = RS[wave];
-    double xv[XPL][8];
-    const double xn = sqrt(load_token<XPL>(x + (size_t)t * d, d, xv));
+    // ||x_t|| first; the token values are loaded again (from cache) for the
+    // exact logits, so that they are not held in registers across the selection
+    double xn;
+    {
+        double xv0[XPL][8];
+        xn = sqrt(load_token<XPL>(x + (size_t)t * d, d, xv0));
+    }
     double lo[NPL], hi[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
         if (e < E) {
             const double zb = (double)zf[(size_t)t * E + e] + (bias ? (double)bias[e] : 0.0);
-            const double del = cbound * xn * sqrt(wnorm2[e]) * (1.0 + 1e-6) + 1e-30;
+            const double del = cbound * xn * wnorm[e] * (1.0 + 1e-6) + 1e-30;
             lo[i] = zb - del;
             hi[i] = zb + del;
         } else {
@@ -298,27 +304,16 @@ __global__ __launch_bounds__(256) void route_refine(const uint16_t* __restrict__
             hi[i] = -DBL_MAX;
         }
     }
-    // L = k-th largest lower bound: k rounds of (lane best, wave best), one
-    // entry removed per round, so equal values count with their multiplicity
-    double L = -DBL_MAX;
+    // L = k-th largest lower bound, counted with multiplicity: the value of
+    // rank k - 1 of the top-k selection over the lower bounds
+    double L;
     {
         double tmp[NPL];
 #pragma unroll
         for (int i = 0; i < NPL; ++i) tmp[i] = lo[i];
-        for (int r = 0; r < k; ++r) {
-            double bv = -DBL_MAX;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < NPL; ++i) {
-                const int e = lane + 64 * i;
-                if (e < E && (tmp[i] > bv || (tmp[i] == bv && e < bi))) { bv = tmp[i]; bi = e; }
-            }
-            wave_argmax(bv, bi);
-#pragma unroll
-            for (int i = 0; i < NPL; ++i)
-                if (lane + 64 * i == bi) tmp[i] = -DBL_MAX;
-            L = bv;
-        }
+        topk_select_regs<NPL>(tmp, E, k, nullptr, S);
+        L = S.v[k - 1];
+        wave_lds_sync();  // S is written again by the ranking below
     }
     // candidates: hi >= L, compacted in index order
     const unsigned long long lt = (1ull << lane) - 1ull;
@@ -337,6 +332,8 @@ __global__ __launch_bounds__(256) void route_refine(const uint16_t* __restrict__
         return;
     }
     wave_lds_sync();
+    double xv[XPL][8];
+    (void)load_token<XPL>(x + (size_t)t * d, d, xv);
     // exact logits of the candidates, in candidate order (one router row in
     // flight per wavefront: the pass is bound by cache bandwidth, and more
     // rows in flight cost occupancy)
@@ -395,7 +392,7 @@ __global__ __launch_bounds__(256) void route_overflow(const uint16_t* __restrict
 }
 
 // scratch in the workspace's logits region: filter logits [T, E] fp32,
-// ||w_e||^2 [E] double, overflow count + list [1 + T] int32, w_hi and w_lo
+// ||w_e|| [E] double, overflow count + list [1 + T] int32, w_hi and w_lo
 // [E, d] bf16 each (256-byte aligned pieces)
 static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 size_t route_filter_bytes(int T, int E, int d) {
@@ -416,7 +413,7 @@ int launch_route_filtered(const void* x, int T, int d, const float* Wr, const fl
         return p;
     };
     float* zf = reinterpret_cast<float*>(take((size_t)T * E * 4));
-    double* wn2 = reinterpret_cast<double*>(take((size_t)E * 8));
+    double* wn = reinterpret_cast<double*>(take((size_t)E * 8));
     int32_t* novf = reinterpret_cast<int32_t*>(take(4 + (size_t)T * 4));
     int32_t* ovf = novf + 1;
     uint16_t* wh = reinterpret_cast<uint16_t*>(take((size_t)E * d * 2));
@@ -426,7 +423,7 @@ int launch_route_filtered(const void* x, int T, int d, const float* Wr, const fl
     const double u = std::ldexp(1.0, -24), n = 2.0 * d;
     const double gamma = n * u / (1.0 - n * u);
     const double cbound = std::ldexp(1.0, -16) + 4.0 * 1.008 * gamma;
-    route_split<<<(E + 3) / 4, 256, 0, s>>>(Wr, d, E, wh, wl, wn2, novf);
+    route_split<<<(E + 3) / 4, 256, 0, s>>>(Wr, d, E, wh, wl, wn, novf);
     int rc = check_launch();
     if (rc) return rc;
     route_filter<kFilterTokens><<<dim3((E + FE - 1) / FE, (T + kFilterTokens - 1) / kFilterTokens), 256, 0, s>>>(
@@ -437,7 +434,7 @@ int launch_route_filtered(const void* x, int T, int d, const float* Wr, const fl
     const int xpl = (d / 8 + 63) / 64;
 #define MOE_RF(NPL, XPL)                                                                                        \
     do {                                                                                                        \
-        route_refine<NPL, XPL><<<(T + 3) / 4, 256, 0, s>>>(xb, T, d, Wr, bias, E, k, cbound, zf, wn2, ids, gates, \
+        route_refine<NPL, XPL><<<(T + 3) / 4, 256, 0, s>>>(xb, T, d, Wr, bias, E, k, cbound, zf, wn, ids, gates, \
                                                            novf, ovf);                                          \
         rc = check_launch();                                                                                    \
         if (rc) return rc;                                                                                      \

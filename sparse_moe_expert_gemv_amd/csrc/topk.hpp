@@ -82,20 +82,11 @@ struct RankScratch {
 // if s_ids is given, the index in s_ids[r]; topk_gates then forms the softmax
 // from S and writes ids and gates, so that a caller can take the selection
 // alone first and the gates later.
+// topk_select_regs: the same selection over values already in registers
+// (entry lane + 64 i in v[i]; entries at or past E must hold -DBL_MAX).
 template <int NPL>
-__device__ __forceinline__ void topk_select(const double* __restrict__ z, int E, int k, int32_t* s_ids,
-                                            RankScratch& S, int planes = 1, size_t plane_stride = 0) {
+__device__ __forceinline__ void topk_select_regs(double (&v)[NPL], int E, int k, int32_t* s_ids, RankScratch& S) {
     const int lane = threadIdx.x & 63;
-    double v[NPL];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) v[i] = z[min(lane + 64 * i, E - 1)];
-    // split-k logits: the partial sums of the k planes are added in plane order
-    for (int p = 1; p < planes; ++p)
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) v[i] += z[p * plane_stride + min(lane + 64 * i, E - 1)];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-        if (lane + 64 * i >= E) v[i] = -DBL_MAX;
     uint64_t key[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) key[i] = order_key(v[i]);
@@ -174,6 +165,23 @@ __device__ __forceinline__ void topk_select(const double* __restrict__ z, int E,
     }
     wave_lds_sync();
     if (s_ids && lane < k) s_ids[lane] = S.i[lane];
+}
+
+template <int NPL>
+__device__ __forceinline__ void topk_select(const double* __restrict__ z, int E, int k, int32_t* s_ids,
+                                            RankScratch& S, int planes = 1, size_t plane_stride = 0) {
+    const int lane = threadIdx.x & 63;
+    double v[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) v[i] = z[min(lane + 64 * i, E - 1)];
+    // split-k logits: the partial sums of the k planes are added in plane order
+    for (int p = 1; p < planes; ++p)
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) v[i] += z[p * plane_stride + min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+        if (lane + 64 * i >= E) v[i] = -DBL_MAX;
+    topk_select_regs<NPL>(v, E, k, s_ids, S);
 }
 
 // softmax over the k selected values of S (rank order) and the global writes
