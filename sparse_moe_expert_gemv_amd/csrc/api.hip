@@ -44,10 +44,12 @@ void workspace_layout(int T, int d, int f, int E, int k, int act_mode, char* bas
     w->permute_bytes = off;
     if (act_mode == MOE_ACT_Q8) {
         w->tiles = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (4 * q8_tile_capacity(T, k, E) + 4)));
+        w->tile_blob = reinterpret_cast<const uint8_t**>(take(sizeof(void*) * q8_tile_capacity(T, k, E)));
         w->h = take(rows * (size_t)f * 2);  // int8 codes (int8 weights) or fp16 q * s (int4 weights)
         w->hs = reinterpret_cast<float*>(take(sizeof(float) * rows * (size_t)(f / 32)));
     } else {
         w->tiles = nullptr;
+        w->tile_blob = nullptr;
         w->h = take(float_h_bytes(T, f, k));
         w->hs = nullptr;
     }

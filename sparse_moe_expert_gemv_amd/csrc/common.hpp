@@ -116,6 +116,7 @@ struct Workspace {
     int32_t* tiles;     // q8 tile list (int2) + count    ffn
     void* h;            // SwiGLU intermediate [T*k + T, f]: fp16 (float mode, q8 with int4 weights) or int8 (q8, int8 weights)
     float* hs;          // q8: [T*k + T, f/32] block scales of h
+    const uint8_t** tile_blob;  // q8 mode: expert blob of each tile of the tile list (int4 weights)
     const uint8_t** slot_blob;  // float mode: [T*k] expert blob of each routed slot (by-slot decode;
                                 // written by the gate/up launch, read by the down + combine launch)
     size_t route_bytes, permute_bytes, bytes;

@@ -360,16 +360,27 @@ constexpr int kDNRows = 256;     // output rows per down work item
 // 16-byte bank groups of the 256 B the LDS serves per cycle.
 __device__ __forceinline__ int chunk_swz(int r) { return (r >> 1) & 7; }
 
-// Tiles of <= kTR rows, balanced per expert: (slot, m0, rows, 0) with slot =
-// position in the active list, or n_active for the shared expert.
+// Tiles of <= kTR rows, balanced per expert: tiles[i] = (e, m0, rows, p)
+// with e the expert (-1 for the shared expert), m0 the tile's first row
+// within the expert's rows and p = the tile's first row in the permuted
+// order (offsets[e] + m0, or T k + m0 for the shared expert), and
+// tile_blob[i] the expert's weights.  The FFN kernels then need one dependent
+// load (the tile's token list) before their data instead of four (tile,
+// active entry, expert pointer and offset, token list).  The shared
+// expert's tiles (all T tokens, the fullest) come first.
 __global__ __launch_bounds__(1024) void q8_tile_plan(const int32_t* __restrict__ counts,
-                                                     const int32_t* __restrict__ active, int T, int has_shared,
-                                                     int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+                                                     const int32_t* __restrict__ active,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const void* const* __restrict__ expert_ptrs,
+                                                     const uint8_t* __restrict__ shared_blob, int T, int k,
+                                                     int4* __restrict__ tiles, const uint8_t** __restrict__ tile_blob,
+                                                     int32_t* __restrict__ n_tiles) {
     __shared__ int32_t sc[1024];
     constexpr int cap = kTR;
     const int a = threadIdx.x;
     const int n_active = active[0];
-    const int c = a < n_active ? counts[active[1 + a]] : 0;
+    const int e = a < n_active ? active[1 + a] : 0;
+    const int c = a < n_active ? counts[e] : 0;
     const int nt = (c + cap - 1) / cap;
     sc[a] = nt;
     __syncthreads();
@@ -379,21 +390,25 @@ __global__ __launch_bounds__(1024) void q8_tile_plan(const int32_t* __restrict__
         sc[a] += v;
         __syncthreads();
     }
-    const int start = sc[a] - nt;
+    const int ns = shared_blob ? (T + cap - 1) / cap : 0;
+    const int start = ns + sc[a] - nt;
     if (nt > 0) {
         const int per = ((c + nt - 1) / nt + 15) / 16 * 16;
-        for (int i = 0; i < nt; ++i) tiles[start + i] = make_int4(a, i * per, min(per, c - i * per), 0);
-    }
-    if (a == 1023) {
-        int total = sc[1023];
-        if (has_shared) {  // the shared expert: slot n_active, all T tokens
-            const int ns = (T + cap - 1) / cap;
-            const int per = ((T + ns - 1) / ns + 15) / 16 * 16;
-            for (int i = 0; i < ns; ++i) tiles[total + i] = make_int4(n_active, i * per, min(per, T - i * per), 0);
-            total += ns;
+        const int oe = offsets[e];
+        const uint8_t* blob = (const uint8_t*)expert_ptrs[e];
+        for (int i = 0; i < nt; ++i) {
+            tiles[start + i] = make_int4(e, i * per, min(per, c - i * per), oe + i * per);
+            tile_blob[start + i] = blob;
         }
-        n_tiles[0] = total;
     }
+    if (ns > 0) {
+        const int per = ((T + ns - 1) / ns + 15) / 16 * 16;
+        for (int i = a; i < ns; i += 1024) {
+            tiles[i] = make_int4(-1, i * per, min(per, T - i * per), T * k + i * per);
+            tile_blob[i] = shared_blob;
+        }
+    }
+    if (a == 1023) n_tiles[0] = ns + sc[1023];
 }
 
 // One packed int4 word (offset binary u = q + 8, nibbles k0 k2 k4 k6 k1 k3 k5
@@ -494,9 +509,9 @@ struct GURegs {
 // 127, and the down projection's operand fp16(q * s) is written.
 __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_gateup(
     const int8_t* __restrict__ xq, const float* __restrict__ sx, int T, int d, int f, int k,
-    const void* const* __restrict__ expert_ptrs, const uint8_t* __restrict__ shared_blob,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_idx, const int32_t* __restrict__ active,
-    const int4* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, _Float16* __restrict__ h_out) {
+    const int32_t* __restrict__ sorted_idx, const int4* __restrict__ tiles,
+    const uint8_t* const* __restrict__ tile_blob, const int32_t* __restrict__ n_tiles_p,
+    _Float16* __restrict__ h_out) {
     // two LDS stages as separate variables: the compiler then knows that the
     // loads filling one do not alias the reads of the other.  The token scales,
     // read 12 times per block and wavefront, are over-aligned so that they are
@@ -512,17 +527,14 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_gateup(
     const int ti = (j / n_groups) * 8 + xcd, grp = j % n_groups;
     if (ti >= n_tiles_p[0]) return;
     const int4 tl = tiles[ti];
-    const int n_active = active[0];
-    const bool routed = tl.x < n_active;
-    const int e = routed ? active[1 + tl.x] : -1;
-    const uint8_t* blob = routed ? (const uint8_t*)expert_ptrs[e] : shared_blob;
+    const uint8_t* blob = tile_blob[ti];
     if (blob == nullptr) return;  // no weights behind this expert (uniform per workgroup)
-    const int p0 = routed ? offsets[e] : T * k;
-    const int m0 = tl.y, mc = tl.z;
+    const bool routed = tl.x >= 0;
+    const int m0 = tl.y, mc = tl.z, prow0 = tl.w;  // prow0: first row of the tile in the permuted order
     const int nmt = (mc + 31) >> 5;
     for (int i = threadIdx.x; i < kTR; i += kPThreads) {
         const int m = min(i, mc - 1);  // rows past the tile repeat its last row (results discarded)
-        s_row[i] = routed ? sorted_idx[p0 + m0 + m] / k : m0 + m;
+        s_row[i] = routed ? sorted_idx[prow0 + m] / k : m0 + m;
     }
     const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
     const int nkt = d / 128;
@@ -664,7 +676,7 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_gateup(
         static_assert(kPThreads / 64 * 32 * HRB <= sizeof(GUStage), "h tiles exceed the stage");
         unsigned char* htile = reinterpret_cast<unsigned char*>(&S0) + wave * (32 * HRB);
         const int hrow = lane >> 1, hhalf = lane & 1;
-        _Float16* hdst = h_out + (size_t)(p0 + m0) * f + grp * kGUFeat + fg * 32 + 16 * hhalf;
+        _Float16* hdst = h_out + (size_t)prow0 * f + grp * kGUFeat + fg * 32 + 16 * hhalf;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
 #pragma unroll
@@ -813,9 +825,8 @@ __device__ __forceinline__ void dn_write_tiles(unsigned char* tile, const float1
 // (2^-11 relative each) only adds to the output's error.
 template <typename YT>
 __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_down(
-    const _Float16* __restrict__ h, int T, int d, int f, int k, const void* const* __restrict__ expert_ptrs,
-    const uint8_t* __restrict__ shared_blob, const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
-    const int4* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p, YT* __restrict__ y_perm,
+    const _Float16* __restrict__ h, int T, int d, int f, int k, const int4* __restrict__ tiles,
+    const uint8_t* const* __restrict__ tile_blob, const int32_t* __restrict__ n_tiles_p, YT* __restrict__ y_perm,
     float* __restrict__ y_shared) {
     __shared__ DNStage S[2];
     const int lane = threadIdx.x & 63;
@@ -825,13 +836,10 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_down(
     const int ti = (j / n_groups) * 8 + xcd, grp = j % n_groups;
     if (ti >= n_tiles_p[0]) return;
     const int4 tl = tiles[ti];
-    const int n_active = active[0];
-    const bool routed = tl.x < n_active;
-    const int e = routed ? active[1 + tl.x] : -1;
-    const uint8_t* blob = routed ? (const uint8_t*)expert_ptrs[e] : shared_blob;
+    const uint8_t* blob = tile_blob[ti];
     if (blob == nullptr) return;
-    const int p0 = routed ? offsets[e] : T * k;
-    const int m0 = tl.y, mc = tl.z;
+    const bool routed = tl.x >= 0;
+    const int m0 = tl.y, mc = tl.z, prow0 = tl.w;  // prow0: first row of the tile in the permuted order
     const int nmt = (mc + 31) >> 5;
     const ExpertLayout L = expert_layout(MOE_WFMT_I4B32, d, f);
     const int nkt = f / 128;
@@ -849,7 +857,7 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_down(
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
         const int idx = threadIdx.x + q * kPThreads, row = idx >> 3;
-        ha_off[q] = (uint32_t)(p0 + m0 + min(row, mc - 1)) * (uint32_t)f * 2 + (idx & 7) * 16;
+        ha_off[q] = (uint32_t)(prow0 + min(row, mc - 1)) * (uint32_t)f * 2 + (idx & 7) * 16;
     }
     // chunk c covers k = 64 c .. 64 c + 63: half (c & 1) of packed tile c >> 1
     auto load_chunk = [&](DNRegs& R, int c) {
@@ -931,7 +939,7 @@ __global__ __launch_bounds__(kPThreads, 1) void ffn_i4_down(
         const int o0 = grp * kDNRows + og * 64;  // first output of this wavefront's columns
         if (o0 < d) {
             if (routed) dn_write_tiles<NM, YT>(reinterpret_cast<unsigned char*>(&S[0]) + wave * dn_tile_bytes<YT>(),
-                                               acc, lane, mt0, mc, y_perm + (size_t)(p0 + m0) * d + o0, d);
+                                               acc, lane, mt0, mc, y_perm + (size_t)prow0 * d + o0, d);
             else dn_write_tiles<NM, float>(reinterpret_cast<unsigned char*>(&S[0]) + wave * dn_tile_bytes<float>(),
                                            acc, lane, mt0, mc, y_shared + (size_t)m0 * d + o0, d);
         }
@@ -959,24 +967,22 @@ static int run_q8(const moe_ffn_args* a, const Workspace& w, hipStream_t s) {
                                (a->shared_blob ? a->T / kTR + 1 : 0);
         const long gt = (max_tiles + 7) / 8 * 8;
         if (a->phase != 2) {
-            q8_tile_plan<<<1, 1024, 0, s>>>(a->counts, a->active, a->T, a->shared_blob ? 1 : 0, t4, n_tiles);
+            q8_tile_plan<<<1, 1024, 0, s>>>(a->counts, a->active, a->offsets, a->expert_ptrs,
+                                            (const uint8_t*)a->shared_blob, a->T, a->k, t4, w.tile_blob, n_tiles);
             rc = check_launch();
             if (rc) return rc;
             ffn_i4_gateup<<<(unsigned)(gt * (a->f / kGUFeat)), kPThreads, 0, s>>>(
-                a->xq, a->sx, a->T, a->d, a->f, a->k, a->expert_ptrs, (const uint8_t*)a->shared_blob, a->offsets,
-                a->sorted_idx, a->active, t4, n_tiles, h16);
+                a->xq, a->sx, a->T, a->d, a->f, a->k, a->sorted_idx, t4, w.tile_blob, n_tiles, h16);
             rc = check_launch();
             if (rc || a->phase == 1) return rc;
         }
         const unsigned g2 = (unsigned)(gt * ((a->d + kDNRows - 1) / kDNRows));
         if (a->y_dtype == MOE_DT_F32)
-            ffn_i4_down<float><<<g2, kPThreads, 0, s>>>(h16, a->T, a->d, a->f, a->k, a->expert_ptrs,
-                                                        (const uint8_t*)a->shared_blob, a->offsets, a->active, t4,
-                                                        n_tiles, (float*)a->y_perm, a->y_shared);
+            ffn_i4_down<float><<<g2, kPThreads, 0, s>>>(h16, a->T, a->d, a->f, a->k, t4, w.tile_blob, n_tiles,
+                                                        (float*)a->y_perm, a->y_shared);
         else
-            ffn_i4_down<_Float16><<<g2, kPThreads, 0, s>>>(h16, a->T, a->d, a->f, a->k, a->expert_ptrs,
-                                                           (const uint8_t*)a->shared_blob, a->offsets, a->active, t4,
-                                                           n_tiles, (_Float16*)a->y_perm, a->y_shared);
+            ffn_i4_down<_Float16><<<g2, kPThreads, 0, s>>>(h16, a->T, a->d, a->f, a->k, t4, w.tile_blob, n_tiles,
+                                                           (_Float16*)a->y_perm, a->y_shared);
         return check_launch();
     }
     if (a->phase != 2) {
