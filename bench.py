@@ -65,14 +65,22 @@ def parse():
     return p.parse_args()
 
 
+def kernel_source_sha256(workload: str) -> str:
+    """SHA-256 over the source of a workload's dominant kernel and the shared
+    device headers it includes (common.hpp, topk.hpp, wave.hpp), in that order."""
+    import hashlib
+    csrc = os.path.join(ROOT, "sparse_moe_expert_gemv_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("ffn_q8.hip" if workload == "prefill" else "ffn_float.hip", "common.hpp", "topk.hpp", "wave.hpp"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     FETCH_SIZE/WRITE_SIZE summary, if one exists for this workload and the
     kernel source has not changed since the counters were taken; else None."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "gateup_%s_hbm_counters.md" % workload)
-    src = os.path.join(ROOT, "sparse_moe_expert_gemv_amd", "csrc",
-                       "ffn_q8.hip" if workload == "prefill" else "ffn_float.hip")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -80,7 +88,7 @@ def measured_traffic(workload: str):
         if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "kernel_source_sha256"):
             key, val = line.split(":", 1)
             fields[key] = val.strip()
-    if fields.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if fields.get("kernel_source_sha256") != kernel_source_sha256(workload):
         return None
     return int(fields["traffic_bytes_per_launch"]) if "traffic_bytes_per_launch" in fields else None
 
